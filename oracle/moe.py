@@ -1,0 +1,301 @@
+"""Plain CPU definition of one GPU's share of a routed MoE layer, fp64.
+
+Test infrastructure only (see the package header).
+
+The steps and their order follow the GC-MoE summary page ("Approach": routing
+counts, W1 on ready token blocks, an epilogue that fuses SwiGLU, routing-weight
+scaling and FP8 requantisation, W2 producing BF16 fragments, then combine;
+"Key contributions": the fused epilogue and optional shared expert) and the
+fusion-kernel blog (SwiGLU definition in the "GLU activation in a fused GEMM
+epilogue" section; per-group token counts kept in device memory in the
+"Removing host-device synchronisation" section; the MXFP8 transposed copy in
+the "Fusing MXFP8/NVFP4 quantisation" section).
+
+Where the pages are silent the readings are:
+* router: softmax over all experts' fp32 logits; the k largest logits are
+  selected (ties to the lower expert id), in descending order; weights are the
+  softmax probabilities, not renormalised unless asked;
+* only experts [e0, e0 + n_local) are computed here; a token with no local
+  slot contributes an exact zero row;
+* grouping is stable: within an expert, rows follow the flattened assignment
+  index t*k + j; experts in ascending local id; the shared expert (if any) is
+  the last group and takes every token in order with weight 1;
+* W1 rows [0, I) are the gate (through SiLU, beta = 1), rows [I, 2I) are up;
+  no bias; the routing weight multiplies h once, before requantisation;
+* quantisation points: h -> MX-E4M3 (blocks of 32 along I), y -> BF16 per
+  row, out -> BF16; every other step is exact or fp64.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import mx
+
+
+# ------------------------------------------------------------------ routing
+def route(logits: np.ndarray, k: int, renorm: bool = False):
+    """Top-k softmax router.
+
+    logits: float32 [T, E].  Returns (topk_idx int32 [T, k], topk_w fp64 [T, k]).
+    Selection compares the fp32 logits themselves (softmax is strictly
+    increasing, so this selects the k largest probabilities) with ties going
+    to the lower expert id; slot j holds the j-th largest.
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    assert 1 <= k <= E
+    assert np.all(np.isfinite(logits)), "router logits must be finite"
+    ids = np.broadcast_to(np.arange(E), (T, E))
+    # np.lexsort: last key is primary; it is stable, so equal logits keep id order.
+    order = np.lexsort((ids, -logits.astype(np.float64)), axis=-1)
+    topk_idx = order[:, :k].astype(np.int32)
+    l64 = logits.astype(np.float64)
+    m = l64.max(axis=1, keepdims=True)
+    ex = np.exp(l64 - m)
+    p = ex / ex.sum(axis=1, keepdims=True)
+    topk_w = np.take_along_axis(p, topk_idx.astype(np.int64), axis=1)
+    if renorm:
+        topk_w = topk_w / topk_w.sum(axis=1, keepdims=True)
+    return topk_idx, topk_w
+
+
+# --------------------------------------------------- counts and permutation
+@dataclass
+class Permutation:
+    counts: np.ndarray      # int32 [G]
+    offsets: np.ndarray     # int32 [G + 1], offsets[0] = 0
+    row_src: np.ndarray     # int32 [R]   source token of each grouped row
+    row_slot: np.ndarray    # int32 [R]   slot j of that token (k for the shared group)
+    row_w: np.ndarray       # fp64  [R]   routing weight of each row
+    slot_row: np.ndarray    # int32 [T, k + s], -1 where the slot is not local
+    G: int = 0
+    E_loc: int = 0
+    shared: bool = False
+
+
+def permute(topk_idx: np.ndarray, topk_w: np.ndarray, e0: int, n_local: int,
+            shared: bool = False) -> Permutation:
+    """Group the local assignments by expert, stably (see the module header)."""
+    T, k = topk_idx.shape
+    s = 1 if shared else 0
+    G = n_local + s
+    lists = [[] for _ in range(G)]
+    for a in range(T * k):                      # flattened assignment index
+        t, j = divmod(a, k)
+        g = int(topk_idx[t, j]) - e0
+        if 0 <= g < n_local:
+            lists[g].append((t, j, float(topk_w[t, j])))
+    if shared:
+        lists[n_local] = [(t, k, 1.0) for t in range(T)]
+    counts = np.array([len(lst) for lst in lists], dtype=np.int32)
+    offsets = np.zeros(G + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    R = int(offsets[-1])
+    row_src = np.zeros(R, dtype=np.int32)
+    row_slot = np.zeros(R, dtype=np.int32)
+    row_w = np.zeros(R, dtype=np.float64)
+    slot_row = np.full((T, k + s), -1, dtype=np.int32)
+    for g, lst in enumerate(lists):
+        for i, (t, j, w) in enumerate(lst):
+            r = offsets[g] + i
+            row_src[r], row_slot[r], row_w[r] = t, j, w
+            slot_row[t, j] = r
+    return Permutation(counts, offsets, row_src, row_slot, row_w, slot_row, G, n_local, shared)
+
+
+def gather_rows(xq: np.ndarray, xs: np.ndarray, perm: Permutation):
+    """Copy each grouped row's FP8 codes and E8M0 scales from its source token."""
+    return xq[perm.row_src], xs[perm.row_src]
+
+
+# -------------------------------------------------------------- expert MLP
+def silu(g: np.ndarray) -> np.ndarray:
+    """Swish with beta = 1: g * sigmoid(g), fp64."""
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_rows(acc: np.ndarray, I: int, w: np.ndarray) -> np.ndarray:
+    """h = SiLU(gate) * up * w for W1 output rows acc [n, 2I] (gate first)."""
+    gate, up = acc[:, :I], acc[:, I:2 * I]
+    return silu(gate) * up * np.asarray(w, dtype=np.float64)[:, None]
+
+
+def quantize_transposed(h: np.ndarray, rule: str = "ocp"):
+    """Transposed MX-E4M3 copy of one expert's h [n, I]: hT [I, n32] with
+    n32 = roundup(n, 32), quantised in blocks of 32 tokens counted from the
+    expert's first row. A partial last block takes its amax over the valid
+    tokens only; its padding columns hold code 0."""
+    n, I = h.shape
+    n32 = -(-n // 32) * 32
+    hT = np.zeros((I, n32), dtype=np.float64)
+    hT[:, :n] = h.T
+    q, sc = mx.quantize_mx(hT, mx.FMT_E4M3, rule)
+    q[:, n:] = 0
+    return q, sc
+
+
+@dataclass
+class W1Out:
+    hq: np.ndarray                       # uint8 [R, I]
+    hs: np.ndarray                       # uint8 [R, I/32]
+    h: np.ndarray                        # fp64  [R, I]   unrounded
+    acc: np.ndarray                      # fp64  [R, 2I]
+    hTq: list = field(default_factory=list)   # per group uint8 [I, roundup(n_g,32)]
+    hTs: list = field(default_factory=list)   # per group uint8 [I, roundup(n_g,32)/32]
+
+
+def grouped_w1(xq_perm, xs_perm, offsets, row_w, w1q, w1s, w1_fmt: str, I: int,
+               transpose: bool = False, rule: str = "ocp", groups=None) -> W1Out:
+    """Per group g: acc = X_g @ W1_g^T in fp64, then the fused epilogue.
+
+    xq_perm/xs_perm: E4M3 codes [R, H] and E8M0 scales [R, H/32].
+    w1q/w1s: per-group sequences of W1 codes [2I, H(*1/2 for FP4)] and scales [2I, H/32].
+    `groups` optionally restricts the computation to a subset of group ids.
+    """
+    R = int(offsets[-1])
+    G = len(offsets) - 1
+    acc = np.zeros((R, 2 * I))
+    h = np.zeros((R, I))
+    hTq, hTs = [], []
+    todo = range(G) if groups is None else groups
+    for g in todo:
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi > lo:
+            X = mx.dequantize_mx(xq_perm[lo:hi], xs_perm[lo:hi], mx.FMT_E4M3)
+            W = mx.dequantize_mx(np.asarray(w1q[g]), np.asarray(w1s[g]), w1_fmt)
+            acc[lo:hi] = X @ W.T
+            h[lo:hi] = swiglu_rows(acc[lo:hi], I, row_w[lo:hi])
+    hq, hs = mx.quantize_mx(h, mx.FMT_E4M3, rule)
+    if transpose:
+        for g in range(G):
+            lo, hi = int(offsets[g]), int(offsets[g + 1])
+            q, sc = quantize_transposed(h[lo:hi], rule)
+            hTq.append(q)
+            hTs.append(sc)
+    return W1Out(hq, hs, h, acc, hTq, hTs)
+
+
+def concat_transposed(hTq_list, hTs_list, I: int):
+    """Lay the per-group transposed copies side by side: [I, sum roundup(n_g,32)]."""
+    q = np.concatenate([np.asarray(x).reshape(I, -1) for x in hTq_list], axis=1) \
+        if hTq_list else np.zeros((I, 0), np.uint8)
+    s = np.concatenate([np.asarray(x).reshape(I, -1) for x in hTs_list], axis=1) \
+        if hTs_list else np.zeros((I, 0), np.uint8)
+    return q, s
+
+
+def grouped_w2(hq, hs, offsets, w2q, w2s, w2_fmt: str, groups=None):
+    """Per group g: y_g = BF16_RNE(dec(h_g) @ dec(W2_g)^T), rounded once from fp64."""
+    R = int(offsets[-1])
+    G = len(offsets) - 1
+    H = np.asarray(w2s[0]).shape[0] if G else 0
+    yv = np.zeros((R, H))
+    todo = range(G) if groups is None else groups
+    for g in todo:
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi > lo:
+            Hd = mx.dequantize_mx(hq[lo:hi], hs[lo:hi], mx.FMT_E4M3)
+            W = mx.dequantize_mx(np.asarray(w2q[g]), np.asarray(w2s[g]), w2_fmt)
+            yv[lo:hi] = Hd @ W.T
+    return mx.bf16_rne(yv)
+
+
+def combine(y_bits: np.ndarray, slot_row: np.ndarray, H: int, row_scale=None):
+    """out[t] = BF16_RNE(sum over the token's local slots of y rows), summed in
+    fp64; a token with no local slot gives +0. `row_scale` (optional, per grouped
+    row) multiplies each row first: the weight-at-combine variant."""
+    T = slot_row.shape[0]
+    acc = np.zeros((T, H))
+    yv = mx.bf16_value(y_bits)
+    for t in range(T):
+        for r in slot_row[t]:
+            if r >= 0:
+                acc[t] += yv[r] if row_scale is None else yv[r] * row_scale[r]
+    return mx.bf16_rne(acc)
+
+
+# ---------------------------------------------------------------- the layer
+@dataclass
+class LayerOut:
+    out: np.ndarray          # uint16 bf16 [T, H]
+    topk_idx: np.ndarray
+    topk_w: np.ndarray
+    perm: Permutation
+    w1: W1Out
+    y: np.ndarray            # uint16 bf16 [R, H]
+
+
+def moe_layer(logits, xq, xs, k: int, w1q, w1s, w2q, w2s, w_fmt: str, I: int,
+              e0: int = 0, n_local: int | None = None, shared=None,
+              renorm: bool = False, transpose: bool = False,
+              weight_at_combine: bool = False, rule: str = "ocp") -> LayerOut:
+    """One GPU's share of the routed MoE layer, from quantised inputs to BF16.
+
+    logits f32 [T, E_tot]; xq uint8 E4M3 [T, H]; xs uint8 E8M0 [T, H/32];
+    w1q/w1s/w2q/w2s: per local expert codes and scales (see grouped_w1/w2);
+    shared: None or (sw1q, sw1s, sw2q, sw2s) for an always-on shared expert.
+    """
+    E_tot = logits.shape[1]
+    n_local = E_tot if n_local is None else n_local
+    idx, w = route(logits, k, renorm)
+    perm = permute(idx, w, e0, n_local, shared is not None)
+    xq_p, xs_p = gather_rows(np.asarray(xq), np.asarray(xs), perm)
+    w1q_g, w1s_g, w2q_g, w2s_g = list(w1q), list(w1s), list(w2q), list(w2s)
+    if shared is not None:
+        w1q_g.append(shared[0]); w1s_g.append(shared[1])
+        w2q_g.append(shared[2]); w2s_g.append(shared[3])
+    row_w_h = np.ones_like(perm.row_w) if weight_at_combine else perm.row_w
+    o1 = grouped_w1(xq_p, xs_p, perm.offsets, row_w_h, w1q_g, w1s_g, w_fmt, I,
+                    transpose=transpose, rule=rule)
+    y = grouped_w2(o1.hq, o1.hs, perm.offsets, w2q_g, w2s_g, w_fmt)
+    H = xq.shape[1]
+    out = combine(y, perm.slot_row, H, perm.row_w if weight_at_combine else None)
+    return LayerOut(out, idx, w, perm, o1, y)
+
+
+def dense_layer(logits, xq, xs, k: int, w1q, w1s, w2q, w2s, w_fmt: str, I: int,
+                e0: int = 0, n_local: int | None = None, shared=None, rule: str = "ocp"):
+    """Brute-force evaluation with no grouping: for every token and every local
+    slot, run that expert's MLP on the token alone, then sum its slots.
+    Returns bf16 bits [T, H]. Used to pin the grouped computation."""
+    T, E_tot = logits.shape
+    n_local = E_tot if n_local is None else n_local
+    H = xq.shape[1]
+    idx, w = route(logits, k)
+    X = mx.dequantize_mx(np.asarray(xq), np.asarray(xs), mx.FMT_E4M3)
+    out = np.zeros((T, H))
+
+    def expert(t, W1q, W1s, W2q, W2s, weight):
+        acc = X[t:t + 1] @ mx.dequantize_mx(np.asarray(W1q), np.asarray(W1s), w_fmt).T
+        h = swiglu_rows(acc, I, np.array([weight]))
+        hq, hs = mx.quantize_mx(h, mx.FMT_E4M3, rule)
+        yv = mx.dequantize_mx(hq, hs, mx.FMT_E4M3) @ \
+            mx.dequantize_mx(np.asarray(W2q), np.asarray(W2s), w_fmt).T
+        return mx.bf16_value(mx.bf16_rne(yv))[0]
+
+    for t in range(T):
+        for j in range(k):
+            g = int(idx[t, j]) - e0
+            if 0 <= g < n_local:
+                out[t] += expert(t, w1q[g], w1s[g], w2q[g], w2s[g], w[t, j])
+        if shared is not None:
+            out[t] += expert(t, shared[0], shared[1], shared[2], shared[3], 1.0)
+    return mx.bf16_rne(out)
+
+
+# ------------------------------------------------------- algorithmic work
+def algorithmic_bytes(T: int, E_tot: int, H: int, I: int, active_groups: int,
+                      w_fmt: str) -> int:
+    """HBM bytes the method must move per call: logits, x (codes + scales), the
+    W1 + W2 codes and scales of the active groups only, and the BF16 output."""
+    bw = 0.5 if w_fmt == mx.FMT_E2M1 else 1.0
+    per_group = int(3 * I * H * bw) + 3 * I * H // 32
+    return 4 * T * E_tot + T * H + T * H // 32 + active_groups * per_group + 2 * T * H
+
+
+def algorithmic_flops(R: int, H: int, I: int) -> int:
+    """Multiply-add work of the two grouped GEMMs over real rows: 6 R H I."""
+    return 6 * R * H * I
