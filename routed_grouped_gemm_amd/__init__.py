@@ -1,0 +1,286 @@
+"""routed_grouped_gemm_amd: one GPU's share of a routed MoE layer on MI355X.
+
+A thin PyTorch binding over libmoe (include/moe.h). Every function here only
+marshals arguments (device pointers, sizes, the current HIP stream) and calls
+the C ABI of the same name; all computation runs in the library's HIP kernels.
+PyTorch provides device memory and streams. Importing the package fails if the
+library has not been built (routed_grouped_gemm_amd.build.build()).
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_FMT_MXFP4, MOE_FMT_MXFP8, MOE_ROUTE_RENORM, MOE_SCALE_RULE_CEIL,  # noqa: F401
+                   MOE_W1_WRITE_TRANSPOSE, MOE_WEIGHT_AT_COMBINE, moe_layer_args, moe_weights)
+
+lib = _lib.load()
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def _check(status: int, name: str) -> None:
+    if status != 0:
+        raise MoeError(f"{name} failed: {lib.moe_status_string(status).decode()} (status {status})")
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    if t.device.type != "cuda":
+        raise MoeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    return t
+
+
+def version() -> str:
+    return lib.moe_version().decode()
+
+
+# ------------------------------------------------------------------ weights
+def moe_prepacked_size(G: int, N: int, K: int, fmt: int) -> int:
+    return int(lib.moe_prepacked_size(G, N, K, fmt))
+
+
+def moe_quantize_mx(src: torch.Tensor, fmt: int, flags: int = 0, q=None, s=None, stream=None):
+    """fp32 [rows, K] -> (codes, E8M0 scales); codes are [rows, K] E4M3 or
+    [rows, K/2] packed E2M1."""
+    _dev(src, torch.float32, "src")
+    rows, K = src.shape
+    if q is None:
+        q = torch.empty((rows, K if fmt == MOE_FMT_MXFP8 else K // 2), dtype=torch.uint8, device=src.device)
+    if s is None:
+        s = torch.empty((rows, K // 32), dtype=torch.uint8, device=src.device)
+    _check(lib.moe_quantize_mx(_p(src), rows, K, fmt, flags, _p(q), _p(s), _stream(stream)), "moe_quantize_mx")
+    return q, s
+
+
+class PackedWeights:
+    """Prepacked expert weights (device buffer + its moe_weights descriptor)."""
+
+    def __init__(self, q: torch.Tensor, s: torch.Tensor, fmt: int, is_w1: bool, stream=None):
+        _dev(q, torch.uint8, "q")
+        _dev(s, torch.uint8, "s")
+        G, N = q.shape[0], q.shape[1]
+        K = s.shape[2] * 32
+        nbytes = moe_prepacked_size(G, N, K, fmt)
+        if nbytes == 0:
+            raise MoeError(f"bad weight shape G={G} N={N} K={K}")
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        _check(lib.moe_prepack_weights(_p(q), _p(s), G, N, K, fmt, int(is_w1), _p(self.buf), nbytes,
+                                       _stream(stream)), "moe_prepack_weights")
+        self.desc = moe_weights(fmt, G, N, K, int(is_w1), 0, _p(self.buf), nbytes)
+        self.G, self.N, self.K, self.fmt, self.is_w1 = G, N, K, fmt, bool(is_w1)
+
+    @classmethod
+    def empty(cls, G: int, N: int, K: int, fmt: int, is_w1: bool, device="cuda"):
+        """An unfilled buffer of the right size (filled later, e.g. one group at a time)."""
+        self = cls.__new__(cls)
+        nbytes = moe_prepacked_size(G, N, K, fmt)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.desc = moe_weights(fmt, G, N, K, int(is_w1), 0, _p(self.buf), nbytes)
+        self.G, self.N, self.K, self.fmt, self.is_w1 = G, N, K, fmt, bool(is_w1)
+        return self
+
+    @property
+    def group_stride(self) -> int:
+        return moe_prepacked_size(1, self.N, self.K, self.fmt)
+
+    def fill_group(self, g: int, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+        """Prepack one expert's logical codes q [N, K or K/2] and scales s [N, K/32]
+        into group slot g."""
+        _dev(q, torch.uint8, "q")
+        _dev(s, torch.uint8, "s")
+        st = self.group_stride
+        dst = self.buf[g * st:(g + 1) * st]
+        _check(lib.moe_prepack_weights(_p(q), _p(s), 1, self.N, self.K, self.fmt, int(self.is_w1),
+                                       _p(dst), st, _stream(stream)), "moe_prepack_weights")
+
+    def ref(self):
+        return C.byref(self.desc)
+
+
+def _wref(w):
+    return None if w is None else w.ref()
+
+
+# ------------------------------------------------------------------- route
+def moe_route(logits: torch.Tensor, k: int, flags: int = 0, topk_idx=None, topk_w=None, stream=None):
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib.moe_route(_p(logits), T, E, k, flags, _p(topk_idx), _p(topk_w), _stream(stream)), "moe_route")
+    return topk_idx, topk_w
+
+
+# ----------------------------------------------------------------- permute
+def moe_permute(topk_idx, topk_w, e0: int, n_local: int, shared: bool, xq=None, xs=None,
+                stream=None):
+    """Returns a dict: counts, offsets, offsets32, row_src, row_w, slot_row,
+    xq_perm, xs_perm (the last two only when xq/xs are given)."""
+    _dev(topk_idx, torch.int32, "topk_idx")
+    _dev(topk_w, torch.float32, "topk_w")
+    T, k = topk_idx.shape
+    s = int(bool(shared))
+    G = n_local + s
+    R_max = T * k + s * T
+    dev = topk_idx.device
+    H = xq.shape[1] if xq is not None else 256
+    out = dict(
+        counts=torch.empty(G, dtype=torch.int32, device=dev),
+        offsets=torch.empty(G + 1, dtype=torch.int32, device=dev),
+        offsets32=torch.empty(G + 1, dtype=torch.int32, device=dev),
+        row_src=torch.empty(max(R_max, 1), dtype=torch.int32, device=dev),
+        row_w=torch.empty(max(R_max, 1), dtype=torch.float32, device=dev),
+        slot_row=torch.empty((T, k + s), dtype=torch.int32, device=dev),
+    )
+    if xq is not None:
+        _dev(xq, torch.uint8, "xq")
+        _dev(xs, torch.uint8, "xs")
+        out["xq_perm"] = torch.empty((max(R_max, 1), H), dtype=torch.uint8, device=dev)
+        out["xs_perm"] = torch.empty((max(R_max, 1), H // 32), dtype=torch.uint8, device=dev)
+    nws = int(lib.moe_permute_workspace_size(T, k, G))
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _check(lib.moe_permute(_p(topk_idx), _p(topk_w), T, k, e0, n_local, s, _p(xq), _p(xs), H,
+                           _p(out["counts"]), _p(out["offsets"]), _p(out["offsets32"]),
+                           _p(out["row_src"]), _p(out["row_w"]), _p(out["slot_row"]),
+                           _p(out.get("xq_perm")), _p(out.get("xs_perm")), _p(ws), nws,
+                           _stream(stream)), "moe_permute")
+    return out
+
+
+# ----------------------------------------------------------------- grouped
+def moe_transposed_ld(R_max: int, G: int) -> int:
+    return int(lib.moe_transposed_ld(R_max, G))
+
+
+def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq_perm, xs_perm, I: int,
+                   flags: int = 0, w1_shared: PackedWeights | None = None, offsets32=None,
+                   hq=None, hs=None, hTq=None, hTs=None, stream=None):
+    R_max, H = xq_perm.shape
+    G = counts.shape[0]
+    dev = xq_perm.device
+    if hq is None:
+        hq = torch.empty((R_max, I), dtype=torch.uint8, device=dev)
+    if hs is None:
+        hs = torch.empty((R_max, I // 32), dtype=torch.uint8, device=dev)
+    if (flags & MOE_W1_WRITE_TRANSPOSE) and hTq is None:
+        ld = moe_transposed_ld(R_max, G)
+        hTq = torch.empty((I, ld), dtype=torch.uint8, device=dev)
+        hTs = torch.empty((I, ld // 32), dtype=torch.uint8, device=dev)
+    nws = int(lib.moe_grouped_workspace_size(R_max, G, 2 * I, H))
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _check(lib.moe_grouped_w1(w1.ref(), _wref(w1_shared), _p(counts), _p(offsets), _p(offsets32),
+                              _p(row_w), _p(xq_perm), _p(xs_perm), R_max, H, I, G, flags, _p(hq),
+                              _p(hs), _p(hTq), _p(hTs), _p(ws), nws, _stream(stream)), "moe_grouped_w1")
+    return hq, hs, hTq, hTs
+
+
+def moe_grouped_w2(w2: PackedWeights, counts, offsets, hq, hs, H: int,
+                   w2_shared: PackedWeights | None = None, y=None, stream=None):
+    R_max, I = hq.shape
+    G = counts.shape[0]
+    if y is None:
+        y = torch.empty((R_max, H), dtype=torch.uint16, device=hq.device)
+    nws = int(lib.moe_grouped_workspace_size(R_max, G, H, I))
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=hq.device)
+    _check(lib.moe_grouped_w2(w2.ref(), _wref(w2_shared), _p(counts), _p(offsets), _p(hq), _p(hs),
+                              R_max, H, I, G, _p(y), _p(ws), nws, _stream(stream)), "moe_grouped_w2")
+    return y
+
+
+# ----------------------------------------------------------------- combine
+def moe_combine(y, slot_row, H: int, row_w=None, out=None, stream=None):
+    T, ks = slot_row.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.uint16, device=y.device)
+    _check(lib.moe_combine(_p(y), _p(slot_row), _p(row_w), T, ks, H, _p(out), _stream(stream)),
+           "moe_combine")
+    return out
+
+
+# ------------------------------------------------------------------- layer
+_NAMES = ["topk_idx", "topk_w", "counts", "offsets", "offsets32", "row_src", "row_w", "slot_row",
+          "xq_perm", "xs_perm", "hq", "hs", "y", "scratch"]
+
+
+class LayerWorkspace:
+    """Device workspace of moe_layer plus views of its intermediates."""
+
+    def __init__(self, T, E_tot, k, E_loc, H, I, shared=False, flags=0, device="cuda"):
+        s = int(bool(shared))
+        self.shape = (T, E_tot, k, E_loc, H, I, s, flags)
+        self.nbytes = int(lib.moe_layer_workspace_size(T, E_tot, k, E_loc, H, I, s, flags))
+        self.buf = torch.empty(max(self.nbytes, 1), dtype=torch.uint8, device=device)
+        offs = (C.c_size_t * 14)()
+        lib.moe_layer_workspace_offsets(T, E_tot, k, E_loc, H, I, s, flags, offs)
+        self.offsets = list(offs)
+
+    def view(self, name: str) -> torch.Tensor:
+        T, E_tot, k, E_loc, H, I, s, _ = self.shape
+        R = T * k + s * T
+        G = E_loc + s
+        shapes = {
+            "topk_idx": ((T, k), torch.int32), "topk_w": ((T, k), torch.float32),
+            "counts": ((G,), torch.int32), "offsets": ((G + 1,), torch.int32),
+            "offsets32": ((G + 1,), torch.int32), "row_src": ((R,), torch.int32),
+            "row_w": ((R,), torch.float32), "slot_row": ((T, k + s), torch.int32),
+            "xq_perm": ((R, H), torch.uint8), "xs_perm": ((R, H // 32), torch.uint8),
+            "hq": ((R, I), torch.uint8), "hs": ((R, I // 32), torch.uint8),
+            "y": ((R, H), torch.uint16),
+        }
+        shp, dt = shapes[name]
+        o = self.offsets[_NAMES.index(name)]
+        n = 1
+        for d in shp:
+            n *= d
+        nbytes = n * torch.tensor([], dtype=dt).element_size()
+        return self.buf[o:o + nbytes].view(dt).view(shp)
+
+
+def moe_layer(logits, xq, xs, w1: PackedWeights, w2: PackedWeights, k: int, e0: int = 0,
+              n_local: int | None = None, shared=None, flags: int = 0, out=None, ws=None,
+              hTq=None, hTs=None, stream=None):
+    """Whole layer. shared = (PackedWeights W1, PackedWeights W2) or None.
+    Returns out (bf16 bits as uint16 [T, H])."""
+    _dev(logits, torch.float32, "logits")
+    _dev(xq, torch.uint8, "xq")
+    _dev(xs, torch.uint8, "xs")
+    T, E_tot = logits.shape
+    H = xq.shape[1]
+    I = w1.N // 2
+    n_local = w1.G if n_local is None else n_local
+    s = 1 if shared is not None else 0
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.uint16, device=xq.device)
+    if ws is None:
+        ws = LayerWorkspace(T, E_tot, k, n_local, H, I, bool(s), flags, device=xq.device)
+    args = moe_layer_args()
+    args.logits, args.T, args.E_tot, args.k = _p(logits), T, E_tot, k
+    args.e0, args.E_loc = e0, n_local
+    args.xq, args.xs, args.H, args.I = _p(xq), _p(xs), H, I
+    args.w1, args.w2 = C.pointer(w1.desc), C.pointer(w2.desc)
+    if shared is not None:
+        args.shared_w1, args.shared_w2 = C.pointer(shared[0].desc), C.pointer(shared[1].desc)
+    args.flags = flags
+    args.hTq, args.hTs = _p(hTq), _p(hTs)
+    args.out = _p(out)
+    _check(lib.moe_layer(C.byref(args), _p(ws.buf), ws.nbytes, _stream(stream)), "moe_layer")
+    return out

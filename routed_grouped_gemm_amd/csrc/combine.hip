@@ -1,0 +1,50 @@
+// S7: combine. out[t] = BF16(sum over the token's local slots of its BF16 rows),
+// summed in fp64 in slot order and rounded once (GC-MoE page, "Approach":
+// the finalize role combines the BF16 fragments into token order).
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVec = 8;                 // bf16 per thread per pass (16 bytes)
+
+__global__ __launch_bounds__(kThreads)
+void combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ slot_row,
+                    const float* __restrict__ row_w, int ks, int H, uint16_t* __restrict__ out) {
+    const int t = blockIdx.x;
+    const int h0 = (blockIdx.y * kThreads + threadIdx.x) * kVec;
+    if (h0 >= H) return;
+    double acc[kVec];
+    #pragma unroll
+    for (int i = 0; i < kVec; ++i) acc[i] = 0.0;
+    const int32_t* sr = slot_row + (size_t)t * ks;
+    for (int j = 0; j < ks; ++j) {
+        const int r = sr[j];
+        if (r < 0) continue;
+        const double w = row_w ? (double)row_w[r] : 1.0;
+        const uint4 v = *(const uint4*)(y + (size_t)r * H + h0);
+        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i]     += (double)bf16_to_f32(p[i] & 0xFFFFu) * w;
+            acc[2 * i + 1] += (double)bf16_to_f32(p[i] >> 16) * w;
+        }
+    }
+    uint4 o;
+    uint32_t q[4];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = f64_to_bf16(acc[2 * i]) | (f64_to_bf16(acc[2 * i + 1]) << 16);
+    o.x = q[0]; o.y = q[1]; o.z = q[2]; o.w = q[3];
+    *(uint4*)(out + (size_t)t * H + h0) = o;
+}
+
+}  // namespace
+
+int moe_launch_combine(const uint16_t* y, const int32_t* slot_row, const float* row_w, int T,
+                       int ks, int H, uint16_t* out, hipStream_t stream) {
+    if (T == 0) return 0;
+    dim3 grid(T, (H / kVec + kThreads - 1) / kThreads), block(kThreads);
+    hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, y, slot_row, row_w, ks, H, out);
+    return (int)hipGetLastError();
+}

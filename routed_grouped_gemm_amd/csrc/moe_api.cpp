@@ -1,0 +1,346 @@
+// C ABI of libmoe: argument validation, workspace carving and the launch
+// sequence of the layer. Validation touches no HIP API, so argument errors can
+// be checked on a machine without a GPU; nothing here allocates device memory,
+// synchronises or reads device data.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+inline int32_t hip_status(int e) { return e == 0 ? MOE_OK : MOE_ERR_HIP; }
+
+bool fmt_ok(int fmt) { return fmt == MOE_FMT_MXFP4 || fmt == MOE_FMT_MXFP8; }
+
+int32_t check_weights(const moe_weights* w, int G, int N, int K, int is_w1) {
+    if (!w || !w->data) return MOE_ERR_NULL;
+    if (!fmt_ok(w->fmt)) return MOE_ERR_UNSUPPORTED;
+    if (w->G != G || w->N != N || w->K != K || w->is_w1 != is_w1) return MOE_ERR_SHAPE;
+    if (w->bytes < moe_prepacked_size(G, N, K, w->fmt)) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+// Workspace layout of moe_layer (all regions 256-byte aligned).
+struct LayerLayout {
+    size_t off[14];
+    size_t total;
+};
+
+LayerLayout layer_layout(int T, int E_tot, int k, int E_loc, int H, int I, int s) {
+    (void)E_tot;
+    const size_t R = (size_t)T * k + (size_t)s * T;
+    const int G = E_loc + s;
+    size_t sz[14] = {
+        (size_t)T * k * 4,            // topk_idx
+        (size_t)T * k * 4,            // topk_w
+        (size_t)G * 4,                // counts
+        (size_t)(G + 1) * 4,          // offsets
+        (size_t)(G + 1) * 4,          // offsets32
+        R * 4,                        // row_src
+        R * 4,                        // row_w
+        (size_t)T * (k + s) * 4,      // slot_row
+        R * H,                        // xq_perm
+        R * (H / 32),                 // xs_perm
+        R * I,                        // hq
+        R * (I / 32),                 // hs
+        R * H * 2,                    // y
+        0,                            // scratch
+    };
+    size_t gws1 = moe_grouped_workspace_size((int)R, G, 2 * I, H);
+    size_t gws2 = moe_grouped_workspace_size((int)R, G, H, I);
+    size_t pws = moe_permute_workspace_size(T, k, G);
+    size_t scr = pws > gws1 ? pws : gws1;
+    sz[13] = scr > gws2 ? scr : gws2;
+    LayerLayout L;
+    size_t o = 0;
+    for (int i = 0; i < 14; ++i) {
+        L.off[i] = o;
+        o += align_up(sz[i]);
+    }
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+MOE_EXPORT const char* moe_status_string(int32_t status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "a size violates the layer's limits";
+        case MOE_ERR_UNSUPPORTED: return "unsupported format or flag combination";
+        case MOE_ERR_WORKSPACE: return "workspace or destination buffer too small";
+        case MOE_ERR_HIP: return "a HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+MOE_EXPORT const char* moe_version(void) { return "moe-mi355x 0.1.0 gfx950"; }
+
+// ---------------------------------------------------------------- weights
+MOE_EXPORT size_t moe_prepacked_size(int32_t G, int32_t N, int32_t K, int32_t fmt) {
+    if (G < 0 || N <= 0 || K <= 0 || N % 64 || K % 128 || !fmt_ok(fmt)) return 0;
+    return moe_pack_geom(G, N, K, fmt).total;
+}
+
+MOE_EXPORT int32_t moe_prepack_weights(const uint8_t* q, const uint8_t* sc, int32_t G, int32_t N,
+                                       int32_t K, int32_t fmt, int32_t is_w1, void* dst,
+                                       size_t dst_bytes, hipStream_t stream) {
+    if (!fmt_ok(fmt)) return MOE_ERR_UNSUPPORTED;
+    if (G < 0 || N <= 0 || K <= 0 || N % 64 || K % 128) return MOE_ERR_SHAPE;
+    if (is_w1 && ((N / 2) % 32)) return MOE_ERR_SHAPE;
+    if (G == 0) return MOE_OK;
+    if (!q || !sc || !dst) return MOE_ERR_NULL;
+    if (dst_bytes < moe_prepacked_size(G, N, K, fmt)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe_launch_prepack(q, sc, G, N, K, fmt, is_w1, (uint8_t*)dst, stream));
+}
+
+MOE_EXPORT int32_t moe_quantize_mx(const float* src, int32_t rows, int32_t K, int32_t fmt,
+                                   uint32_t flags, uint8_t* q, uint8_t* s, hipStream_t stream) {
+    if (!fmt_ok(fmt)) return MOE_ERR_UNSUPPORTED;
+    if (rows < 0 || K <= 0 || K % 32) return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!src || !q || !s) return MOE_ERR_NULL;
+    return hip_status(moe_launch_quantize(src, rows, K, fmt, flags, q, s, stream));
+}
+
+// ------------------------------------------------------------------ route
+MOE_EXPORT int32_t moe_route(const float* logits, int32_t T, int32_t E_tot, int32_t k,
+                             uint32_t flags, int32_t* topk_idx, float* topk_w,
+                             hipStream_t stream) {
+    if (T < 0 || E_tot < 1 || E_tot > MOE_MAX_EXPERTS || k < 1 || k > E_tot || k > MOE_MAX_SLOTS)
+        return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_idx || !topk_w) return MOE_ERR_NULL;
+    return hip_status(moe_launch_route(logits, T, E_tot, k, flags, topk_idx, topk_w, stream));
+}
+
+// ---------------------------------------------------------------- permute
+MOE_EXPORT size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t G) {
+    if (T < 0 || k < 1 || G < 1) return 0;
+    return moe_permute_scratch_bytes(T, k, G);
+}
+
+static int32_t check_permute(int T, int k, int e0, int E_loc, int s, int H) {
+    if (T < 0 || k < 1 || E_loc < 1 || e0 < 0 || (s != 0 && s != 1)) return MOE_ERR_SHAPE;
+    if (k + s > MOE_MAX_SLOTS || e0 + E_loc > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+    if (H <= 0 || H % 256) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+MOE_EXPORT int32_t moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t k,
+                               int32_t e0, int32_t E_loc, int32_t s, const uint8_t* xq,
+                               const uint8_t* xs, int32_t H, int32_t* counts, int32_t* offsets,
+                               int32_t* offsets32, int32_t* row_src, float* row_w,
+                               int32_t* slot_row, uint8_t* xq_perm, uint8_t* xs_perm, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_permute(T, k, e0, E_loc, s, H);
+    if (st) return st;
+    if (!counts || !offsets || !row_src || !row_w || !slot_row) return MOE_ERR_NULL;
+    if (T > 0 && (!topk_idx || !topk_w)) return MOE_ERR_NULL;
+    if (xq_perm && (!xs_perm || !xq || !xs)) return MOE_ERR_NULL;
+    const size_t need = moe_permute_workspace_size(T, k, E_loc + s);
+    if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe_launch_permute(topk_idx, topk_w, T, k, e0, E_loc, s, xq, xs, H, counts,
+                                         offsets, offsets32, row_src, row_w, slot_row, xq_perm,
+                                         xs_perm, ws, stream));
+}
+
+// ---------------------------------------------------------------- grouped
+MOE_EXPORT int32_t moe_transposed_ld(int32_t R_max, int32_t G) {
+    if (R_max < 0 || G < 0) return 0;
+    return (R_max + 31 * G + 31) & ~31;
+}
+
+MOE_EXPORT size_t moe_grouped_workspace_size(int32_t R_max, int32_t G, int32_t N, int32_t K) {
+    (void)R_max; (void)G; (void)N; (void)K;
+    return 0;
+}
+
+static int32_t fill_gemm_args(GemmArgs& a, const moe_weights* w, const moe_weights* wsh, int G,
+                              int N, int K, int is_w1) {
+    const int s = (wsh != nullptr) ? 1 : 0;
+    const int E_loc = G - s;
+    if (E_loc < 1) return MOE_ERR_SHAPE;
+    int32_t st = check_weights(w, E_loc, N, K, is_w1);
+    if (st) return st;
+    if (wsh) {
+        st = check_weights(wsh, 1, N, K, is_w1);
+        if (st) return st;
+        if (wsh->fmt != w->fmt) return MOE_ERR_UNSUPPORTED;
+    }
+    a.w_base[0] = (const uint8_t*)w->data;
+    a.w_base[1] = wsh ? (const uint8_t*)wsh->data : a.w_base[0];
+    a.E_loc = E_loc; a.G = G; a.N = N; a.K = K; a.fmt = w->fmt;
+    return MOE_OK;
+}
+
+static int32_t check_hi(int H, int I) {
+    if (H <= 0 || H % 256 || I <= 0 || I % 128 || I > MOE_MAX_I) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shared,
+                               const int32_t* counts, const int32_t* offsets,
+                               const int32_t* offsets32, const float* row_w,
+                               const uint8_t* xq_perm, const uint8_t* xs_perm, int32_t R_max,
+                               int32_t H, int32_t I, int32_t G, uint32_t flags, uint8_t* hq,
+                               uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes,
+                               int rows_hint, hipStream_t stream) {
+    int32_t st = check_hi(H, I);
+    if (st) return st;
+    if (R_max < 0 || G < 1 || G > MOE_MAX_EXPERTS + 1) return MOE_ERR_SHAPE;
+    GemmArgs a{};
+    st = fill_gemm_args(a, w1, w1_shared, G, 2 * I, H, 1);
+    if (st) return st;
+    if (!counts || !offsets || !xq_perm || !xs_perm || !hq || !hs) return MOE_ERR_NULL;
+    const bool transpose = (flags & MOE_W1_WRITE_TRANSPOSE) != 0;
+    if (transpose && (!hTq || !hTs || !offsets32)) return MOE_ERR_NULL;
+    if (!(flags & MOE_WEIGHT_AT_COMBINE) && !row_w) return MOE_ERR_NULL;
+    const size_t need = moe_grouped_workspace_size(R_max, G, 2 * I, H);
+    if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
+    a.counts = counts; a.offsets = offsets; a.offsets32 = offsets32; a.row_w = row_w;
+    a.aq = xq_perm; a.as = xs_perm; a.R_max = R_max; a.rows_hint = rows_hint; a.flags = flags;
+    a.hq = hq; a.hs = hs; a.hTq = hTq; a.hTs = hTs; a.ldT = moe_transposed_ld(R_max, G);
+    return hip_status(moe_launch_grouped_w1(a, stream));
+}
+
+MOE_EXPORT int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_shared,
+                                  const int32_t* counts, const int32_t* offsets,
+                                  const int32_t* offsets32, const float* row_w,
+                                  const uint8_t* xq_perm, const uint8_t* xs_perm, int32_t R_max,
+                                  int32_t H, int32_t I, int32_t G, uint32_t flags, uint8_t* hq,
+                                  uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    return grouped_w1_impl(w1, w1_shared, counts, offsets, offsets32, row_w, xq_perm, xs_perm,
+                           R_max, H, I, G, flags, hq, hs, hTq, hTs, ws, ws_bytes, 0, stream);
+}
+
+static int32_t grouped_w2_impl(const moe_weights* w2, const moe_weights* w2_shared,
+                               const int32_t* counts, const int32_t* offsets, const uint8_t* hq,
+                               const uint8_t* hs, int32_t R_max, int32_t H, int32_t I, int32_t G,
+                               uint16_t* y, void* ws, size_t ws_bytes, int rows_hint,
+                               hipStream_t stream) {
+    int32_t st = check_hi(H, I);
+    if (st) return st;
+    if (R_max < 0 || G < 1 || G > MOE_MAX_EXPERTS + 1) return MOE_ERR_SHAPE;
+    GemmArgs a{};
+    st = fill_gemm_args(a, w2, w2_shared, G, H, I, 0);
+    if (st) return st;
+    if (!counts || !offsets || !hq || !hs || !y) return MOE_ERR_NULL;
+    const size_t need = moe_grouped_workspace_size(R_max, G, H, I);
+    if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
+    a.counts = counts; a.offsets = offsets; a.aq = hq; a.as = hs; a.R_max = R_max;
+    a.rows_hint = rows_hint; a.y = y;
+    return hip_status(moe_launch_grouped_w2(a, stream));
+}
+
+MOE_EXPORT int32_t moe_grouped_w2(const moe_weights* w2, const moe_weights* w2_shared,
+                                  const int32_t* counts, const int32_t* offsets, const uint8_t* hq,
+                                  const uint8_t* hs, int32_t R_max, int32_t H, int32_t I,
+                                  int32_t G, uint16_t* y, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+    return grouped_w2_impl(w2, w2_shared, counts, offsets, hq, hs, R_max, H, I, G, y, ws, ws_bytes,
+                           0, stream);
+}
+
+// ---------------------------------------------------------------- combine
+MOE_EXPORT int32_t moe_combine(const uint16_t* y, const int32_t* slot_row, const float* row_w,
+                               int32_t T, int32_t k_plus_s, int32_t H, uint16_t* out,
+                               hipStream_t stream) {
+    if (T < 0 || k_plus_s < 1 || k_plus_s > MOE_MAX_SLOTS || H <= 0 || H % 8) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!y || !slot_row || !out) return MOE_ERR_NULL;
+    return hip_status(moe_launch_combine(y, slot_row, row_w, T, k_plus_s, H, out, stream));
+}
+
+// ------------------------------------------------------------------ layer
+MOE_EXPORT size_t moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
+                                           int32_t H, int32_t I, int32_t s, uint32_t flags) {
+    (void)flags;
+    if (T < 0 || k < 1 || E_loc < 1 || H <= 0 || I <= 0 || (s != 0 && s != 1)) return 0;
+    return layer_layout(T, E_tot, k, E_loc, H, I, s).total;
+}
+
+MOE_EXPORT int32_t moe_layer_workspace_offsets(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
+                                               int32_t H, int32_t I, int32_t s, uint32_t flags,
+                                               size_t* offsets14) {
+    (void)flags;
+    if (!offsets14) return 0;
+    LayerLayout L = layer_layout(T, E_tot, k, E_loc, H, I, s);
+    memcpy(offsets14, L.off, sizeof(L.off));
+    return 14;
+}
+
+MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    if (!a) return MOE_ERR_NULL;
+    const int T = a->T, E_tot = a->E_tot, k = a->k, e0 = a->e0, E_loc = a->E_loc;
+    const int H = a->H, I = a->I;
+    const int s = a->shared_w1 ? 1 : 0;
+    if ((a->shared_w1 == nullptr) != (a->shared_w2 == nullptr)) return MOE_ERR_NULL;
+    if (T < 0 || E_tot < 1 || E_tot > MOE_MAX_EXPERTS || k < 1 || k > E_tot) return MOE_ERR_SHAPE;
+    if (e0 < 0 || E_loc < 1 || e0 + E_loc > E_tot || k + s > MOE_MAX_SLOTS) return MOE_ERR_SHAPE;
+    int32_t st = check_hi(H, I);
+    if (st) return st;
+    const int G = E_loc + s;
+    st = check_weights(a->w1, E_loc, 2 * I, H, 1);
+    if (st) return st;
+    st = check_weights(a->w2, E_loc, H, I, 0);
+    if (st) return st;
+    if (s) {
+        if ((st = check_weights(a->shared_w1, 1, 2 * I, H, 1))) return st;
+        if ((st = check_weights(a->shared_w2, 1, H, I, 0))) return st;
+        if (a->shared_w1->fmt != a->w1->fmt || a->shared_w2->fmt != a->w2->fmt)
+            return MOE_ERR_UNSUPPORTED;
+    }
+    const bool transpose = (a->flags & MOE_W1_WRITE_TRANSPOSE) != 0;
+    if (transpose && (!a->hTq || !a->hTs)) return MOE_ERR_NULL;
+    if (T == 0) return MOE_OK;
+    if (!a->logits || !a->xq || !a->xs || !a->out) return MOE_ERR_NULL;
+    const LayerLayout L = layer_layout(T, E_tot, k, E_loc, H, I, s);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+    char* base = (char*)ws;
+    int32_t* topk_idx = (int32_t*)(base + L.off[0]);
+    float* topk_w = (float*)(base + L.off[1]);
+    int32_t* counts = (int32_t*)(base + L.off[2]);
+    int32_t* offsets = (int32_t*)(base + L.off[3]);
+    int32_t* offsets32 = (int32_t*)(base + L.off[4]);
+    int32_t* row_src = (int32_t*)(base + L.off[5]);
+    float* row_w = (float*)(base + L.off[6]);
+    int32_t* slot_row = (int32_t*)(base + L.off[7]);
+    uint8_t* xq_perm = (uint8_t*)(base + L.off[8]);
+    uint8_t* xs_perm = (uint8_t*)(base + L.off[9]);
+    uint8_t* hq = (uint8_t*)(base + L.off[10]);
+    uint8_t* hs = (uint8_t*)(base + L.off[11]);
+    uint16_t* y = (uint16_t*)(base + L.off[12]);
+    void* scratch = base + L.off[13];
+    const size_t scratch_bytes = L.total - L.off[13];
+    const int R_max = T * k + s * T;
+
+    int e = moe_launch_route(a->logits, T, E_tot, k, a->flags, topk_idx, topk_w, stream);
+    if (e) return MOE_ERR_HIP;
+    e = moe_launch_permute(topk_idx, topk_w, T, k, e0, E_loc, s, a->xq, a->xs, H, counts, offsets,
+                           offsets32, row_src, row_w, slot_row, xq_perm, xs_perm, scratch, stream);
+    if (e) return MOE_ERR_HIP;
+    // expected rows of a routed group under uniform routing; the shared group
+    // (T rows) gets more passes from the grid's pass dimension
+    const int hint = (T * k + E_tot - 1) / E_tot;
+    st = grouped_w1_impl(a->w1, a->shared_w1, counts, offsets, offsets32, row_w, xq_perm, xs_perm,
+                         R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch, scratch_bytes,
+                         hint, stream);
+    if (st) return st;
+    st = grouped_w2_impl(a->w2, a->shared_w2, counts, offsets, hq, hs, R_max, H, I, G, y, scratch,
+                         scratch_bytes, hint, stream);
+    if (st) return st;
+    const bool wc = (a->flags & MOE_WEIGHT_AT_COMBINE) != 0;
+    e = moe_launch_combine(y, slot_row, wc ? row_w : nullptr, T, k + s, H, a->out, stream);
+    return hip_status(e);
+}

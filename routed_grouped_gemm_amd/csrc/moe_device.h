@@ -1,0 +1,121 @@
+// Device-side building blocks shared by the libmoe kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int   i32x4  __attribute__((ext_vector_type(4)));
+typedef int   i32x8  __attribute__((ext_vector_type(8)));
+typedef float f32x4  __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define MOE_DEV __device__ __forceinline__
+
+// Operand format selectors of V_MFMA_SCALE_F32_*_F8F6F4 (cbsz / blgp fields).
+enum { MFMA_FMT_FP8 = 0, MFMA_FMT_FP4 = 4 };
+
+// ---------------------------------------------------------------------------
+// Scaled MFMA, 16x16x128. Measured operand layout on gfx950 (G = 4 lane groups):
+//   lane l -> row (A) / column (B) l % 16, lane group g = l / 16.
+//   FP4 operand: the lane's 16 bytes are K [32g, 32g+32), element 2i in the low nibble.
+//   FP8 operand: bytes 0..15 are K [16g, 16g+16), bytes 16..31 are K [64+16g, 64+16g+16).
+//   Scale: the lane's selected E8M0 byte scales K-block g (K [32g, 32g+32)) of its row.
+//   Result: lane l holds D[4*(l/16) + v][l % 16], v = 0..3.
+// ---------------------------------------------------------------------------
+template <int FA, int FB, int SELA, int SELB>
+MOE_DEV f32x4 mfma16x16x128(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, SELA, sa, SELB, sb);
+}
+
+// ---------------------------------------------------------------------------
+// Number conversions (OCP MX v1.0 element rules), all exact bit manipulation.
+// ---------------------------------------------------------------------------
+
+// fp32 (finite) -> E4M3 code, round to nearest even, saturating to +-448; the
+// sign bit follows the input's sign bit.
+MOE_DEV uint32_t f32_to_e4m3(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t s = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t c;
+    if (a < 0x3C800000u) {                         // |v| < 2^-6: subnormal grid, step 2^-9
+        c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    } else {
+        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);  // RNE to 3 mantissa bits
+        c = (r >> 20) - (120u << 3);               // rebias exponent 127 -> 7
+        c = c > 0x7Eu ? 0x7Eu : c;
+    }
+    return s | c;
+}
+
+// fp32 (finite) -> E2M1 code (0..15), round to nearest even, saturating to +-6.
+MOE_DEV uint32_t f32_to_e2m1(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t s = (u >> 28) & 0x8u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t c;
+    if (a < 0x3F800000u) {                         // |v| < 1: subnormal grid, step 0.5
+        c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
+    } else {
+        uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);  // RNE to 1 mantissa bit
+        c = (r >> 22) - (126u << 1);               // rebias exponent 127 -> 1
+        c = c > 0x7u ? 0x7u : c;
+    }
+    return s | c;
+}
+
+// E8M0 scale code of a block from its amax (>= 0, finite).
+//  OCP rule:  E = floor(log2 amax) - emax_elem, clamped to [-127, 127]; code = E + 127.
+//  ceil rule: E = ceil(log2(amax / max_finite)).
+// A zero or fp32-subnormal amax gives code 0.
+template <int EMAX, uint32_t MAXMANT>
+MOE_DEV uint32_t mx_scale_code(float amax, bool ceil_rule) {
+    uint32_t u = __float_as_uint(amax);
+    int e32 = (int)(u >> 23);                      // biased exponent; 0 for zero/subnormal
+    if (e32 == 0) return 0u;
+    int code = e32 - EMAX;                         // (e32 - 127 - EMAX) + 127
+    if (ceil_rule) {
+        // amax <= max_finite * 2^(e-emax) iff its mantissa <= the max element's mantissa
+        // max_finite = (1 + MAXMANT/2^23) * 2^EMAX
+        code += ((u & 0x7FFFFFu) > MAXMANT) ? 1 : 0;
+    }
+    code = code < 0 ? 0 : (code > 254 ? 254 : code);
+    return (uint32_t)code;
+}
+// E4M3: emax 8, max 448 = 1.75 * 2^8 (mantissa 0x600000); E2M1: emax 2, max 6 = 1.5 * 2^2.
+MOE_DEV uint32_t e4m3_scale_code(float amax, bool ceil_rule) { return mx_scale_code<8, 0x600000u>(amax, ceil_rule); }
+MOE_DEV uint32_t e2m1_scale_code(float amax, bool ceil_rule) { return mx_scale_code<2, 0x400000u>(amax, ceil_rule); }
+
+// 2^(127 - code): multiplying by it divides by the block scale, exactly.
+MOE_DEV float inv_scale(uint32_t code) { return __uint_as_float((254u - code) << 23); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+MOE_DEV uint32_t f32_to_bf16(float v) {
+    uint32_t u = __float_as_uint(v);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+MOE_DEV float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp64 -> bf16 bits with a single rounding (nearest even): round to fp32 with
+// round-to-odd (sticky last bit), then to bf16 with nearest-even. fp32 keeps
+// 24 >= 8 + 2 significant bits, so the result equals direct rounding.
+MOE_DEV uint32_t f64_to_bf16(double d) {
+    float f = (float)d;
+    if ((double)f != d) {
+        uint32_t u = __float_as_uint(f);
+        if ((u & 1u) == 0u) {
+            // f was rounded to an even neighbour: step one ulp towards d
+            bool mag_up = fabs(d) > fabs((double)f);
+            u = mag_up ? u + 1u : u - 1u;
+            if ((__float_as_uint(f) & 0x7FFFFFFFu) == 0u) u = (d < 0 ? 0x80000001u : 1u);
+        }
+        f = __uint_as_float(u);
+    }
+    return f32_to_bf16(f);
+}
+
+MOE_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Wave-wide helpers (wave64).
+MOE_DEV float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+
+MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }

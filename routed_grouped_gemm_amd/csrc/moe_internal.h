@@ -1,0 +1,58 @@
+// Internal launcher interface between the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+#include "../../include/moe.h"
+
+// Prepacked weight geometry (see prepack.hip): 64-row units, 128-wide K tiles.
+struct PackGeom {
+    int units;        // N / 64
+    int kt;           // K / 128
+    int kt4;          // ceil(kt / 4)
+    int bpl;          // bytes per lane per 16x128 tile: 16 (FP4) or 32 (FP8)
+    size_t data_per_unit;   // kt * 4 tiles * 64 lanes * bpl
+    size_t scale_per_unit;  // kt4 * 4 tiles * 64 lanes * 4
+    size_t data_per_group, scale_per_group;
+    size_t group_stride;    // data_per_group + scale_per_group (scales follow the data)
+    size_t total;
+};
+PackGeom moe_pack_geom(int G, int N, int K, int fmt);
+
+// Launchers return 0 or a hipError_t value.
+int moe_launch_route(const float* logits, int T, int E, int k, uint32_t flags,
+                     int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+size_t moe_permute_scratch_bytes(int T, int k, int G);
+int moe_launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int k, int e0,
+                       int E_loc, int s, const uint8_t* xq, const uint8_t* xs, int H,
+                       int32_t* counts, int32_t* offsets, int32_t* offsets32, int32_t* row_src,
+                       float* row_w, int32_t* slot_row, uint8_t* xq_perm, uint8_t* xs_perm,
+                       void* scratch, hipStream_t stream);
+
+struct GemmArgs {
+    const uint8_t* w_base[2];    // prepacked routed groups, shared group
+    int E_loc;                   // groups < E_loc use [0], group E_loc uses [1]
+    int G, N, K, fmt;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* offsets32;
+    const float* row_w;          // W1 only; null = weight 1
+    const uint8_t* aq;           // activations [R_max, K] E4M3
+    const uint8_t* as;           // [R_max, K/32]
+    int R_max;
+    int rows_hint;               // expected rows per group (0: R_max / G)
+    uint32_t flags;
+    uint8_t* hq; uint8_t* hs;    // W1 outputs
+    uint8_t* hTq; uint8_t* hTs; int ldT;
+    uint16_t* y;                 // W2 output
+};
+int moe_launch_grouped_w1(const GemmArgs& a, hipStream_t stream);
+int moe_launch_grouped_w2(const GemmArgs& a, hipStream_t stream);
+
+int moe_launch_combine(const uint16_t* y, const int32_t* slot_row, const float* row_w, int T,
+                       int ks, int H, uint16_t* out, hipStream_t stream);
+int moe_launch_quantize(const float* src, int rows, int K, int fmt, uint32_t flags,
+                        uint8_t* q, uint8_t* s, hipStream_t stream);
+int moe_launch_prepack(const uint8_t* q, const uint8_t* sc, int G, int N, int K, int fmt,
+                       int is_w1, uint8_t* dst, hipStream_t stream);

@@ -1,0 +1,104 @@
+"""Helpers for the GPU parity tests: device upload of oracle-made inputs and
+the comparison rules. Imported only by tests marked `gpu`."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import mx
+
+DEV = "cuda"
+
+
+def banner(msg: str) -> None:
+    """Name the case before each GPU step so a failing run says which it was."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return host(t).view(np.uint16)
+
+
+# ------------------------------------------------------------------ rules
+def e4m3_ulp(mag_scaled: np.ndarray) -> np.ndarray:
+    """Grid spacing of E4M3 at a scaled magnitude (value / block scale)."""
+    m = np.maximum(mag_scaled, 2.0 ** -6)
+    e = np.floor(np.log2(m))
+    return np.ldexp(1.0, (e - 3).astype(np.int32))
+
+
+# Bound on the scaled MFMA's inner-sum error relative to the sum of |terms| of
+# a dot product: the hardware does not accumulate like an IEEE fp32 FMA chain
+# (probe: up to 2.6e-4 for random full-range FP8 bytes, about 1.5e-6 for
+# MX-quantised Gaussian data); 2^-12 covers both.
+MFMA_REL = 2.0 ** -12
+
+
+def assert_mx_within_1ulp(q_gpu, s_gpu, q_ref, s_ref, what: str, max_frac_diff: float = 0.02,
+                          extra_tol=None):
+    """FP8 requantised values may differ by at most one E4M3 step at the
+    coarser of the two block scales (plus `extra_tol`, the propagated bound of
+    the fp32 accumulation, where given); report how many codes/scales differ."""
+    q_gpu, s_gpu = np.asarray(q_gpu), np.asarray(s_gpu)
+    q_ref, s_ref = np.asarray(q_ref), np.asarray(s_ref)
+    assert q_gpu.shape == q_ref.shape and s_gpu.shape == s_ref.shape, (what, q_gpu.shape, q_ref.shape)
+    a = mx.dequantize_mx(q_gpu, s_gpu, mx.FMT_E4M3)
+    b = mx.dequantize_mx(q_ref, s_ref, mx.FMT_E4M3)
+    X = np.repeat(np.maximum(mx.decode_e8m0(s_gpu), mx.decode_e8m0(s_ref)), 32, axis=-1)
+    tol = e4m3_ulp(np.maximum(np.abs(a), np.abs(b)) / X) * X
+    if extra_tol is not None:
+        tol = tol + extra_tol
+    bad = np.abs(a - b) > tol * (1 + 1e-12)
+    frac_q = float(np.mean(q_gpu != q_ref)) if q_gpu.size else 0.0
+    frac_s = float(np.mean(s_gpu != s_ref)) if s_gpu.size else 0.0
+    print(f"  {what}: codes differing {frac_q:.2e}, scales differing {frac_s:.2e}, "
+          f"beyond 1 ulp {int(bad.sum())}", flush=True)
+    assert not bad.any(), f"{what}: {int(bad.sum())} values beyond 1 E4M3 ulp"
+    assert frac_q <= max_frac_diff, f"{what}: {frac_q:.3f} of codes differ"
+
+
+def assert_bf16_close(got_bits, ref_bits, what: str, max_ulp: int = 1, abs_floor=None):
+    """|got - ref| <= max_ulp BF16 steps of |ref| (or abs_floor, whichever is larger)."""
+    g = mx.bf16_value(got_bits)
+    r = mx.bf16_value(ref_bits)
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(r), 2.0 ** -126))[1] - 8)
+    tol = max_ulp * ulp
+    if abs_floor is not None:
+        tol = np.maximum(tol, abs_floor)
+    bad = np.abs(g - r) > tol
+    print(f"  {what}: bits equal {float(np.mean(got_bits == ref_bits)):.4f}, beyond tol {int(bad.sum())}",
+          flush=True)
+    assert not bad.any(), f"{what}: {int(bad.sum())} values beyond tolerance"
+
+
+def rel_l2_cos(got: np.ndarray, ref: np.ndarray):
+    got = got.astype(np.float64).ravel()
+    ref = ref.astype(np.float64).ravel()
+    nr = np.linalg.norm(ref)
+    rel = np.linalg.norm(got - ref) / max(nr, 1e-300)
+    cos = float(got @ ref / max(np.linalg.norm(got) * nr, 1e-300))
+    return rel, cos
+
+
+def assert_layer_close(got_bits, ref_bits, what: str, rel_max=2e-2, cos_min=0.999):
+    """The layer-output bar: rel-L2 <= 2e-2 and cosine >= 0.999."""
+    g, r = mx.bf16_value(got_bits), mx.bf16_value(ref_bits)
+    rel, cos = rel_l2_cos(g, r)
+    eq = float(np.mean(np.asarray(got_bits) == np.asarray(ref_bits)))
+    print(f"  {what}: rel-L2 {rel:.3e} cosine {cos:.7f} bits equal {eq:.4f}", flush=True)
+    if np.linalg.norm(r) == 0:
+        assert np.all(g == 0), what
+        return
+    assert rel <= rel_max and cos >= cos_min, f"{what}: rel-L2 {rel:.3e} cosine {cos:.6f}"
