@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of the routed MoE layer on MI355X.
+
+Workload: the decode share of a large MoE (H=7168, I=2048, top-8 over 256
+experts, this GPU holding experts 0..31, FP8 activations x MXFP4 weights).
+One step runs the whole layer (route, permute, grouped W1 + fused epilogue,
+grouped W2, combine) once for each decode batch T in {1, 8, 32, 128}, each
+call on a new routing draw (logits and x) over the same experts. The weights
+are held in several identical copies and consecutive calls rotate through
+them, as consecutive MoE layers of a model would, so a call never finds the
+previous call's weights in the 256 MB last-level cache.
+
+Printed JSON line (stdout): value = algorithmic HBM bytes of the step's layer
+calls / wall time of the step, in TB/s. Algorithmic bytes per call: router
+logits, x codes + scales, the W1 and W2 codes + scales of the experts that
+received at least one token, and the BF16 output. The "roofline" object is
+for the dominant kernel (the grouped W1 GEMM), timed with HIP events around
+its launches on the launching stream; "cpu_baseline" times the CPU oracle on
+a bounded sample (the T=8 call of one routing draw).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DECODE_T = (1, 8, 32, 128)
+N_VARIANTS = 16
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes_per_group(H: int, I: int, fp4: bool) -> int:
+    """W1 [2I, H] + W2 [H, I] codes and their E8M0 scales, one expert."""
+    n = 3 * I * H
+    return (n // 2 if fp4 else n) + n // 32
+
+
+def layer_bytes(T: int, E: int, H: int, I: int, active: int, fp4: bool) -> int:
+    return 4 * T * E + T * H + T * H // 32 + active * weight_bytes_per_group(H, I, fp4) + 2 * T * H
+
+
+def w1_bytes(R: int, H: int, I: int, active: int, fp4: bool) -> int:
+    """The W1 launch: active experts' W1 codes + scales, the grouped x rows
+    once, the routing weights, and the h codes + scales it writes."""
+    n = 2 * I * H
+    wb = (n // 2 if fp4 else n) + n // 32
+    return active * wb + R * (H + H // 32) + 4 * R + R * (I + I // 32)
+
+
+def cpu_baseline(c8, moe_bytes_fn):
+    """Time the oracle on one T=8 call (routing draw 0); weights of the experts
+    that call touches are quantised by the oracle beforehand (untimed)."""
+    import numpy as np
+    from oracle import moe as omoe, mx
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    lg = synth.logits(c8, 0)
+    xq, xs = mx.quantize_mx(synth.x(c8, 0), mx.FMT_E4M3)
+    idx, _ = omoe.route(lg, c8.k)
+    active = sorted({int(e) - c8.e0 for e in idx.ravel() if 0 <= int(e) - c8.e0 < c8.n_local})
+    w1q, w1s, w2q, w2s = [None] * c8.n_local, [None] * c8.n_local, [None] * c8.n_local, [None] * c8.n_local
+    for g in active:
+        w1q[g], w1s[g] = mx.quantize_mx(synth.w1(c8, g), c8.w_fmt)
+        w2q[g], w2s[g] = mx.quantize_mx(synth.w2(c8, g), c8.w_fmt)
+    t0 = time.perf_counter()
+    omoe.moe_layer(lg, xq, xs, c8.k, w1q, w1s, w2q, w2s, c8.w_fmt, c8.I, e0=c8.e0, n_local=c8.n_local)
+    dt = time.perf_counter() - t0
+    nbytes = moe_bytes_fn(c8.T, len(active))
+    return {"value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one layer call at T=8 (routing draw 0, {len(active)} active experts), "
+                      f"{dt:.2f} s wall on the host CPU, fp64 NumPy"}, dt
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated between calls")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the expert-parallel layer on one MI355X; "
+              "runs on more than one GPU are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import routed_grouped_gemm_amd as moe
+    import synth
+    from synth import device
+
+    torch.cuda.set_device(0)
+    c = synth.config("decode", 128)
+    fp4 = c.w_fmt == "e2m1"
+    t_setup = time.perf_counter()
+    dw = device.build_weights(c)
+    copies = [dw]
+    for _ in range(args.copies - 1):
+        w1 = moe.PackedWeights.empty(c.n_local, 2 * c.I, c.H, dw.w1.fmt, True)
+        w2 = moe.PackedWeights.empty(c.n_local, c.H, c.I, dw.w2.fmt, False)
+        w1.buf.copy_(dw.w1.buf)
+        w2.buf.copy_(dw.w2.buf)
+        copies.append(device.DeviceWeights(w1, w2, None))
+    cfg = {T: synth.config("decode", T) for T in DECODE_T}
+    inputs = {T: [device.build_inputs(cfg[T], v) for v in range(N_VARIANTS)] for T in DECODE_T}
+    wss = {T: moe.LayerWorkspace(T, c.E, c.k, c.n_local, c.H, c.I) for T in DECODE_T}
+    outs = {T: torch.empty((T, c.H), dtype=torch.uint16, device="cuda") for T in DECODE_T}
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s on {torch.cuda.get_device_name(0)}")
+
+    # active experts and rows of every (T, draw): one untimed pass
+    active, rows = {}, {}
+    for T in DECODE_T:
+        for v in range(N_VARIANTS):
+            lg, xq, xs = inputs[T][v]
+            moe.moe_layer(lg, xq, xs, dw.w1, dw.w2, c.k, c.e0, c.n_local, None, 0, out=outs[T], ws=wss[T])
+            cnt = wss[T].view("counts").cpu()
+            active[T, v] = int((cnt > 0).sum())
+            rows[T, v] = int(cnt.sum())
+
+    def call(T, v, w):
+        lg, xq, xs = inputs[T][v]
+        moe.moe_layer(lg, xq, xs, w.w1, w.w2, c.k, c.e0, c.n_local, None, 0, out=outs[T], ws=wss[T])
+
+    def step(i):
+        for j, T in enumerate(DECODE_T):
+            call(T, i % N_VARIANTS, copies[(i * len(DECODE_T) + j) % len(copies)])
+
+    def step_bytes(i):
+        return sum(layer_bytes(T, c.E, c.H, c.I, active[T, i % N_VARIANTS], fp4) for T in DECODE_T)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + args.steps))
+    value = total_bytes / wall / 1e12
+    ms_per_step = wall / args.steps * 1e3
+
+    # per-T layer latency (HIP events on the launching stream), same rotation
+    stream = torch.cuda.current_stream()
+    per_t = {}
+    reps = max(8, args.steps)
+    for T in DECODE_T:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            call(T, r % N_VARIANTS, copies[r % len(copies)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        b = sum(layer_bytes(T, c.E, c.H, c.I, active[T, r % N_VARIANTS], fp4) for r in range(reps)) / reps
+        per_t[str(T)] = {"latency_us": round(us, 2), "TBps": round(b / us / 1e6, 3),
+                         "active_experts": round(sum(active[T, v] for v in range(N_VARIANTS)) / N_VARIANTS, 2)}
+
+    # dominant kernel: grouped W1, launched through its own entry point with the
+    # same arguments moe_layer gives it, HIP events around each launch
+    w1_ms, w1_b = 0.0, 0
+    nlaunch = 0
+    for T in DECODE_T:
+        ws = wss[T]
+        hint = moe.moe_layer_rows_hint(T, c.E, c.k)
+        for r in range(reps):
+            v = r % N_VARIANTS
+            w = copies[r % len(copies)]
+            lg, xq, xs = inputs[T][v]
+            idx, wt = moe.moe_route(lg, c.k, topk_idx=ws.view("topk_idx"), topk_w=ws.view("topk_w"))
+            moe.lib.moe_permute(idx.data_ptr(), wt.data_ptr(), T, c.k, c.e0, c.n_local, 0,
+                                xq.data_ptr(), xs.data_ptr(), c.H,
+                                ws.view("counts").data_ptr(), ws.view("offsets").data_ptr(),
+                                ws.view("offsets32").data_ptr(), ws.view("row_src").data_ptr(),
+                                ws.view("row_w").data_ptr(), ws.view("slot_row").data_ptr(),
+                                ws.view("xq_perm").data_ptr(), ws.view("xs_perm").data_ptr(),
+                                ws.buf.data_ptr() + ws.offsets[13], ws.nbytes - ws.offsets[13],
+                                stream.cuda_stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            moe.moe_grouped_w1(w.w1, ws.view("counts"), ws.view("offsets"), ws.view("row_w"),
+                               ws.view("xq_perm"), ws.view("xs_perm"), c.I, 0,
+                               offsets32=ws.view("offsets32"), hq=ws.view("hq"), hs=ws.view("hs"),
+                               rows_hint=hint)
+            b.record(stream)
+            moe.moe_grouped_w2(w.w2, ws.view("counts"), ws.view("offsets"), ws.view("hq"), ws.view("hs"),
+                               c.H, y=ws.view("y"), rows_hint=hint)
+            moe.moe_combine(ws.view("y"), ws.view("slot_row"), c.H, out=outs[T])
+            torch.cuda.synchronize()
+            w1_ms += a.elapsed_time(b)
+            w1_b += w1_bytes(rows[T, v], c.H, c.I, active[T, v], fp4)
+            nlaunch += 1
+    w1_gbs = w1_b / (w1_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(w1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(w1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "grouped_gemm_kernel (W1, MXFP4)",
+                "avg_launch_us": round(w1_ms * 1e3 / nlaunch, 2), "launches": nlaunch}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu, _ = cpu_baseline(cfg[8], lambda T, act: layer_bytes(T, c.E, c.H, c.I, act, fp4))
+
+    line = {
+        "metric": "MoE layer latency µs + achieved HBM TB/s (decode), MFMA TFLOPS (prefill)",
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp4e2m1 (MX), fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "decode share: T in {1,8,32,128} per step, H=7168, I=2048, "
+                               "top-8 of 256 experts, experts 0-31 local, MXFP4 weights",
+                   "weight_copies": args.copies, "routing_draws": N_VARIANTS},
+        "per_T": per_t,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -191,6 +191,8 @@ int32_t moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t T, int
  * backward). ldT = moe_transposed_ld(R_max, G).
  * w1 holds the routed groups [0, E_loc); w1_shared (NULL when G == E_loc)
  * holds group E_loc. hq [R_max, I], hs [R_max, I/32]; rows >= R untouched.
+ * rows_hint: expected rows per group, used only to choose the tiling
+ * (0: R_max / G); results do not depend on it.
  * ws: moe_grouped_workspace_size(...) bytes.
  */
 int32_t moe_transposed_ld(int32_t R_max, int32_t G);
@@ -198,21 +200,26 @@ size_t  moe_grouped_workspace_size(int32_t R_max, int32_t G, int32_t N, int32_t 
 int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_shared,
                        const int32_t* counts, const int32_t* offsets, const int32_t* offsets32,
                        const float* row_w, const uint8_t* xq_perm, const uint8_t* xs_perm,
-                       int32_t R_max, int32_t H, int32_t I, int32_t G, uint32_t flags,
-                       uint8_t* hq, uint8_t* hs, uint8_t* hTq, uint8_t* hTs,
+                       int32_t R_max, int32_t H, int32_t I, int32_t G, int32_t rows_hint,
+                       uint32_t flags, uint8_t* hq, uint8_t* hs, uint8_t* hTq, uint8_t* hTs,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- S6: grouped W2 ----------------------------------------------------- */
 /*
  * y[r] = BF16_RNE(dec(hq[r]) . dec(W2_g)^T) for every row r of group g
  * (W2 produces BF16 fragments: GC-MoE page, "Approach"). hq [R_max, I],
- * hs [R_max, I/32], y bf16 [R_max, H]; rows >= R untouched.
+ * hs [R_max, I/32], y bf16 [R_max, H]; rows >= R untouched. rows_hint as
+ * for moe_grouped_w1.
  */
 int32_t moe_grouped_w2(const moe_weights* w2, const moe_weights* w2_shared,
                        const int32_t* counts, const int32_t* offsets,
                        const uint8_t* hq, const uint8_t* hs,
-                       int32_t R_max, int32_t H, int32_t I, int32_t G,
+                       int32_t R_max, int32_t H, int32_t I, int32_t G, int32_t rows_hint,
                        uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The rows_hint moe_layer passes to the grouped GEMMs: the expected rows of a
+ * routed group under uniform routing, ceil(T * k / E_tot). */
+int32_t moe_layer_rows_hint(int32_t T, int32_t E_tot, int32_t k);
 
 /* ---- S7: combine ---------------------------------------------------------- */
 /*

@@ -187,11 +187,14 @@ def concat_transposed(hTq_list, hTs_list, I: int):
     return q, s
 
 
-def grouped_w2(hq, hs, offsets, w2q, w2s, w2_fmt: str, groups=None):
-    """Per group g: y_g = BF16_RNE(dec(h_g) @ dec(W2_g)^T), rounded once from fp64."""
+def grouped_w2(hq, hs, offsets, w2q, w2s, w2_fmt: str, groups=None, H: int | None = None):
+    """Per group g: y_g = BF16_RNE(dec(h_g) @ dec(W2_g)^T), rounded once from fp64.
+    Groups with no rows are never read (their entries may be None); H defaults
+    to the row count of the first group's W2."""
     R = int(offsets[-1])
     G = len(offsets) - 1
-    H = np.asarray(w2s[0]).shape[0] if G else 0
+    if H is None:
+        H = next(np.asarray(s).shape[0] for s in w2s if s is not None)
     yv = np.zeros((R, H))
     todo = range(G) if groups is None else groups
     for g in todo:
@@ -250,40 +253,54 @@ def moe_layer(logits, xq, xs, k: int, w1q, w1s, w2q, w2s, w_fmt: str, I: int,
     row_w_h = np.ones_like(perm.row_w) if weight_at_combine else perm.row_w
     o1 = grouped_w1(xq_p, xs_p, perm.offsets, row_w_h, w1q_g, w1s_g, w_fmt, I,
                     transpose=transpose, rule=rule)
-    y = grouped_w2(o1.hq, o1.hs, perm.offsets, w2q_g, w2s_g, w_fmt)
     H = xq.shape[1]
+    y = grouped_w2(o1.hq, o1.hs, perm.offsets, w2q_g, w2s_g, w_fmt, H=H)
     out = combine(y, perm.slot_row, H, perm.row_w if weight_at_combine else None)
     return LayerOut(out, idx, w, perm, o1, y)
 
 
+def expert_output(x_row: np.ndarray, w1q, w1s, w2q, w2s, w_fmt: str, I: int, weight: float,
+                  rule: str = "ocp") -> np.ndarray:
+    """One expert's contribution for one token, from dequantised x [H]:
+    BF16 value of W2 . Q8(SiLU(gate) * up * weight), fp64 inside."""
+    acc = x_row[None, :] @ mx.dequantize_mx(np.asarray(w1q), np.asarray(w1s), w_fmt).T
+    h = swiglu_rows(acc, I, np.array([weight]))
+    hq, hs = mx.quantize_mx(h, mx.FMT_E4M3, rule)
+    yv = mx.dequantize_mx(hq, hs, mx.FMT_E4M3) @ \
+        mx.dequantize_mx(np.asarray(w2q), np.asarray(w2s), w_fmt).T
+    return mx.bf16_value(mx.bf16_rne(yv))[0]
+
+
+def token_output(logit_row, xq_row, xs_row, k: int, get_expert, w_fmt: str, I: int,
+                 e0: int = 0, n_local: int | None = None, shared=None, rule: str = "ocp"):
+    """Brute-force output of one token: route it, run each local slot's expert
+    MLP on it alone, sum in fp64, round to BF16. `get_expert(g)` returns the
+    local expert's (w1q, w1s, w2q, w2s) codes, so weights can be produced on
+    demand; `shared` is the shared expert's codes or None. Returns bf16 bits [H]."""
+    logit_row = np.asarray(logit_row, dtype=np.float32)[None, :]
+    E_tot = logit_row.shape[1]
+    n_local = E_tot if n_local is None else n_local
+    idx, w = route(logit_row, k)
+    x = mx.dequantize_mx(np.asarray(xq_row)[None, :], np.asarray(xs_row)[None, :], mx.FMT_E4M3)[0]
+    out = np.zeros(x.shape[0])
+    for j in range(k):
+        g = int(idx[0, j]) - e0
+        if 0 <= g < n_local:
+            out += expert_output(x, *get_expert(g), w_fmt, I, float(w[0, j]), rule)
+    if shared is not None:
+        out += expert_output(x, *shared, w_fmt, I, 1.0, rule)
+    return mx.bf16_rne(out)
+
+
 def dense_layer(logits, xq, xs, k: int, w1q, w1s, w2q, w2s, w_fmt: str, I: int,
                 e0: int = 0, n_local: int | None = None, shared=None, rule: str = "ocp"):
-    """Brute-force evaluation with no grouping: for every token and every local
-    slot, run that expert's MLP on the token alone, then sum its slots.
-    Returns bf16 bits [T, H]. Used to pin the grouped computation."""
-    T, E_tot = logits.shape
-    n_local = E_tot if n_local is None else n_local
-    H = xq.shape[1]
-    idx, w = route(logits, k)
-    X = mx.dequantize_mx(np.asarray(xq), np.asarray(xs), mx.FMT_E4M3)
-    out = np.zeros((T, H))
-
-    def expert(t, W1q, W1s, W2q, W2s, weight):
-        acc = X[t:t + 1] @ mx.dequantize_mx(np.asarray(W1q), np.asarray(W1s), w_fmt).T
-        h = swiglu_rows(acc, I, np.array([weight]))
-        hq, hs = mx.quantize_mx(h, mx.FMT_E4M3, rule)
-        yv = mx.dequantize_mx(hq, hs, mx.FMT_E4M3) @ \
-            mx.dequantize_mx(np.asarray(W2q), np.asarray(W2s), w_fmt).T
-        return mx.bf16_value(mx.bf16_rne(yv))[0]
-
-    for t in range(T):
-        for j in range(k):
-            g = int(idx[t, j]) - e0
-            if 0 <= g < n_local:
-                out[t] += expert(t, w1q[g], w1s[g], w2q[g], w2s[g], w[t, j])
-        if shared is not None:
-            out[t] += expert(t, shared[0], shared[1], shared[2], shared[3], 1.0)
-    return mx.bf16_rne(out)
+    """Brute-force evaluation with no grouping: every token on its own (see
+    token_output). Returns bf16 bits [T, H]. Used to pin the grouped computation."""
+    T = logits.shape[0]
+    get = lambda g: (w1q[g], w1s[g], w2q[g], w2s[g])  # noqa: E731
+    rows = [token_output(logits[t], xq[t], xs[t], k, get, w_fmt, I, e0, n_local, shared, rule)
+            for t in range(T)]
+    return np.stack(rows) if rows else np.zeros((0, xq.shape[1]), np.uint16)
 
 
 # ------------------------------------------------------- algorithmic work

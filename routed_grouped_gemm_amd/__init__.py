@@ -4,7 +4,7 @@ A thin PyTorch binding over libmoe (include/moe.h). Every function here only
 marshals arguments (device pointers, sizes, the current HIP stream) and calls
 the C ABI of the same name; all computation runs in the library's HIP kernels.
 PyTorch provides device memory and streams. Importing the package fails if the
-library has not been built (routed_grouped_gemm_amd.build.build()).
+library has not been built (python routed_grouped_gemm_amd/build.py).
 """
 from __future__ import annotations
 
@@ -171,9 +171,13 @@ def moe_transposed_ld(R_max: int, G: int) -> int:
     return int(lib.moe_transposed_ld(R_max, G))
 
 
+def moe_layer_rows_hint(T: int, E_tot: int, k: int) -> int:
+    return int(lib.moe_layer_rows_hint(T, E_tot, k))
+
+
 def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq_perm, xs_perm, I: int,
                    flags: int = 0, w1_shared: PackedWeights | None = None, offsets32=None,
-                   hq=None, hs=None, hTq=None, hTs=None, stream=None):
+                   hq=None, hs=None, hTq=None, hTs=None, rows_hint: int = 0, stream=None):
     R_max, H = xq_perm.shape
     G = counts.shape[0]
     dev = xq_perm.device
@@ -188,13 +192,13 @@ def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq_perm, xs_perm, 
     nws = int(lib.moe_grouped_workspace_size(R_max, G, 2 * I, H))
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     _check(lib.moe_grouped_w1(w1.ref(), _wref(w1_shared), _p(counts), _p(offsets), _p(offsets32),
-                              _p(row_w), _p(xq_perm), _p(xs_perm), R_max, H, I, G, flags, _p(hq),
+                              _p(row_w), _p(xq_perm), _p(xs_perm), R_max, H, I, G, rows_hint, flags, _p(hq),
                               _p(hs), _p(hTq), _p(hTs), _p(ws), nws, _stream(stream)), "moe_grouped_w1")
     return hq, hs, hTq, hTs
 
 
 def moe_grouped_w2(w2: PackedWeights, counts, offsets, hq, hs, H: int,
-                   w2_shared: PackedWeights | None = None, y=None, stream=None):
+                   w2_shared: PackedWeights | None = None, y=None, rows_hint: int = 0, stream=None):
     R_max, I = hq.shape
     G = counts.shape[0]
     if y is None:
@@ -202,7 +206,8 @@ def moe_grouped_w2(w2: PackedWeights, counts, offsets, hq, hs, H: int,
     nws = int(lib.moe_grouped_workspace_size(R_max, G, H, I))
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=hq.device)
     _check(lib.moe_grouped_w2(w2.ref(), _wref(w2_shared), _p(counts), _p(offsets), _p(hq), _p(hs),
-                              R_max, H, I, G, _p(y), _p(ws), nws, _stream(stream)), "moe_grouped_w2")
+                              R_max, H, I, G, rows_hint, _p(y), _p(ws), nws, _stream(stream)),
+           "moe_grouped_w2")
     return y
 
 

@@ -45,8 +45,9 @@ SIGNATURES = {
     "moe_permute": (I32, [P, P, I32, I32, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_transposed_ld": (I32, [I32, I32]),
     "moe_grouped_workspace_size": (SZ, [I32, I32, I32, I32]),
-    "moe_grouped_w1": (I32, [WP, WP, P, P, P, P, P, P, I32, I32, I32, I32, U32, P, P, P, P, P, SZ, P]),
-    "moe_grouped_w2": (I32, [WP, WP, P, P, P, P, I32, I32, I32, I32, P, P, SZ, P]),
+    "moe_grouped_w1": (I32, [WP, WP, P, P, P, P, P, P, I32, I32, I32, I32, I32, U32, P, P, P, P, P, SZ, P]),
+    "moe_grouped_w2": (I32, [WP, WP, P, P, P, P, I32, I32, I32, I32, I32, P, P, SZ, P]),
+    "moe_layer_rows_hint": (I32, [I32, I32, I32]),
     "moe_combine": (I32, [P, P, P, I32, I32, I32, P, P]),
     "moe_layer_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, U32]),
     "moe_layer": (I32, [C.POINTER(moe_layer_args), P, SZ, P]),
@@ -62,7 +63,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise ImportError(f"libmoe.so not found at {path}: run routed_grouped_gemm_amd.build.build()")
+        raise ImportError(f"libmoe.so not found at {path}: run python routed_grouped_gemm_amd/build.py")
     lib = C.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         f = getattr(lib, name)

@@ -1,6 +1,7 @@
 """Build libmoe.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m routed_grouped_gemm_amd.build          # or build() from Python
+    python routed_grouped_gemm_amd/build.py     # (a plain script: importing the
+                                                # package itself needs the built library)
 
 Objects go to _build/ at the repository root; the shared library is written
 next to this file so that it travels with the source tree.

@@ -215,11 +215,12 @@ MOE_EXPORT int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_s
                                   const int32_t* counts, const int32_t* offsets,
                                   const int32_t* offsets32, const float* row_w,
                                   const uint8_t* xq_perm, const uint8_t* xs_perm, int32_t R_max,
-                                  int32_t H, int32_t I, int32_t G, uint32_t flags, uint8_t* hq,
-                                  uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
+                                  int32_t H, int32_t I, int32_t G, int32_t rows_hint,
+                                  uint32_t flags, uint8_t* hq, uint8_t* hs, uint8_t* hTq,
+                                  uint8_t* hTs, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (rows_hint < 0) return MOE_ERR_SHAPE;
     return grouped_w1_impl(w1, w1_shared, counts, offsets, offsets32, row_w, xq_perm, xs_perm,
-                           R_max, H, I, G, flags, hq, hs, hTq, hTs, ws, ws_bytes, 0, stream);
+                           R_max, H, I, G, flags, hq, hs, hTq, hTs, ws, ws_bytes, rows_hint, stream);
 }
 
 static int32_t grouped_w2_impl(const moe_weights* w2, const moe_weights* w2_shared,
@@ -244,10 +245,16 @@ static int32_t grouped_w2_impl(const moe_weights* w2, const moe_weights* w2_shar
 MOE_EXPORT int32_t moe_grouped_w2(const moe_weights* w2, const moe_weights* w2_shared,
                                   const int32_t* counts, const int32_t* offsets, const uint8_t* hq,
                                   const uint8_t* hs, int32_t R_max, int32_t H, int32_t I,
-                                  int32_t G, uint16_t* y, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
+                                  int32_t G, int32_t rows_hint, uint16_t* y, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    if (rows_hint < 0) return MOE_ERR_SHAPE;
     return grouped_w2_impl(w2, w2_shared, counts, offsets, hq, hs, R_max, H, I, G, y, ws, ws_bytes,
-                           0, stream);
+                           rows_hint, stream);
+}
+
+MOE_EXPORT int32_t moe_layer_rows_hint(int32_t T, int32_t E_tot, int32_t k) {
+    if (T <= 0 || E_tot <= 0 || k <= 0) return 0;
+    return (int32_t)(((int64_t)T * k + E_tot - 1) / E_tot);
 }
 
 // ---------------------------------------------------------------- combine
@@ -332,7 +339,7 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     if (e) return MOE_ERR_HIP;
     // expected rows of a routed group under uniform routing; the shared group
     // (T rows) gets more passes from the grid's pass dimension
-    const int hint = (T * k + E_tot - 1) / E_tot;
+    const int hint = moe_layer_rows_hint(T, E_tot, k);
     st = grouped_w1_impl(a->w1, a->shared_w1, counts, offsets, offsets32, row_w, xq_perm, xs_perm,
                          R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch, scratch_bytes,
                          hint, stream);

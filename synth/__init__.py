@@ -23,7 +23,11 @@ top-k of such logits samples k experts without replacement in proportion to
 p (the Gumbel-top-k identity), so expert e has popularity rank e+1.
 
 Every array has its own stream, keyed by (seed, stream tag, index), so one
-expert's weights can be drawn without drawing the others.
+expert's weights can be drawn without drawing the others. Weights depend on
+the workload's seed only (the decode sweep and the shared-expert workload use
+one set of routed experts); logits and x also depend on T and on a routing
+variant, so a benchmark can cycle through several routing draws over the same
+weights.
 """
 from __future__ import annotations
 
@@ -67,7 +71,7 @@ def config(name: str, T: int | None = None) -> Config:
         c = Config("tiny", 16, 512, 256, 8, 2, 0, 8, "e2m1", "normal", seed=1000)
     elif name == "decode":
         T = 128 if T is None else T
-        c = Config("decode", T, 7168, 2048, 256, 8, 0, 32, "e2m1", "normal", seed=1000 + 10 * T)
+        c = Config("decode", T, 7168, 2048, 256, 8, 0, 32, "e2m1", "normal", seed=1001)
     elif name == "full":
         c = Config("full", 256, 6144, 1536, 128, 8, 0, 128, "e2m1", "normal+bias", seed=1002)
     elif name == "prefill":
@@ -75,7 +79,7 @@ def config(name: str, T: int | None = None) -> Config:
                    transpose=True, seed=1003)
     elif name == "shared":
         c = Config("shared", 32, 7168, 2048, 256, 8, 0, 32, "e2m1", "normal",
-                   shared=True, seed=1004)
+                   shared=True, seed=1001)       # the decode workload's routed experts
     else:
         raise KeyError(name)
     if T is not None and name != "decode":
@@ -83,28 +87,29 @@ def config(name: str, T: int | None = None) -> Config:
     return c
 
 
-def _rng(seed: int, tag: str, index: int = 0) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _TAG[tag], index])))
+def _rng(seed: int, tag: str, *index: int) -> np.random.Generator:
+    key = [seed, _TAG[tag], *index]
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
 
 
 def logits(c: Config, variant: int = 0) -> np.ndarray:
     """Router logits, float32 [T, E]. `variant` selects one of several routing
     draws over the same weights (new logits and x, same experts)."""
-    g = _rng(c.seed, "logits", variant)
+    g = _rng(c.seed, "logits", c.T, variant)
     if c.logit_kind == "zipf":
         p = (np.arange(1, c.E + 1, dtype=np.float64)) ** -1.1
         p /= p.sum()
         return (np.log(p)[None, :] + g.gumbel(size=(c.T, c.E))).astype(np.float32)
     lg = g.standard_normal((c.T, c.E), dtype=np.float32)
     if c.logit_kind == "normal+bias":
-        b = _rng(c.seed, "bias").standard_normal(c.E, dtype=np.float32)
+        b = _rng(c.seed, "bias", 0).standard_normal(c.E, dtype=np.float32)
         lg = (lg + b[None, :]).astype(np.float32)
     return lg
 
 
 def x(c: Config, variant: int = 0) -> np.ndarray:
     """Activations, float32 [T, H]."""
-    return _rng(c.seed, "x", variant).standard_normal((c.T, c.H), dtype=np.float32)
+    return _rng(c.seed, "x", c.T, variant).standard_normal((c.T, c.H), dtype=np.float32)
 
 
 def w1(c: Config, g: int) -> np.ndarray:
@@ -118,8 +123,8 @@ def w2(c: Config, g: int) -> np.ndarray:
 
 
 def shared_w1(c: Config) -> np.ndarray:
-    return _rng(c.seed, "sw1").standard_normal((2 * c.I, c.H), dtype=np.float32) * np.float32(W_STD)
+    return _rng(c.seed, "sw1", 0).standard_normal((2 * c.I, c.H), dtype=np.float32) * np.float32(W_STD)
 
 
 def shared_w2(c: Config) -> np.ndarray:
-    return _rng(c.seed, "sw2").standard_normal((c.H, c.I), dtype=np.float32) * np.float32(W_STD)
+    return _rng(c.seed, "sw2", 0).standard_normal((c.H, c.I), dtype=np.float32) * np.float32(W_STD)

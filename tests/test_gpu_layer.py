@@ -1,0 +1,209 @@
+"""Whole-layer parity of moe_layer against the oracle (GPU).
+
+Small shapes: every element, every intermediate, with the oracle's quantised
+inputs uploaded to the GPU. Full workload sizes, called exactly as the
+benchmark calls them: routing, counts and offsets for every token, and the
+outputs of sampled tokens, which the oracle computes one by one from its own
+quantisation of the same float32 draws (checked equal to the library's
+quantisation of those draws first, so no oracle input comes from the GPU).
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as omoe, mx
+import synth
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("routed_grouped_gemm_amd")
+from gpu_util import (MFMA_REL, assert_layer_close, assert_mx_within_1ulp, banner, bf16_bits,  # noqa: E402
+                      dev, host)
+
+FMT = {"e2m1": moe.MOE_FMT_MXFP4, "e4m3": moe.MOE_FMT_MXFP8}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _oracle_inputs(c, variant=0):
+    lg = synth.logits(c, variant)
+    xq, xs = mx.quantize_mx(synth.x(c, variant), mx.FMT_E4M3)
+    w1 = [mx.quantize_mx(synth.w1(c, g), c.w_fmt) for g in range(c.n_local)]
+    w2 = [mx.quantize_mx(synth.w2(c, g), c.w_fmt) for g in range(c.n_local)]
+    sh = None
+    if c.shared:
+        a, b = mx.quantize_mx(synth.shared_w1(c), c.w_fmt), mx.quantize_mx(synth.shared_w2(c), c.w_fmt)
+        sh = (a[0], a[1], b[0], b[1])
+    return lg, xq, xs, w1, w2, sh
+
+
+def _packed(ws, fmt, is_w1):
+    return moe.PackedWeights(dev(np.stack([a[0] for a in ws])), dev(np.stack([a[1] for a in ws])),
+                             FMT[fmt], is_w1)
+
+
+SMALL = [
+    ("tiny", dict(), 0),
+    ("mid-share", dict(T=40, H=1024, I=512, E=32, k=4, e0=8, n_local=12, shared=True), 0),
+    ("mxfp8-transpose", dict(T=300, H=512, I=384, E=8, k=2, n_local=8, w_fmt="e4m3",
+                             transpose=True), moe.MOE_W1_WRITE_TRANSPOSE),
+    ("renorm-ceil", dict(T=24, E=16, k=4, n_local=16), moe.MOE_ROUTE_RENORM | moe.MOE_SCALE_RULE_CEIL),
+    ("weight-at-combine", dict(T=20, E=8, k=3, n_local=8), moe.MOE_WEIGHT_AT_COMBINE),
+    ("ragged-passes", dict(T=200, H=768, I=256, E=4, k=2, n_local=4, shared=True), 0),
+]
+
+
+@pytest.mark.parametrize("name,kw,flags", SMALL, ids=[s[0] for s in SMALL])
+def test_layer_small_every_element(name, kw, flags):
+    c = replace(synth.config("tiny"), **kw)
+    banner(f"layer {name} {c}")
+    lg, xq, xs, w1, w2, sh = _oracle_inputs(c)
+    rule = "ceil" if flags & moe.MOE_SCALE_RULE_CEIL else "ocp"
+    ref = omoe.moe_layer(lg, xq, xs, c.k, [a[0] for a in w1], [a[1] for a in w1], [a[0] for a in w2],
+                         [a[1] for a in w2], c.w_fmt, c.I, e0=c.e0, n_local=c.n_local, shared=sh,
+                         renorm=bool(flags & moe.MOE_ROUTE_RENORM),
+                         transpose=bool(flags & moe.MOE_W1_WRITE_TRANSPOSE),
+                         weight_at_combine=bool(flags & moe.MOE_WEIGHT_AT_COMBINE), rule=rule)
+    pw1, pw2 = _packed(w1, c.w_fmt, True), _packed(w2, c.w_fmt, False)
+    shared = None
+    if sh is not None:
+        shared = (moe.PackedWeights(dev(sh[0][None]), dev(sh[1][None]), FMT[c.w_fmt], True),
+                  moe.PackedWeights(dev(sh[2][None]), dev(sh[3][None]), FMT[c.w_fmt], False))
+    ws = moe.LayerWorkspace(c.T, c.E, c.k, c.n_local, c.H, c.I, c.shared, flags)
+    hTq = hTs = None
+    if flags & moe.MOE_W1_WRITE_TRANSPOSE:
+        ld = moe.moe_transposed_ld(c.R_max, c.G)
+        hTq = torch.zeros((c.I, ld), dtype=torch.uint8, device="cuda")
+        hTs = torch.zeros((c.I, ld // 32), dtype=torch.uint8, device="cuda")
+    out = moe.moe_layer(dev(lg), dev(xq), dev(xs), pw1, pw2, c.k, c.e0, c.n_local, shared, flags,
+                        ws=ws, hTq=hTq, hTs=hTs)
+    R = int(ref.perm.offsets[-1])
+    np.testing.assert_array_equal(host(ws.view("topk_idx")), ref.topk_idx)
+    np.testing.assert_allclose(host(ws.view("topk_w")), ref.topk_w, rtol=1e-5)
+    np.testing.assert_array_equal(host(ws.view("counts")), ref.perm.counts)
+    np.testing.assert_array_equal(host(ws.view("offsets")), ref.perm.offsets)
+    np.testing.assert_array_equal(host(ws.view("slot_row")), ref.perm.slot_row)
+    np.testing.assert_array_equal(host(ws.view("row_src"))[:R], ref.perm.row_src)
+    # h: one E4M3 step plus the propagated accumulation bound
+    xq_p, xs_p = omoe.gather_rows(xq, xs, ref.perm)
+    X = np.abs(mx.dequantize_mx(xq_p, xs_p, mx.FMT_E4M3))
+    ws1 = [a for a in w1] + ([(sh[0], sh[1])] if sh else [])
+    mag = np.zeros_like(ref.w1.acc)
+    for g in range(c.G):
+        lo, hi = ref.perm.offsets[g], ref.perm.offsets[g + 1]
+        if hi > lo:
+            mag[lo:hi] = X[lo:hi] @ np.abs(mx.dequantize_mx(ws1[g][0], ws1[g][1], c.w_fmt)).T
+    wts = np.ones(R) if flags & moe.MOE_WEIGHT_AT_COMBINE else ref.perm.row_w
+    gate, up = ref.w1.acc[:, :c.I], ref.w1.acc[:, c.I:]
+    dg, du = MFMA_REL * mag[:, :c.I], MFMA_REL * mag[:, c.I:]
+    dh = (1.1 * (np.abs(up) + du) * dg + np.abs(omoe.silu(gate)) * du) * np.abs(wts)[:, None] \
+        + 2e-5 * np.abs(ref.w1.h)                         # fp32 routing weight vs fp64
+    assert_mx_within_1ulp(host(ws.view("hq"))[:R], host(ws.view("hs"))[:R], ref.w1.hq, ref.w1.hs,
+                          "h", extra_tol=dh)
+    if flags & moe.MOE_W1_WRITE_TRANSPOSE:
+        q_ref, s_ref = omoe.concat_transposed(ref.w1.hTq, ref.w1.hTs, c.I)
+        n = q_ref.shape[1]
+        assert_mx_within_1ulp(host(hTq)[:, :n], host(hTs)[:, :n // 32], q_ref, s_ref, "hT",
+                              max_frac_diff=0.02, extra_tol=_transpose_tol(dh, ref, c))
+    assert_layer_close(bf16_bits(out), ref.out, "out")
+
+
+def _transpose_tol(dh, ref, c):
+    n = sum((int(ref.perm.counts[g]) + 31) // 32 * 32 for g in range(c.G))
+    t = np.zeros((c.I, n))
+    col = 0
+    for g in range(c.G):
+        lo, hi = ref.perm.offsets[g], ref.perm.offsets[g + 1]
+        t[:, col:col + hi - lo] = dh[lo:hi].T
+        col += (hi - lo + 31) // 32 * 32
+    return t
+
+
+# ---------------------------------------------------------------- full size
+_WEIGHTS = {}
+
+
+def _device_weights(c):
+    from synth import device
+    key = (c.seed, c.w_fmt, c.n_local, c.H, c.I, c.shared)
+    if key not in _WEIGHTS:
+        _WEIGHTS.clear()
+        torch.cuda.empty_cache()
+        _WEIGHTS[key] = device.build_weights(c)
+    return _WEIGHTS[key]
+
+
+FULL = [("decode", 1), ("decode", 8), ("decode", 32), ("decode", 128), ("shared", None),
+        ("full", None), ("prefill", None)]
+
+
+@pytest.mark.parametrize("name,T", FULL, ids=[f"{n}-{t}" for n, t in FULL])
+def test_layer_full_size_sampled(name, T):
+    from synth import device
+    c = synth.config(name, T)
+    banner(f"full-size layer {name} T={c.T} H={c.H} I={c.I} E={c.E} k={c.k}")
+    dw = _device_weights(c)
+    logits, xq_d, xs_d = device.build_inputs(c)
+    flags = moe.MOE_W1_WRITE_TRANSPOSE if c.transpose else 0
+    ws = moe.LayerWorkspace(c.T, c.E, c.k, c.n_local, c.H, c.I, c.shared, flags)
+    hTq = hTs = None
+    if c.transpose:
+        ld = moe.moe_transposed_ld(c.R_max, c.G)
+        hTq = torch.empty((c.I, ld), dtype=torch.uint8, device="cuda")
+        hTs = torch.empty((c.I, ld // 32), dtype=torch.uint8, device="cuda")
+    out = moe.moe_layer(logits, xq_d, xs_d, dw.w1, dw.w2, c.k, c.e0, c.n_local, dw.shared, flags,
+                        ws=ws, hTq=hTq, hTs=hTs)
+    got = bf16_bits(out)
+
+    # routing and grouping of every token
+    lg = synth.logits(c)
+    idx_ref, w_ref = omoe.route(lg, c.k)
+    np.testing.assert_array_equal(host(ws.view("topk_idx")), idx_ref)
+    perm = omoe.permute(idx_ref, w_ref, c.e0, c.n_local, c.shared)
+    np.testing.assert_array_equal(host(ws.view("counts")), perm.counts)
+    np.testing.assert_array_equal(host(ws.view("offsets")), perm.offsets)
+
+    # sampled tokens, computed one by one by the oracle
+    x32 = synth.x(c)
+    rng = np.random.default_rng(c.T)
+    local = (perm.slot_row[:, :c.k] >= 0).sum(1)
+    cand = np.flatnonzero(local > 0)
+    picks = list(rng.choice(cand, size=min(2, len(cand)), replace=False)) if len(cand) else []
+    none = np.flatnonzero(local == 0)
+    if len(none) and not c.shared:
+        picks.append(int(none[0]))                 # a token with no local slot: exact zeros
+    cache = {}
+
+    def get_expert(g):
+        if g not in cache:
+            a32, b32 = synth.w1(c, g), synth.w2(c, g)
+            qa, sa = mx.quantize_mx(a32, c.w_fmt)
+            qb, sb = mx.quantize_mx(b32, c.w_fmt)
+            # the library's quantisation of the same draws must be identical
+            gq, gs = moe.moe_quantize_mx(dev(a32), FMT[c.w_fmt])
+            assert np.array_equal(host(gq), qa) and np.array_equal(host(gs), sa), f"W1[{g}] quantisation"
+            gq, gs = moe.moe_quantize_mx(dev(b32), FMT[c.w_fmt])
+            assert np.array_equal(host(gq), qb) and np.array_equal(host(gs), sb), f"W2[{g}] quantisation"
+            cache[g] = (qa, sa, qb, sb)
+        return cache[g]
+
+    sh = None
+    if c.shared:
+        a, b = mx.quantize_mx(synth.shared_w1(c), c.w_fmt), mx.quantize_mx(synth.shared_w2(c), c.w_fmt)
+        sh = (a[0], a[1], b[0], b[1])
+    xq_ref, xs_ref = mx.quantize_mx(x32[picks], mx.FMT_E4M3)
+    np.testing.assert_array_equal(host(xq_d)[picks], xq_ref)
+    np.testing.assert_array_equal(host(xs_d)[picks], xs_ref)
+    ref_rows = np.stack([omoe.token_output(lg[t], xq_ref[i], xs_ref[i], c.k, get_expert, c.w_fmt, c.I,
+                                           c.e0, c.n_local, sh) for i, t in enumerate(picks)])
+    for i, t in enumerate(picks):
+        if local[t] == 0 and not c.shared:
+            assert np.all(got[t] == 0), f"token {t} has no local slot but a nonzero row"
+        else:
+            assert_layer_close(got[t], ref_rows[i], f"token {t} ({local[t]} local slots)")
