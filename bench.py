@@ -10,8 +10,9 @@ are held in several identical copies and consecutive calls rotate through
 them, as consecutive MoE layers of a model would, so a call never finds the
 previous call's weights in the 256 MB last-level cache.
 
-Printed JSON line (stdout): value = algorithmic HBM bytes of the step's layer
-calls / wall time of the step, in TB/s. Algorithmic bytes per call: router
+Each step's launch sequence is captured once per routing draw into a HIP
+graph and replayed. Printed JSON line (stdout): value = algorithmic HBM bytes
+of the step's layer calls / wall time of the steps, in TB/s. Algorithmic bytes per call: router
 logits, x codes + scales, the W1 and W2 codes + scales of the experts that
 received at least one token, and the BF16 output. The "roofline" object is
 for the dominant kernel (the grouped W1 GEMM), timed with HIP events around
@@ -145,27 +146,53 @@ def main():
     def step_bytes(i):
         return sum(layer_bytes(T, c.E, c.H, c.I, active[T, i % N_VARIANTS], fp4) for T in DECODE_T)
 
+    # The launch sequence is captured once per routing draw into a HIP graph
+    # (no host work or host sync inside a layer call) and replayed.
+    torch.cuda.synchronize()
+    step_graphs = []
+    for v in range(N_VARIANTS):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(v)
+        step_graphs.append(g)
+    call_graphs = {}
+    for T in DECODE_T:
+        for v in range(N_VARIANTS):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                call(T, v, copies[v % len(copies)])
+            call_graphs[T, v] = g
+    torch.cuda.synchronize()
+
     for i in range(args.warmup):
-        step(i)
+        step_graphs[i % N_VARIANTS].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, args.warmup + args.steps):
-        step(i)
+        step_graphs[i % N_VARIANTS].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + args.steps))
     value = total_bytes / wall / 1e12
     ms_per_step = wall / args.steps * 1e3
 
-    # per-T layer latency (HIP events on the launching stream), same rotation
+    # the same steps launched eagerly (one host call per layer), for reference
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_tbps = sum(step_bytes(i) for i in range(args.steps)) / (time.perf_counter() - t0) / 1e12
+
+    # per-T layer latency (HIP events on the replay stream), same rotation
     stream = torch.cuda.current_stream()
     per_t = {}
-    reps = max(8, args.steps)
+    reps = max(16, args.steps)
     for T in DECODE_T:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for r in range(reps):
-            call(T, r % N_VARIANTS, copies[r % len(copies)])
+            call_graphs[T, r % N_VARIANTS].replay()
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
@@ -173,8 +200,10 @@ def main():
         per_t[str(T)] = {"latency_us": round(us, 2), "TBps": round(b / us / 1e6, 3),
                          "active_experts": round(sum(active[T, v] for v in range(N_VARIANTS)) / N_VARIANTS, 2)}
 
-    # dominant kernel: grouped W1, launched through its own entry point with the
-    # same arguments moe_layer gives it, HIP events around each launch
+    # dominant kernel: grouped W1. After a layer call has grouped the tokens,
+    # W1 is launched again through its own entry point with the arguments
+    # moe_layer gives it (on another weight copy, so it streams from HBM), with
+    # HIP events around the launch on the launching stream.
     w1_ms, w1_b = 0.0, 0
     nlaunch = 0
     for T in DECODE_T:
@@ -182,27 +211,16 @@ def main():
         hint = moe.moe_layer_rows_hint(T, c.E, c.k)
         for r in range(reps):
             v = r % N_VARIANTS
-            w = copies[r % len(copies)]
             lg, xq, xs = inputs[T][v]
-            idx, wt = moe.moe_route(lg, c.k, topk_idx=ws.view("topk_idx"), topk_w=ws.view("topk_w"))
-            moe.lib.moe_permute(idx.data_ptr(), wt.data_ptr(), T, c.k, c.e0, c.n_local, 0,
-                                xq.data_ptr(), xs.data_ptr(), c.H,
-                                ws.view("counts").data_ptr(), ws.view("offsets").data_ptr(),
-                                ws.view("offsets32").data_ptr(), ws.view("row_src").data_ptr(),
-                                ws.view("row_w").data_ptr(), ws.view("slot_row").data_ptr(),
-                                ws.view("xq_perm").data_ptr(), ws.view("xs_perm").data_ptr(),
-                                ws.buf.data_ptr() + ws.offsets[13], ws.nbytes - ws.offsets[13],
-                                stream.cuda_stream)
+            call(T, v, copies[r % len(copies)])
+            w = copies[(r + 2) % len(copies)]
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            moe.moe_grouped_w1(w.w1, ws.view("counts"), ws.view("offsets"), ws.view("row_w"),
-                               ws.view("xq_perm"), ws.view("xs_perm"), c.I, 0,
-                               offsets32=ws.view("offsets32"), hq=ws.view("hq"), hs=ws.view("hs"),
-                               rows_hint=hint)
+            moe.moe_grouped_w1(w.w1, ws.view("counts"), ws.view("offsets"), ws.view("row_w"), xq, xs,
+                               c.I, 0, offsets32=ws.view("offsets32"), hq=ws.view("hq"),
+                               hs=ws.view("hs"), rows_hint=hint, row_src=ws.view("row_src"),
+                               R_max=T * c.k)
             b.record(stream)
-            moe.moe_grouped_w2(w.w2, ws.view("counts"), ws.view("offsets"), ws.view("hq"), ws.view("hs"),
-                               c.H, y=ws.view("y"), rows_hint=hint)
-            moe.moe_combine(ws.view("y"), ws.view("slot_row"), c.H, out=outs[T])
             torch.cuda.synchronize()
             w1_ms += a.elapsed_time(b)
             w1_b += w1_bytes(rows[T, v], c.H, c.I, active[T, v], fp4)
@@ -234,6 +252,7 @@ def main():
                                "top-8 of 256 experts, experts 0-31 local, MXFP4 weights",
                    "weight_copies": args.copies, "routing_draws": N_VARIANTS},
         "per_T": per_t,
+        "eager_TBps": round(eager_tbps, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

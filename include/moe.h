@@ -177,12 +177,16 @@ int32_t moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t T, int
 /* ---- S4 + S5: grouped W1 with the fused epilogue ------------------------ */
 /*
  * For every group g and row r in [offsets[g], offsets[g+1]):
- *   acc = dec(xq_perm[r]) . dec(W1_g)^T  (fp32 accumulation on MFMA)
+ *   acc = dec(x_r) . dec(W1_g)^T  (fp32 accumulation on MFMA)
  *   h   = SiLU(acc[0:I]) * acc[I:2I] * row_w[r]   (row_w ignored, i.e. 1,
  *         with MOE_WEIGHT_AT_COMBINE)
  *   hq[r], hs[r] = MX-E4M3 quantisation of h in blocks of 32 along I
  * (SwiGLU with beta = 1 and no bias: fusion blog, GLU epilogue section; the
  * epilogue fusion: GC-MoE page, "Key contributions".)
+ * x_r is row r of xq/xs when row_src is NULL (xq [R_max, H], xs [R_max, H/32],
+ * the grouped rows moe_permute gathers), or row row_src[r] of the ungrouped
+ * token arrays xq [T, H], xs [T, H/32] when row_src is given (the gather is
+ * then done by this kernel's loads).
  * With MOE_W1_WRITE_TRANSPOSE also hTq/hTs: for group g, columns
  * [offsets32[g], offsets32[g+1]) of hTq [I, ldT] hold h_g^T quantised in
  * blocks of 32 tokens counted from the group's first row (hTs [I, ldT/32]);
@@ -199,7 +203,8 @@ int32_t moe_transposed_ld(int32_t R_max, int32_t G);
 size_t  moe_grouped_workspace_size(int32_t R_max, int32_t G, int32_t N, int32_t K);
 int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_shared,
                        const int32_t* counts, const int32_t* offsets, const int32_t* offsets32,
-                       const float* row_w, const uint8_t* xq_perm, const uint8_t* xs_perm,
+                       const float* row_w, const uint8_t* xq, const uint8_t* xs,
+                       const int32_t* row_src,
                        int32_t R_max, int32_t H, int32_t I, int32_t G, int32_t rows_hint,
                        uint32_t flags, uint8_t* hq, uint8_t* hs, uint8_t* hTq, uint8_t* hTs,
                        void* ws, size_t ws_bytes, hipStream_t stream);
@@ -255,18 +260,20 @@ size_t  moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_
                                  int32_t H, int32_t I, int32_t s, uint32_t flags);
 
 /*
- * Run route -> permute -> W1 -> W2 -> combine on `stream`.
+ * Run route -> permute -> W1 -> W2 -> combine on `stream`: 4 launches when
+ * T <= 64 (router and grouping share one workgroup), more otherwise. The
+ * grouped token rows are not materialised: W1 reads them through row_src.
  * Intermediates live in ws at offsets given by moe_layer_workspace_offsets.
  */
 int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Byte offsets of the intermediates inside the moe_layer workspace, for
  * inspection by tests: [0] topk_idx [1] topk_w [2] counts [3] offsets
- * [4] offsets32 [5] row_src [6] row_w [7] slot_row [8] xq_perm [9] xs_perm
- * [10] hq [11] hs [12] y [13] scratch. Returns the number written (14). */
+ * [4] offsets32 [5] row_src [6] row_w [7] slot_row [8] hq [9] hs [10] y
+ * [11] scratch. Returns the number written (12). */
 int32_t moe_layer_workspace_offsets(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
                                     int32_t H, int32_t I, int32_t s, uint32_t flags,
-                                    size_t* offsets14);
+                                    size_t* offsets12);
 
 #ifdef __cplusplus
 }

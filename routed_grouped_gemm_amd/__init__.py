@@ -175,12 +175,17 @@ def moe_layer_rows_hint(T: int, E_tot: int, k: int) -> int:
     return int(lib.moe_layer_rows_hint(T, E_tot, k))
 
 
-def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq_perm, xs_perm, I: int,
+def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq, xs, I: int,
                    flags: int = 0, w1_shared: PackedWeights | None = None, offsets32=None,
-                   hq=None, hs=None, hTq=None, hTs=None, rows_hint: int = 0, stream=None):
-    R_max, H = xq_perm.shape
+                   hq=None, hs=None, hTq=None, hTs=None, rows_hint: int = 0, row_src=None,
+                   R_max: int | None = None, stream=None):
+    """xq/xs: the grouped rows [R_max, H] (row_src None) or the token rows
+    [T, H] read through row_src (then R_max must be given)."""
+    H = xq.shape[1]
+    if R_max is None:
+        R_max = xq.shape[0]
     G = counts.shape[0]
-    dev = xq_perm.device
+    dev = xq.device
     if hq is None:
         hq = torch.empty((R_max, I), dtype=torch.uint8, device=dev)
     if hs is None:
@@ -192,7 +197,7 @@ def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq_perm, xs_perm, 
     nws = int(lib.moe_grouped_workspace_size(R_max, G, 2 * I, H))
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     _check(lib.moe_grouped_w1(w1.ref(), _wref(w1_shared), _p(counts), _p(offsets), _p(offsets32),
-                              _p(row_w), _p(xq_perm), _p(xs_perm), R_max, H, I, G, rows_hint, flags, _p(hq),
+                              _p(row_w), _p(xq), _p(xs), _p(row_src), R_max, H, I, G, rows_hint, flags, _p(hq),
                               _p(hs), _p(hTq), _p(hTs), _p(ws), nws, _stream(stream)), "moe_grouped_w1")
     return hq, hs, hTq, hTs
 
@@ -223,7 +228,7 @@ def moe_combine(y, slot_row, H: int, row_w=None, out=None, stream=None):
 
 # ------------------------------------------------------------------- layer
 _NAMES = ["topk_idx", "topk_w", "counts", "offsets", "offsets32", "row_src", "row_w", "slot_row",
-          "xq_perm", "xs_perm", "hq", "hs", "y", "scratch"]
+          "hq", "hs", "y", "scratch"]
 
 
 class LayerWorkspace:
@@ -234,9 +239,10 @@ class LayerWorkspace:
         self.shape = (T, E_tot, k, E_loc, H, I, s, flags)
         self.nbytes = int(lib.moe_layer_workspace_size(T, E_tot, k, E_loc, H, I, s, flags))
         self.buf = torch.empty(max(self.nbytes, 1), dtype=torch.uint8, device=device)
-        offs = (C.c_size_t * 14)()
+        offs = (C.c_size_t * len(_NAMES))()
         lib.moe_layer_workspace_offsets(T, E_tot, k, E_loc, H, I, s, flags, offs)
         self.offsets = list(offs)
+        self.scratch_offset = self.offsets[_NAMES.index("scratch")]
 
     def view(self, name: str) -> torch.Tensor:
         T, E_tot, k, E_loc, H, I, s, _ = self.shape
@@ -247,7 +253,6 @@ class LayerWorkspace:
             "counts": ((G,), torch.int32), "offsets": ((G + 1,), torch.int32),
             "offsets32": ((G + 1,), torch.int32), "row_src": ((R,), torch.int32),
             "row_w": ((R,), torch.float32), "slot_row": ((T, k + s), torch.int32),
-            "xq_perm": ((R, H), torch.uint8), "xs_perm": ((R, H // 32), torch.uint8),
             "hq": ((R, I), torch.uint8), "hs": ((R, I // 32), torch.uint8),
             "y": ((R, H), torch.uint16),
         }

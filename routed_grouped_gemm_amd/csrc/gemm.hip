@@ -30,6 +30,7 @@ struct KParams {
     const float* row_w;
     const uint8_t* aq;
     const uint8_t* as;
+    const int32_t* row_src;       // null: grouped row r is activation row r
     int N;                        // W1: 2I ; W2: H (y row length)
     int ceil_rule, transpose, use_w;
     uint8_t* hq; uint8_t* hs; uint8_t* hTq; uint8_t* hTs; int ldT;
@@ -61,12 +62,14 @@ MOE_DEV i32x8 load_x(const uint8_t* row_kt, int grp) {
     return r;
 }
 
-// One K-tile (index kt, scale byte SEL of the packed dword) for all active token tiles.
+// One K-tile (index kt, scale byte SEL of the packed dword) for all active
+// token tiles. xrow[tt] is this lane's activation row for token tile tt, or
+// -1 past the end of the pass.
 template <int WFMT, int NTT, int SEL>
 MOE_DEV void k_step(const KParams& p, const uint8_t* wunit, const int (&sA)[4], int kt, int lane,
-                    int rbase, int nrows, int ntt_active, f32x4 (&acc)[NTT][4]) {
+                    const long (&xrow)[NTT], int ntt_active, f32x4 (&acc)[NTT][4]) {
     if (kt >= p.kt) return;
-    const int grp = lane >> 4, col = lane & 15;
+    const int grp = lane >> 4;
     i32x8 A[4];
     #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -74,11 +77,10 @@ MOE_DEV void k_step(const KParams& p, const uint8_t* wunit, const int (&sA)[4], 
     #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
         if (tt < ntt_active) {
-            const int r = tt * 16 + col;
             i32x8 B;
             int sB = 127;
-            if (r < nrows) {
-                const size_t row = (size_t)(rbase + r);
+            if (xrow[tt] >= 0) {
+                const size_t row = (size_t)xrow[tt];
                 B = load_x(p.aq + row * p.K + (size_t)kt * 128, grp);
                 sB = p.as[row * (p.K / 32) + kt * 4 + grp];
             } else {
@@ -119,20 +121,24 @@ void grouped_gemm_kernel(KParams p) {
         const int ntt_active = (nrows + 15) / 16;
 
         f32x4 acc[NTT][4];
+        long xrow[NTT];
         #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt)
+        for (int tt = 0; tt < NTT; ++tt) {
             #pragma unroll
             for (int t = 0; t < 4; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int r = tt * 16 + (lane & 15);
+            xrow[tt] = r < nrows ? (p.row_src ? (long)p.row_src[rbase + r] : (long)(rbase + r)) : -1;
+        }
 
         for (int kg = kg0; kg < kg1; ++kg) {
             int sA[4];
             #pragma unroll
             for (int t = 0; t < 4; ++t)
                 sA[t] = *(const int*)(sunit + ((size_t)(kg * 4 + t) * 64 + lane) * 4);
-            k_step<WFMT, NTT, 0>(p, wunit, sA, kg * 4 + 0, lane, rbase, nrows, ntt_active, acc);
-            k_step<WFMT, NTT, 1>(p, wunit, sA, kg * 4 + 1, lane, rbase, nrows, ntt_active, acc);
-            k_step<WFMT, NTT, 2>(p, wunit, sA, kg * 4 + 2, lane, rbase, nrows, ntt_active, acc);
-            k_step<WFMT, NTT, 3>(p, wunit, sA, kg * 4 + 3, lane, rbase, nrows, ntt_active, acc);
+            k_step<WFMT, NTT, 0>(p, wunit, sA, kg * 4 + 0, lane, xrow, ntt_active, acc);
+            k_step<WFMT, NTT, 1>(p, wunit, sA, kg * 4 + 1, lane, xrow, ntt_active, acc);
+            k_step<WFMT, NTT, 2>(p, wunit, sA, kg * 4 + 2, lane, xrow, ntt_active, acc);
+            k_step<WFMT, NTT, 3>(p, wunit, sA, kg * 4 + 3, lane, xrow, ntt_active, acc);
         }
 
         // Sum the four waves' partials in a fixed order, ((w0 + w2) + (w1 + w3)),
@@ -245,7 +251,7 @@ KParams make_params(const GemmArgs& a, bool w1) {
     p.dpu = geo.data_per_unit;    p.spu = geo.scale_per_unit;
     p.E_loc = a.E_loc; p.K = a.K; p.kt = geo.kt; p.kt4 = geo.kt4;
     p.counts = a.counts; p.offsets = a.offsets; p.offsets32 = a.offsets32;
-    p.row_w = a.row_w; p.aq = a.aq; p.as = a.as; p.N = a.N;
+    p.row_w = a.row_w; p.aq = a.aq; p.as = a.as; p.row_src = a.row_src; p.N = a.N;
     p.ceil_rule = (a.flags & MOE_SCALE_RULE_CEIL) ? 1 : 0;
     p.transpose = (w1 && (a.flags & MOE_W1_WRITE_TRANSPOSE)) ? 1 : 0;
     p.use_w = (w1 && a.row_w && !(a.flags & MOE_WEIGHT_AT_COMBINE)) ? 1 : 0;

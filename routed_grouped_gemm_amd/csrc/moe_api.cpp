@@ -27,8 +27,9 @@ int32_t check_weights(const moe_weights* w, int G, int N, int K, int is_w1) {
 }
 
 // Workspace layout of moe_layer (all regions 256-byte aligned).
+constexpr int kRegions = 12;
 struct LayerLayout {
-    size_t off[14];
+    size_t off[kRegions];
     size_t total;
 };
 
@@ -36,7 +37,7 @@ LayerLayout layer_layout(int T, int E_tot, int k, int E_loc, int H, int I, int s
     (void)E_tot;
     const size_t R = (size_t)T * k + (size_t)s * T;
     const int G = E_loc + s;
-    size_t sz[14] = {
+    size_t sz[kRegions] = {
         (size_t)T * k * 4,            // topk_idx
         (size_t)T * k * 4,            // topk_w
         (size_t)G * 4,                // counts
@@ -45,8 +46,6 @@ LayerLayout layer_layout(int T, int E_tot, int k, int E_loc, int H, int I, int s
         R * 4,                        // row_src
         R * 4,                        // row_w
         (size_t)T * (k + s) * 4,      // slot_row
-        R * H,                        // xq_perm
-        R * (H / 32),                 // xs_perm
         R * I,                        // hq
         R * (I / 32),                 // hs
         R * H * 2,                    // y
@@ -56,10 +55,10 @@ LayerLayout layer_layout(int T, int E_tot, int k, int E_loc, int H, int I, int s
     size_t gws2 = moe_grouped_workspace_size((int)R, G, H, I);
     size_t pws = moe_permute_workspace_size(T, k, G);
     size_t scr = pws > gws1 ? pws : gws1;
-    sz[13] = scr > gws2 ? scr : gws2;
+    sz[kRegions - 1] = scr > gws2 ? scr : gws2;
     LayerLayout L;
     size_t o = 0;
-    for (int i = 0; i < 14; ++i) {
+    for (int i = 0; i < kRegions; ++i) {
         L.off[i] = o;
         o += align_up(sz[i]);
     }
@@ -189,7 +188,8 @@ static int32_t check_hi(int H, int I) {
 static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shared,
                                const int32_t* counts, const int32_t* offsets,
                                const int32_t* offsets32, const float* row_w,
-                               const uint8_t* xq_perm, const uint8_t* xs_perm, int32_t R_max,
+                               const uint8_t* xq_perm, const uint8_t* xs_perm,
+                               const int32_t* row_src, int32_t R_max,
                                int32_t H, int32_t I, int32_t G, uint32_t flags, uint8_t* hq,
                                uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes,
                                int rows_hint, hipStream_t stream) {
@@ -206,7 +206,8 @@ static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shar
     const size_t need = moe_grouped_workspace_size(R_max, G, 2 * I, H);
     if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
     a.counts = counts; a.offsets = offsets; a.offsets32 = offsets32; a.row_w = row_w;
-    a.aq = xq_perm; a.as = xs_perm; a.R_max = R_max; a.rows_hint = rows_hint; a.flags = flags;
+    a.aq = xq_perm; a.as = xs_perm; a.row_src = row_src;
+    a.R_max = R_max; a.rows_hint = rows_hint; a.flags = flags;
     a.hq = hq; a.hs = hs; a.hTq = hTq; a.hTs = hTs; a.ldT = moe_transposed_ld(R_max, G);
     return hip_status(moe_launch_grouped_w1(a, stream));
 }
@@ -214,12 +215,13 @@ static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shar
 MOE_EXPORT int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_shared,
                                   const int32_t* counts, const int32_t* offsets,
                                   const int32_t* offsets32, const float* row_w,
-                                  const uint8_t* xq_perm, const uint8_t* xs_perm, int32_t R_max,
-                                  int32_t H, int32_t I, int32_t G, int32_t rows_hint,
-                                  uint32_t flags, uint8_t* hq, uint8_t* hs, uint8_t* hTq,
-                                  uint8_t* hTs, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                  const uint8_t* xq, const uint8_t* xs, const int32_t* row_src,
+                                  int32_t R_max, int32_t H, int32_t I, int32_t G,
+                                  int32_t rows_hint, uint32_t flags, uint8_t* hq, uint8_t* hs,
+                                  uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
     if (rows_hint < 0) return MOE_ERR_SHAPE;
-    return grouped_w1_impl(w1, w1_shared, counts, offsets, offsets32, row_w, xq_perm, xs_perm,
+    return grouped_w1_impl(w1, w1_shared, counts, offsets, offsets32, row_w, xq, xs, row_src,
                            R_max, H, I, G, flags, hq, hs, hTq, hTs, ws, ws_bytes, rows_hint, stream);
 }
 
@@ -277,12 +279,12 @@ MOE_EXPORT size_t moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, 
 
 MOE_EXPORT int32_t moe_layer_workspace_offsets(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
                                                int32_t H, int32_t I, int32_t s, uint32_t flags,
-                                               size_t* offsets14) {
+                                               size_t* offsets12) {
     (void)flags;
-    if (!offsets14) return 0;
+    if (!offsets12) return 0;
     LayerLayout L = layer_layout(T, E_tot, k, E_loc, H, I, s);
-    memcpy(offsets14, L.off, sizeof(L.off));
-    return 14;
+    memcpy(offsets12, L.off, sizeof(L.off));
+    return kRegions;
 }
 
 MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
@@ -323,26 +325,33 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     int32_t* row_src = (int32_t*)(base + L.off[5]);
     float* row_w = (float*)(base + L.off[6]);
     int32_t* slot_row = (int32_t*)(base + L.off[7]);
-    uint8_t* xq_perm = (uint8_t*)(base + L.off[8]);
-    uint8_t* xs_perm = (uint8_t*)(base + L.off[9]);
-    uint8_t* hq = (uint8_t*)(base + L.off[10]);
-    uint8_t* hs = (uint8_t*)(base + L.off[11]);
-    uint16_t* y = (uint16_t*)(base + L.off[12]);
-    void* scratch = base + L.off[13];
-    const size_t scratch_bytes = L.total - L.off[13];
+    uint8_t* hq = (uint8_t*)(base + L.off[8]);
+    uint8_t* hs = (uint8_t*)(base + L.off[9]);
+    uint16_t* y = (uint16_t*)(base + L.off[10]);
+    void* scratch = base + L.off[11];
+    const size_t scratch_bytes = L.total - L.off[11];
     const int R_max = T * k + s * T;
 
-    int e = moe_launch_route(a->logits, T, E_tot, k, a->flags, topk_idx, topk_w, stream);
-    if (e) return MOE_ERR_HIP;
-    e = moe_launch_permute(topk_idx, topk_w, T, k, e0, E_loc, s, a->xq, a->xs, H, counts, offsets,
-                           offsets32, row_src, row_w, slot_row, xq_perm, xs_perm, scratch, stream);
-    if (e) return MOE_ERR_HIP;
+    int e;
+    if (moe_route_permute_fusable(T, E_tot, k, E_loc, s)) {
+        e = moe_launch_route_permute(a->logits, T, E_tot, k, a->flags, e0, E_loc, s, topk_idx,
+                                     topk_w, counts, offsets, offsets32, row_src, row_w, slot_row,
+                                     stream);
+        if (e) return MOE_ERR_HIP;
+    } else {
+        e = moe_launch_route(a->logits, T, E_tot, k, a->flags, topk_idx, topk_w, stream);
+        if (e) return MOE_ERR_HIP;
+        e = moe_launch_permute(topk_idx, topk_w, T, k, e0, E_loc, s, nullptr, nullptr, H, counts,
+                               offsets, offsets32, row_src, row_w, slot_row, nullptr, nullptr,
+                               scratch, stream);
+        if (e) return MOE_ERR_HIP;
+    }
     // expected rows of a routed group under uniform routing; the shared group
     // (T rows) gets more passes from the grid's pass dimension
     const int hint = moe_layer_rows_hint(T, E_tot, k);
-    st = grouped_w1_impl(a->w1, a->shared_w1, counts, offsets, offsets32, row_w, xq_perm, xs_perm,
-                         R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch, scratch_bytes,
-                         hint, stream);
+    st = grouped_w1_impl(a->w1, a->shared_w1, counts, offsets, offsets32, row_w, a->xq, a->xs,
+                         row_src, R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch,
+                         scratch_bytes, hint, stream);
     if (st) return st;
     st = grouped_w2_impl(a->w2, a->shared_w2, counts, offsets, hq, hs, R_max, H, I, G, y, scratch,
                          scratch_bytes, hint, stream);

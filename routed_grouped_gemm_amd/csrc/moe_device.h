@@ -119,3 +119,92 @@ MOE_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
 MOE_DEV float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 
 MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions with DPP (no LDS traffic). The result is returned to every
+// lane; the combination order is fixed, so sums are deterministic.
+// ---------------------------------------------------------------------------
+#define MOE_DPP(v, ctrl, rmask) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), \
+                                                         __builtin_bit_cast(int, v), ctrl, rmask, 0xF, false))
+#define MOE_DPP_XOR1 0xB1        // quad_perm(1,0,3,2)
+#define MOE_DPP_XOR2 0x4E        // quad_perm(2,3,0,1)
+#define MOE_DPP_HALF_MIRROR 0x141
+#define MOE_DPP_MIRROR 0x140
+#define MOE_DPP_BCAST15 0x142
+#define MOE_DPP_BCAST31 0x143
+
+MOE_DEV float wave_max(float v) {
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_XOR1, 0xF));
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_XOR2, 0xF));
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_HALF_MIRROR, 0xF));
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_MIRROR, 0xF));
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_BCAST15, 0xA));
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_BCAST31, 0xC));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+MOE_DEV float wave_sum(float v) {
+    v += MOE_DPP(v, MOE_DPP_XOR1, 0xF);
+    v += MOE_DPP(v, MOE_DPP_XOR2, 0xF);
+    v += MOE_DPP(v, MOE_DPP_HALF_MIRROR, 0xF);
+    v += MOE_DPP(v, MOE_DPP_MIRROR, 0xF);
+    v += MOE_DPP(v, MOE_DPP_BCAST15, 0xA);
+    v += MOE_DPP(v, MOE_DPP_BCAST31, 0xC);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// ---------------------------------------------------------------------------
+// Top-k softmax routing of one token by one wave (logits row of E <= 64*VPL
+// floats). Lane l holds experts [l*VPL, l*VPL + VPL): a lower lane holds lower
+// expert ids, so among lanes whose best remaining logit equals the wave
+// maximum, the lowest lane holds the lowest id, which resolves ties to the
+// lower expert id. Selection compares fp32 logits; the weight of a selected
+// expert is exp(l - max) / sum_e exp(l_e - max) in fp32. On return lane j < k
+// holds the j-th selection in (sel_e, sel_w); other lanes are unchanged.
+// ---------------------------------------------------------------------------
+template <int VPL>
+MOE_DEV void wave_route_values(const float (&v)[VPL], int E, int k, bool renorm, int lane,
+                               int& sel_e, float& sel_w) {
+    const int base = lane * VPL;
+    float lm = -INFINITY;
+    #pragma unroll
+    for (int i = 0; i < VPL; ++i) lm = (base + i < E) ? fmaxf(lm, v[i]) : lm;
+    const float m = wave_max(lm);
+    float ls = 0.f;
+    #pragma unroll
+    for (int i = 0; i < VPL; ++i) ls += (base + i < E) ? expf(v[i] - m) : 0.f;
+    const float inv = 1.0f / wave_sum(ls);
+
+    uint32_t taken = 0;
+    float wsum = 0.f, my_w = 0.f;
+    int my_e = -1;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = -1;
+        #pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const bool ok = (base + i < E) && !((taken >> i) & 1u);
+            if (ok && (bi < 0 || v[i] > bv)) { bv = v[i]; bi = i; }
+        }
+        const float mx = wave_max(bi >= 0 ? bv : -INFINITY);
+        const uint64_t hit = __ballot(bi >= 0 && bv == mx);
+        const int win = __ffsll((unsigned long long)hit) - 1;
+        const int e = __builtin_amdgcn_readlane(base + bi, win);
+        if (lane == win) taken |= 1u << bi;
+        const float w = expf(mx - m) * inv;
+        wsum += w;
+        if (lane == j) { my_e = e; my_w = w; }
+    }
+    if (lane < k) {
+        sel_e = my_e;
+        sel_w = renorm ? my_w / wsum : my_w;
+    }
+}
+
+template <int VPL>
+MOE_DEV void load_logits(const float* __restrict__ row, int E, int lane, float (&v)[VPL]) {
+    const int base = lane * VPL;
+    #pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] = (base + i < E) ? row[base + i] : -INFINITY;
+}

@@ -30,6 +30,12 @@ int moe_launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int 
                        float* row_w, int32_t* slot_row, uint8_t* xq_perm, uint8_t* xs_perm,
                        void* scratch, hipStream_t stream);
 
+bool moe_route_permute_fusable(int T, int E, int k, int E_loc, int s);
+int moe_launch_route_permute(const float* logits, int T, int E, int k, uint32_t flags, int e0,
+                             int E_loc, int s, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                             int32_t* offsets, int32_t* offsets32, int32_t* row_src, float* row_w,
+                             int32_t* slot_row, hipStream_t stream);
+
 struct GemmArgs {
     const uint8_t* w_base[2];    // prepacked routed groups, shared group
     int E_loc;                   // groups < E_loc use [0], group E_loc uses [1]
@@ -38,8 +44,9 @@ struct GemmArgs {
     const int32_t* offsets;
     const int32_t* offsets32;
     const float* row_w;          // W1 only; null = weight 1
-    const uint8_t* aq;           // activations [R_max, K] E4M3
-    const uint8_t* as;           // [R_max, K/32]
+    const uint8_t* aq;           // activations [R_max, K] E4M3 (or [T, K] with row_src)
+    const uint8_t* as;           // [R_max, K/32]               (or [T, K/32])
+    const int32_t* row_src;      // null, or: grouped row r reads activation row row_src[r]
     int R_max;
     int rows_hint;               // expected rows per group (0: R_max / G)
     uint32_t flags;

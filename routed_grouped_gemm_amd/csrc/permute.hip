@@ -8,14 +8,21 @@
 // takes tokens 0..T-1. Determinism comes from construction, not from the
 // order of atomics: per-wave ranks use a ballot "match any" loop, per-chunk
 // wave totals are scanned in LDS, and chunk bases come from a scan over chunks.
+//
+// Paths: up to 4096 assignments a single workgroup does everything; for a few
+// tokens the router runs in that same workgroup (one launch for S1-S3). Larger
+// inputs use three kernels: per-chunk histograms, a scan, a scatter.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace {
 
-constexpr int kThreads = 512;          // 8 waves; one chunk = 512 assignments
-constexpr int kWaves = kThreads / 64;
-constexpr int kSmallChunks = 8;        // single-workgroup path up to 4096 assignments
+constexpr int kChunkThreads = 512;      // chunked path: one chunk = 512 assignments
+constexpr int kSmallMax = 4096;         // single-workgroup path up to this many assignments
+constexpr int kFusedThreads = 1024;     // route + permute in one workgroup
+constexpr int kFusedTPW = 4;            // tokens per wave in the fused kernel
+constexpr int kFusedMaxT = kFusedThreads / 64 * kFusedTPW;
+constexpr int kFusedMaxG = 513;
 
 MOE_DEV uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
 
@@ -42,7 +49,8 @@ MOE_DEV int block_exclusive_scan(int* vals, int n, int* part) {
     return total;
 }
 
-// counts (LDS, G entries) -> counts/offsets/offsets32 in global memory.
+// counts (LDS, G entries) -> counts/offsets/offsets32 in global memory; the
+// LDS array holds the offsets afterwards.
 MOE_DEV void write_offsets(int* lds_counts, int* lds_tmp, int G, int* part,
                            int32_t* counts, int32_t* offsets, int32_t* offsets32) {
     const int tid = threadIdx.x, nt = blockDim.x;
@@ -51,7 +59,7 @@ MOE_DEV void write_offsets(int* lds_counts, int* lds_tmp, int G, int* part,
         lds_tmp[g] = (lds_counts[g] + 31) & ~31;
     }
     __syncthreads();
-    int total = block_exclusive_scan(lds_counts, G, part);   // lds_counts becomes offsets
+    int total = block_exclusive_scan(lds_counts, G, part);
     int total32 = 0;
     if (offsets32) total32 = block_exclusive_scan(lds_tmp, G, part);
     for (int g = tid; g < G; g += nt) {
@@ -81,13 +89,14 @@ MOE_DEV int wave_match_rank(int g, int lane, uint16_t* wave_cnt /* [E_loc] of th
     return rank;
 }
 
-// Chunk: wave ranks -> per-wave exclusive prefix in cnt (in place) and the
-// chunk totals in tot (if non-null). Callers zero cnt beforehand.
+// Per-wave lane counts of one chunk -> per-wave exclusive prefix (in place),
+// and the chunk totals in tot (if non-null).
+template <int NW>
 MOE_DEV void scan_waves(uint16_t* cnt, int E_loc, int* tot) {
     for (int g = threadIdx.x; g < E_loc; g += blockDim.x) {
         int run = 0;
         #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             int v = cnt[w * E_loc + g];
             cnt[w * E_loc + g] = (uint16_t)run;
             run += v;
@@ -96,12 +105,12 @@ MOE_DEV void scan_waves(uint16_t* cnt, int E_loc, int* tot) {
     }
 }
 
-MOE_DEV void write_row(int a, int g, int row, int k, int ks, const float* topk_w,
+MOE_DEV void write_row(int a, int g, int row, int k, int ks, float w,
                        int32_t* row_src, float* row_w, int32_t* slot_row) {
     int t = a / k, j = a - t * k;
     if (g >= 0) {
         row_src[row] = t;
-        row_w[row] = topk_w[a];
+        row_w[row] = w;
         slot_row[(size_t)t * ks + j] = row;
     } else {
         slot_row[(size_t)t * ks + j] = -1;
@@ -118,74 +127,130 @@ MOE_DEV void write_shared_rows(int t0, int t1, int T, int k, int ks, int base,
     }
 }
 
-// ---- single-workgroup path ---------------------------------------------
-__global__ __launch_bounds__(kThreads)
-void permute_small_kernel(const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
-                          int T, int k, int e0, int E_loc, int s,
-                          int32_t* counts, int32_t* offsets, int32_t* offsets32,
-                          int32_t* row_src, float* row_w, int32_t* slot_row) {
-    extern __shared__ int lds[];
+// LDS ints needed by permute_in_block.
+constexpr size_t block_lds_ints(int NW, int G, int E_loc) {
+    return (size_t)3 * G + (size_t)NW * 64 + ((size_t)NW * E_loc * 2 + 3) / 4;
+}
+
+// The whole S2/S3 computation of up to 4096 assignments in one workgroup of
+// NW waves. idx_of(a) / w_of(a) read the routing of flattened assignment a.
+template <int NW, class IdxF, class WF>
+MOE_DEV void permute_in_block(IdxF idx_of, WF w_of, int T, int k, int e0, int E_loc, int s,
+                              int32_t* counts, int32_t* offsets, int32_t* offsets32,
+                              int32_t* row_src, float* row_w, int32_t* slot_row, int* lds) {
+    constexpr int NT = NW * 64;
     const int G = E_loc + s;
     int* hist = lds;                       // [G]   counts, then offsets
     int* tmp = hist + G;                   // [G]   roundup counts / chunk totals
     int* base = tmp + G;                   // [G]   running row of each group
-    int* part = base + G;                  // [kThreads]
-    uint16_t* cnt = (uint16_t*)(part + kThreads);   // [kWaves][E_loc]
+    int* part = base + G;                  // [NT]
+    uint16_t* cnt = (uint16_t*)(part + NT);    // [NW][E_loc]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int Tk = T * k, ks = k + s;
 
-    for (int g = tid; g < G; g += kThreads) hist[g] = 0;
+    for (int g = tid; g < G; g += NT) hist[g] = 0;
     __syncthreads();
-    for (int a = tid; a < Tk; a += kThreads) {
-        int g = topk_idx[a] - e0;
+    for (int a = tid; a < Tk; a += NT) {
+        int g = idx_of(a) - e0;
         if (g >= 0 && g < E_loc) atomicAdd(&hist[g], 1);
     }
     __syncthreads();
     if (s && tid == 0) hist[E_loc] = T;
     __syncthreads();
     write_offsets(hist, tmp, G, part, counts, offsets, offsets32);
-    for (int g = tid; g < G; g += kThreads) base[g] = hist[g];
+    for (int g = tid; g < G; g += NT) base[g] = hist[g];
     __syncthreads();
 
-    for (int c0 = 0; c0 < Tk; c0 += kThreads) {
-        for (int i = tid; i < kWaves * E_loc; i += kThreads) cnt[i] = 0;
+    for (int c0 = 0; c0 < Tk; c0 += NT) {
+        for (int i = tid; i < NW * E_loc; i += NT) cnt[i] = 0;
         __syncthreads();
-        int a = c0 + tid;
+        const int a = c0 + tid;
         int g = -1;
         if (a < Tk) {
-            int gg = topk_idx[a] - e0;
+            int gg = idx_of(a) - e0;
             if (gg >= 0 && gg < E_loc) g = gg;
         }
-        int rank = wave_match_rank(g, lane, cnt + w * E_loc);
+        const int rank = wave_match_rank(g, lane, cnt + w * E_loc);
         __syncthreads();
-        scan_waves(cnt, E_loc, tmp);
+        scan_waves<NW>(cnt, E_loc, tmp);
         __syncthreads();
         if (a < Tk) {
             int row = g >= 0 ? base[g] + cnt[w * E_loc + g] + rank : -1;
-            write_row(a, g, row, k, ks, topk_w, row_src, row_w, slot_row);
+            write_row(a, g, row, k, ks, g >= 0 ? w_of(a) : 0.f, row_src, row_w, slot_row);
         }
         __syncthreads();
-        for (int gg = tid; gg < E_loc; gg += kThreads) base[gg] += tmp[gg];
+        for (int gg = tid; gg < E_loc; gg += NT) base[gg] += tmp[gg];
         __syncthreads();
     }
     if (s) write_shared_rows(0, T, T, k, ks, hist[E_loc], row_src, row_w, slot_row);
 }
 
+// ---- single-workgroup path ---------------------------------------------
+__global__ __launch_bounds__(kChunkThreads)
+void permute_small_kernel(const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+                          int T, int k, int e0, int E_loc, int s,
+                          int32_t* counts, int32_t* offsets, int32_t* offsets32,
+                          int32_t* row_src, float* row_w, int32_t* slot_row) {
+    extern __shared__ int lds[];
+    permute_in_block<kChunkThreads / 64>(
+        [&](int a) { return topk_idx[a]; }, [&](int a) { return topk_w[a]; },
+        T, k, e0, E_loc, s, counts, offsets, offsets32, row_src, row_w, slot_row, lds);
+}
+
+// ---- router + single-workgroup permute in one launch (few tokens) -------
+template <int VPL>
+__global__ __launch_bounds__(kFusedThreads)
+void route_permute_kernel(const float* __restrict__ logits, int T, int E, int k, int renorm,
+                          int e0, int E_loc, int s, int32_t* __restrict__ topk_idx,
+                          float* __restrict__ topk_w, int32_t* counts, int32_t* offsets,
+                          int32_t* offsets32, int32_t* row_src, float* row_w, int32_t* slot_row) {
+    extern __shared__ int lds[];
+    int* sidx = lds;                        // [T*k]
+    float* sw = (float*)(lds + T * k);      // [T*k]
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    constexpr int NW = kFusedThreads / 64;
+    float v[kFusedTPW][VPL];
+    #pragma unroll
+    for (int i = 0; i < kFusedTPW; ++i) {       // issue every token's loads first
+        const int t = w + NW * i;
+        if (t < T) load_logits<VPL>(logits + (size_t)t * E, E, lane, v[i]);
+    }
+    #pragma unroll
+    for (int i = 0; i < kFusedTPW; ++i) {
+        const int t = w + NW * i;
+        if (t < T) {
+            int e = 0;
+            float wt = 0.f;
+            wave_route_values<VPL>(v[i], E, k, renorm != 0, lane, e, wt);
+            if (lane < k) {
+                sidx[t * k + lane] = e;
+                sw[t * k + lane] = wt;
+                topk_idx[(size_t)t * k + lane] = e;
+                topk_w[(size_t)t * k + lane] = wt;
+            }
+        }
+    }
+    __syncthreads();
+    permute_in_block<NW>([&](int a) { return sidx[a]; }, [&](int a) { return sw[a]; },
+                         T, k, e0, E_loc, s, counts, offsets, offsets32, row_src, row_w, slot_row,
+                         lds + 2 * T * k);
+}
+
 // ---- chunked path: count, scan, scatter --------------------------------
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kChunkThreads)
 void permute_count_kernel(const int32_t* __restrict__ topk_idx, int Tk, int e0, int E_loc,
                           int32_t* __restrict__ chunk_hist) {
     extern __shared__ int lds[];
     const int tid = threadIdx.x, c = blockIdx.x;
-    for (int g = tid; g < E_loc; g += kThreads) lds[g] = 0;
+    for (int g = tid; g < E_loc; g += kChunkThreads) lds[g] = 0;
     __syncthreads();
-    int a = c * kThreads + tid;
+    int a = c * kChunkThreads + tid;
     if (a < Tk) {
         int g = topk_idx[a] - e0;
         if (g >= 0 && g < E_loc) atomicAdd(&lds[g], 1);
     }
     __syncthreads();
-    for (int g = tid; g < E_loc; g += kThreads) chunk_hist[(size_t)c * E_loc + g] = lds[g];
+    for (int g = tid; g < E_loc; g += kChunkThreads) chunk_hist[(size_t)c * E_loc + g] = lds[g];
 }
 
 // Scan of the per-chunk histograms: for every expert, the exclusive prefix over
@@ -258,18 +323,19 @@ void permute_scan_kernel(int32_t* __restrict__ chunk_hist, int nchunks, int T, i
     }
 }
 
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kChunkThreads)
 void permute_scatter_kernel(const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
                             int T, int k, int e0, int E_loc, int s,
                             const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
                             int32_t* row_src, float* row_w, int32_t* slot_row) {
+    constexpr int NW = kChunkThreads / 64;
     extern __shared__ int lds[];
-    uint16_t* cnt = (uint16_t*)lds;          // [kWaves][E_loc]
+    uint16_t* cnt = (uint16_t*)lds;          // [NW][E_loc]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = blockIdx.x;
     const int Tk = T * k, ks = k + s;
-    for (int i = tid; i < kWaves * E_loc; i += kThreads) cnt[i] = 0;
+    for (int i = tid; i < NW * E_loc; i += kChunkThreads) cnt[i] = 0;
     __syncthreads();
-    int a = c * kThreads + tid;
+    int a = c * kChunkThreads + tid;
     int g = -1;
     if (a < Tk) {
         int gg = topk_idx[a] - e0;
@@ -277,13 +343,13 @@ void permute_scatter_kernel(const int32_t* __restrict__ topk_idx, const float* _
     }
     int rank = wave_match_rank(g, lane, cnt + w * E_loc);
     __syncthreads();
-    scan_waves(cnt, E_loc, nullptr);
+    scan_waves<NW>(cnt, E_loc, nullptr);
     __syncthreads();
     if (a < Tk) {
         int row = g >= 0 ? chunk_base[(size_t)c * E_loc + g] + cnt[w * E_loc + g] + rank : -1;
-        write_row(a, g, row, k, ks, topk_w, row_src, row_w, slot_row);
+        write_row(a, g, row, k, ks, g >= 0 ? topk_w[a] : 0.f, row_src, row_w, slot_row);
     }
-    if (s) write_shared_rows(c * kThreads, (c + 1) * kThreads, T, k, ks, offsets[E_loc],
+    if (s) write_shared_rows(c * kChunkThreads, (c + 1) * kChunkThreads, T, k, ks, offsets[E_loc],
                              row_src, row_w, slot_row);
 }
 
@@ -311,11 +377,21 @@ void gather_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ x
     }
 }
 
+int launch_gather(const uint8_t* xq, const uint8_t* xs, int H, const int32_t* row_src,
+                  const int32_t* offsets, int G, int R_max, uint8_t* xq_perm, uint8_t* xs_perm,
+                  hipStream_t stream) {
+    int blocks = (R_max + kGatherRows - 1) / kGatherRows;
+    hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, stream, xq, xs, H, row_src,
+                       offsets, G, xq_perm, xs_perm);
+    return (int)hipGetLastError();
+}
+
 }  // namespace
 
 size_t moe_permute_scratch_bytes(int T, int k, int G) {
-    size_t nchunks = ((size_t)T * k + kThreads - 1) / kThreads;
-    return (nchunks > (size_t)kSmallChunks) ? nchunks * (size_t)G * 4 : 0;
+    size_t Tk = (size_t)T * k;
+    size_t nchunks = (Tk + kChunkThreads - 1) / kChunkThreads;
+    return (Tk > (size_t)kSmallMax) ? nchunks * (size_t)G * 4 : 0;
 }
 
 int moe_launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int k, int e0,
@@ -325,33 +401,57 @@ int moe_launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int 
                        void* scratch, hipStream_t stream) {
     const int G = E_loc + s;
     const int Tk = T * k;
-    const int nchunks = (Tk + kThreads - 1) / kThreads;
     hipError_t e;
-    if (nchunks <= kSmallChunks) {
-        size_t lds = (size_t)(3 * G + kThreads) * 4 + (size_t)kWaves * E_loc * 2;
-        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kThreads), lds, stream,
+    if (Tk <= kSmallMax) {
+        size_t lds = block_lds_ints(kChunkThreads / 64, G, E_loc) * 4;
+        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kChunkThreads), lds, stream,
                            topk_idx, topk_w, T, k, e0, E_loc, s, counts, offsets, offsets32,
                            row_src, row_w, slot_row);
     } else {
+        const int nchunks = (Tk + kChunkThreads - 1) / kChunkThreads;
         int32_t* chunk_hist = (int32_t*)scratch;
-        hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(kThreads),
+        hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(kChunkThreads),
                            (size_t)E_loc * 4, stream, topk_idx, Tk, e0, E_loc, chunk_hist);
         int P = 1;
         while (P * 2 <= kScanThreads / E_loc && P * 2 <= nchunks) P *= 2;
         hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads),
                            (size_t)(2 * G + 2 * kScanThreads) * 4, stream, chunk_hist, nchunks, T,
                            E_loc, s, P, counts, offsets, offsets32);
-        hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(kThreads),
-                           (size_t)kWaves * E_loc * 2 + 4, stream, topk_idx, topk_w, T, k, e0,
-                           E_loc, s, chunk_hist, offsets, row_src, row_w, slot_row);
+        hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(kChunkThreads),
+                           (size_t)(kChunkThreads / 64) * E_loc * 2 + 4, stream, topk_idx, topk_w,
+                           T, k, e0, E_loc, s, chunk_hist, offsets, row_src, row_w, slot_row);
     }
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-    if (xq_perm && T > 0) {
-        const int R_max = Tk + s * T;
-        int blocks = (R_max + kGatherRows - 1) / kGatherRows;
-        hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, stream, xq, xs, H, row_src,
-                           offsets, G, xq_perm, xs_perm);
-        if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-    }
+    if (xq_perm && T > 0)
+        return launch_gather(xq, xs, H, row_src, offsets, G, Tk + s * T, xq_perm, xs_perm, stream);
     return 0;
+}
+
+bool moe_route_permute_fusable(int T, int E, int k, int E_loc, int s) {
+    return T <= kFusedMaxT && E <= 2048 && E_loc + s <= kFusedMaxG && T * k <= kSmallMax;
+}
+
+int moe_launch_route_permute(const float* logits, int T, int E, int k, uint32_t flags, int e0,
+                             int E_loc, int s, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                             int32_t* offsets, int32_t* offsets32, int32_t* row_src, float* row_w,
+                             int32_t* slot_row, hipStream_t stream) {
+    const int G = E_loc + s;
+    const int renorm = (flags & MOE_ROUTE_RENORM) ? 1 : 0;
+    const size_t lds = ((size_t)2 * T * k + block_lds_ints(kFusedThreads / 64, G, E_loc)) * 4;
+    const int vpl = (E + 63) / 64;
+#define MOE_RP_CASE(N)                                                                         \
+    if (vpl <= N) {                                                                            \
+        hipLaunchKernelGGL(route_permute_kernel<N>, dim3(1), dim3(kFusedThreads), lds, stream, \
+                           logits, T, E, k, renorm, e0, E_loc, s, topk_idx, topk_w, counts,    \
+                           offsets, offsets32, row_src, row_w, slot_row);                      \
+        return (int)hipGetLastError();                                                         \
+    }
+    MOE_RP_CASE(1)
+    MOE_RP_CASE(2)
+    MOE_RP_CASE(4)
+    MOE_RP_CASE(8)
+    MOE_RP_CASE(16)
+    MOE_RP_CASE(32)
+#undef MOE_RP_CASE
+    return -1;
 }

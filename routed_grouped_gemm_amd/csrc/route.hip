@@ -12,7 +12,6 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-// Lane-strided: lane l holds experts l, l + 64, l + 128, ... (VPL per lane).
 template <int VPL>
 __global__ __launch_bounds__(64 * kWavesPerBlock)
 void route_kernel(const float* __restrict__ logits, int T, int E, int k, int renorm,
@@ -20,62 +19,14 @@ void route_kernel(const float* __restrict__ logits, int T, int E, int k, int ren
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float* row = logits + (size_t)t * E;
-
+    int e = 0;
+    float w = 0.f;
     float v[VPL];
-    #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        int e = lane + 64 * i;
-        v[i] = e < E ? row[e] : -INFINITY;
-    }
-    // global max: the top-1 logit
-    float m = v[0];
-    #pragma unroll
-    for (int i = 1; i < VPL; ++i) m = fmaxf(m, v[i]);
-    #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-    // softmax denominator, fp32, fixed reduction tree
-    float sum = 0.f;
-    #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        int e = lane + 64 * i;
-        if (e < E) sum += expf(v[i] - m);
-    }
-    #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) sum += __shfl_xor(sum, s, 64);
-    const float inv = 1.0f / sum;
-
-    uint32_t taken = 0;                 // per-lane bitmask over its VPL slots
-    float wsum = 0.f;
-    int my_j = -1;                      // lane j (< k) stores result j
-    int   res_e = 0;
-    float res_w = 0.f;
-    for (int j = 0; j < k; ++j) {
-        // lane-local best among not-taken: larger value, then lower expert id
-        float bv = -INFINITY;
-        int be = 0x7FFFFFFF;
-        #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            int e = lane + 64 * i;
-            bool ok = e < E && !((taken >> i) & 1u);
-            if (ok && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
-        }
-        // wave argmax
-        #pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) {
-            float ov = __shfl_xor(bv, s, 64);
-            int oe = __shfl_xor(be, s, 64);
-            if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        float w = expf(bv - m) * inv;
-        wsum += w;
-        if (lane == j) { res_e = be; res_w = w; my_j = j; }
-    }
-    if (my_j >= 0) {
-        float w = renorm ? res_w / wsum : res_w;
-        topk_idx[(size_t)t * k + my_j] = res_e;
-        topk_w[(size_t)t * k + my_j] = w;
+    load_logits<VPL>(logits + (size_t)t * E, E, lane, v);
+    wave_route_values<VPL>(v, E, k, renorm != 0, lane, e, w);
+    if (lane < k) {
+        topk_idx[(size_t)t * k + lane] = e;
+        topk_w[(size_t)t * k + lane] = w;
     }
 }
 

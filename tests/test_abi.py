@@ -68,10 +68,10 @@ def test_sizes_are_pure_host_functions():
     # layer workspace holds at least every intermediate for R_max rows
     T, E, k, El, H, I = 128, 256, 8, 32, 7168, 2048
     R = T * k
-    need = R * H + R * H // 32 + R * I + R * I // 32 + 2 * R * H
+    need = R * I + R * I // 32 + 2 * R * H
     assert lib.moe_layer_workspace_size(T, E, k, El, H, I, 0, 0) >= need
-    offs = (C.c_size_t * 14)()
-    assert lib.moe_layer_workspace_offsets(T, E, k, El, H, I, 0, 0, offs) == 14
+    offs = (C.c_size_t * 12)()
+    assert lib.moe_layer_workspace_offsets(T, E, k, El, H, I, 0, 0, offs) == 12
     assert all(o % 256 == 0 for o in offs) and list(offs) == sorted(offs)
 
 

@@ -130,8 +130,10 @@ def _packed(ws, fmt, is_w1):
 
 
 W1_CASES = [
-    # counts, H, I, fmt, flags
+    # counts, H, I, fmt, flags  (flags bit 31: read the token rows through row_src)
     ([0, 1, 17, 70, 33, 5], 1024, 512, "e2m1", 0),
+    ([2, 0, 40, 9], 1024, 256, "e2m1", 1 << 31),
+    ([64, 3], 512, 256, "e4m3", (1 << 31) | moe.MOE_W1_WRITE_TRANSPOSE),
     ([3, 0, 64, 129], 512, 256, "e4m3", 0),
     ([45, 0, 100, 32, 1], 512, 384, "e4m3", moe.MOE_W1_WRITE_TRANSPOSE),
     ([7, 90], 768, 256, "e2m1", moe.MOE_SCALE_RULE_CEIL | moe.MOE_W1_WRITE_TRANSPOSE),
@@ -142,9 +144,19 @@ W1_CASES = [
 @pytest.mark.parametrize("counts,H,I,fmt,flags", W1_CASES)
 def test_grouped_w1_parity(counts, H, I, fmt, flags):
     banner(f"grouped_w1 counts={counts} H={H} I={I} fmt={fmt} flags={flags}")
+    gather = bool(flags & (1 << 31))
+    flags &= ~(1 << 31)
     offsets, xq, xs, row_w, w1, _ = _grouped_problem(counts, H, I, fmt, 5 + H + I)
     G = len(counts)
     R = int(offsets[-1])
+    row_src = None
+    if gather:
+        # the grouped rows are token rows picked through row_src from a token array
+        rng = np.random.default_rng(R)
+        T = max(R // 2, 1)
+        tq, ts = mx.quantize_mx(rng.standard_normal((T, H)), mx.FMT_E4M3)
+        row_src = rng.integers(0, T, R).astype(np.int32)
+        xq, xs = tq[row_src], ts[row_src]
     rule = "ceil" if flags & moe.MOE_SCALE_RULE_CEIL else "ocp"
     wts = np.ones(R) if flags & moe.MOE_WEIGHT_AT_COMBINE else row_w.astype(np.float64)
     transpose = bool(flags & moe.MOE_W1_WRITE_TRANSPOSE)
@@ -154,8 +166,12 @@ def test_grouped_w1_parity(counts, H, I, fmt, flags):
     counts_d = dev(np.array(counts, np.int32))
     off32 = np.zeros(G + 1, np.int32)
     off32[1:] = np.cumsum((np.array(counts) + 31) // 32 * 32)
-    hq, hs, hTq, hTs = moe.moe_grouped_w1(pw, counts_d, dev(offsets), dev(row_w), dev(xq), dev(xs), I,
-                                          flags, offsets32=dev(off32))
+    if gather:
+        hq, hs, hTq, hTs = moe.moe_grouped_w1(pw, counts_d, dev(offsets), dev(row_w), dev(tq), dev(ts), I,
+                                              flags, offsets32=dev(off32), row_src=dev(row_src), R_max=R)
+    else:
+        hq, hs, hTq, hTs = moe.moe_grouped_w1(pw, counts_d, dev(offsets), dev(row_w), dev(xq), dev(xs), I,
+                                              flags, offsets32=dev(off32))
     dh = _h_error_bound(xq, xs, offsets, w1, fmt, I, ref, wts)
     assert_mx_within_1ulp(host(hq)[:R], host(hs)[:R], ref.hq, ref.hs, "h", extra_tol=dh)
     if transpose:
