@@ -90,7 +90,7 @@ def cpu_baseline(c8, moe_bytes_fn):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated between calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -146,8 +146,9 @@ def main():
     def step_bytes(i):
         return sum(layer_bytes(T, c.E, c.H, c.I, active[T, i % N_VARIANTS], fp4) for T in DECODE_T)
 
-    # The launch sequence is captured once per routing draw into a HIP graph
-    # (no host work or host sync inside a layer call) and replayed.
+    # The launch sequence is captured once into HIP graphs and replayed: one
+    # graph per single step (routing draw i % 16) and one graph holding the 16
+    # steps of a full cycle of draws, so the host never paces the GPU.
     torch.cuda.synchronize()
     step_graphs = []
     for v in range(N_VARIANTS):
@@ -155,21 +156,26 @@ def main():
         with torch.cuda.graph(g):
             step(v)
         step_graphs.append(g)
-    call_graphs = {}
-    for T in DECODE_T:
+    cycle_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cycle_graph):
         for v in range(N_VARIANTS):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                call(T, v, copies[v % len(copies)])
-            call_graphs[T, v] = g
+            step(v)
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        step_graphs[i % N_VARIANTS].replay()
+    def run_steps(first, n):
+        i = first
+        while i < first + n:
+            if i % N_VARIANTS == 0 and first + n - i >= N_VARIANTS:
+                cycle_graph.replay()
+                i += N_VARIANTS
+            else:
+                step_graphs[i % N_VARIANTS].replay()
+                i += 1
+
+    run_steps(0, args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.warmup, args.warmup + args.steps):
-        step_graphs[i % N_VARIANTS].replay()
+    run_steps(args.warmup, args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + args.steps))
@@ -184,21 +190,37 @@ def main():
     torch.cuda.synchronize()
     eager_tbps = sum(step_bytes(i) for i in range(args.steps)) / (time.perf_counter() - t0) / 1e12
 
-    # per-T layer latency (HIP events on the replay stream), same rotation
+    # a plain copy of known size (1 GiB), so hardware byte counters collected
+    # on this run can be calibrated against it
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+    # per-T layer latency: a graph of 16 consecutive calls (one per routing
+    # draw, rotating weight copies), timed with HIP events on the replay stream
     stream = torch.cuda.current_stream()
     per_t = {}
-    reps = max(16, args.steps)
     for T in DECODE_T:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for v in range(N_VARIANTS):
+                call(T, v, copies[v % len(copies)])
+        g.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 4
         e0.record(stream)
-        for r in range(reps):
-            call_graphs[T, r % N_VARIANTS].replay()
+        for _ in range(reps):
+            g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        b = sum(layer_bytes(T, c.E, c.H, c.I, active[T, r % N_VARIANTS], fp4) for r in range(reps)) / reps
+        us = e0.elapsed_time(e1) * 1e3 / (reps * N_VARIANTS)
+        b = sum(layer_bytes(T, c.E, c.H, c.I, active[T, v], fp4) for v in range(N_VARIANTS)) / N_VARIANTS
         per_t[str(T)] = {"latency_us": round(us, 2), "TBps": round(b / us / 1e6, 3),
                          "active_experts": round(sum(active[T, v] for v in range(N_VARIANTS)) / N_VARIANTS, 2)}
+    reps = max(16, args.steps)
 
     # dominant kernel: grouped W1. After a layer call has grouped the tokens,
     # W1 is launched again through its own entry point with the arguments
@@ -209,6 +231,7 @@ def main():
     for T in DECODE_T:
         ws = wss[T]
         hint = moe.moe_layer_rows_hint(T, c.E, c.k)
+        ahint = moe.moe_layer_active_hint(T, c.E, c.k, c.n_local, 0)
         for r in range(reps):
             v = r % N_VARIANTS
             lg, xq, xs = inputs[T][v]
@@ -219,7 +242,7 @@ def main():
             moe.moe_grouped_w1(w.w1, ws.view("counts"), ws.view("offsets"), ws.view("row_w"), xq, xs,
                                c.I, 0, offsets32=ws.view("offsets32"), hq=ws.view("hq"),
                                hs=ws.view("hs"), rows_hint=hint, row_src=ws.view("row_src"),
-                               R_max=T * c.k)
+                               R_max=T * c.k, active_hint=ahint)
             b.record(stream)
             torch.cuda.synchronize()
             w1_ms += a.elapsed_time(b)

@@ -186,7 +186,8 @@ int32_t moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t T, int
  * x_r is row r of xq/xs when row_src is NULL (xq [R_max, H], xs [R_max, H/32],
  * the grouped rows moe_permute gathers), or row row_src[r] of the ungrouped
  * token arrays xq [T, H], xs [T, H/32] when row_src is given (the gather is
- * then done by this kernel's loads).
+ * then done by this kernel's loads). x_rows is the row count of xq/xs
+ * (R_max or T); reads are bounded by it. x_rows * H < 2^31.
  * With MOE_W1_WRITE_TRANSPOSE also hTq/hTs: for group g, columns
  * [offsets32[g], offsets32[g+1]) of hTq [I, ldT] hold h_g^T quantised in
  * blocks of 32 tokens counted from the group's first row (hTs [I, ldT/32]);
@@ -195,8 +196,9 @@ int32_t moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t T, int
  * backward). ldT = moe_transposed_ld(R_max, G).
  * w1 holds the routed groups [0, E_loc); w1_shared (NULL when G == E_loc)
  * holds group E_loc. hq [R_max, I], hs [R_max, I/32]; rows >= R untouched.
- * rows_hint: expected rows per group, used only to choose the tiling
- * (0: R_max / G); results do not depend on it.
+ * rows_hint / active_hint: expected rows per group and expected number of
+ * groups with rows, used only to choose the tiling (0: derived from R_max
+ * and G); results do not depend on them.
  * ws: moe_grouped_workspace_size(...) bytes.
  */
 int32_t moe_transposed_ld(int32_t R_max, int32_t G);
@@ -204,27 +206,30 @@ size_t  moe_grouped_workspace_size(int32_t R_max, int32_t G, int32_t N, int32_t 
 int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_shared,
                        const int32_t* counts, const int32_t* offsets, const int32_t* offsets32,
                        const float* row_w, const uint8_t* xq, const uint8_t* xs,
-                       const int32_t* row_src,
+                       const int32_t* row_src, int32_t x_rows,
                        int32_t R_max, int32_t H, int32_t I, int32_t G, int32_t rows_hint,
-                       uint32_t flags, uint8_t* hq, uint8_t* hs, uint8_t* hTq, uint8_t* hTs,
-                       void* ws, size_t ws_bytes, hipStream_t stream);
+                       int32_t active_hint, uint32_t flags, uint8_t* hq, uint8_t* hs,
+                       uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- S6: grouped W2 ----------------------------------------------------- */
 /*
  * y[r] = BF16_RNE(dec(hq[r]) . dec(W2_g)^T) for every row r of group g
  * (W2 produces BF16 fragments: GC-MoE page, "Approach"). hq [R_max, I],
- * hs [R_max, I/32], y bf16 [R_max, H]; rows >= R untouched. rows_hint as
- * for moe_grouped_w1.
+ * hs [R_max, I/32], y bf16 [R_max, H]; rows >= R untouched. rows_hint and
+ * active_hint as for moe_grouped_w1. R_max * I < 2^31.
  */
 int32_t moe_grouped_w2(const moe_weights* w2, const moe_weights* w2_shared,
                        const int32_t* counts, const int32_t* offsets,
                        const uint8_t* hq, const uint8_t* hs,
                        int32_t R_max, int32_t H, int32_t I, int32_t G, int32_t rows_hint,
-                       uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+                       int32_t active_hint, uint16_t* y, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
 
-/* The rows_hint moe_layer passes to the grouped GEMMs: the expected rows of a
- * routed group under uniform routing, ceil(T * k / E_tot). */
+/* The hints moe_layer passes to the grouped GEMMs, from uniform routing: the
+ * expected rows of a routed group, ceil(T * k / E_tot), and the expected
+ * groups with rows, ceil(E_loc * (1 - (1 - k/E_tot)^T)) + s. */
 int32_t moe_layer_rows_hint(int32_t T, int32_t E_tot, int32_t k);
+int32_t moe_layer_active_hint(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc, int32_t s);
 
 /* ---- S7: combine ---------------------------------------------------------- */
 /*

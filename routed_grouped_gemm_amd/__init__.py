@@ -175,10 +175,14 @@ def moe_layer_rows_hint(T: int, E_tot: int, k: int) -> int:
     return int(lib.moe_layer_rows_hint(T, E_tot, k))
 
 
+def moe_layer_active_hint(T: int, E_tot: int, k: int, E_loc: int, s: int = 0) -> int:
+    return int(lib.moe_layer_active_hint(T, E_tot, k, E_loc, s))
+
+
 def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq, xs, I: int,
                    flags: int = 0, w1_shared: PackedWeights | None = None, offsets32=None,
                    hq=None, hs=None, hTq=None, hTs=None, rows_hint: int = 0, row_src=None,
-                   R_max: int | None = None, stream=None):
+                   R_max: int | None = None, active_hint: int = 0, stream=None):
     """xq/xs: the grouped rows [R_max, H] (row_src None) or the token rows
     [T, H] read through row_src (then R_max must be given)."""
     H = xq.shape[1]
@@ -197,13 +201,15 @@ def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq, xs, I: int,
     nws = int(lib.moe_grouped_workspace_size(R_max, G, 2 * I, H))
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     _check(lib.moe_grouped_w1(w1.ref(), _wref(w1_shared), _p(counts), _p(offsets), _p(offsets32),
-                              _p(row_w), _p(xq), _p(xs), _p(row_src), R_max, H, I, G, rows_hint, flags, _p(hq),
+                              _p(row_w), _p(xq), _p(xs), _p(row_src), xq.shape[0], R_max, H, I, G,
+                              rows_hint, active_hint, flags, _p(hq),
                               _p(hs), _p(hTq), _p(hTs), _p(ws), nws, _stream(stream)), "moe_grouped_w1")
     return hq, hs, hTq, hTs
 
 
 def moe_grouped_w2(w2: PackedWeights, counts, offsets, hq, hs, H: int,
-                   w2_shared: PackedWeights | None = None, y=None, rows_hint: int = 0, stream=None):
+                   w2_shared: PackedWeights | None = None, y=None, rows_hint: int = 0,
+                   active_hint: int = 0, stream=None):
     R_max, I = hq.shape
     G = counts.shape[0]
     if y is None:
@@ -211,7 +217,7 @@ def moe_grouped_w2(w2: PackedWeights, counts, offsets, hq, hs, H: int,
     nws = int(lib.moe_grouped_workspace_size(R_max, G, H, I))
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=hq.device)
     _check(lib.moe_grouped_w2(w2.ref(), _wref(w2_shared), _p(counts), _p(offsets), _p(hq), _p(hs),
-                              R_max, H, I, G, rows_hint, _p(y), _p(ws), nws, _stream(stream)),
+                              R_max, H, I, G, rows_hint, active_hint, _p(y), _p(ws), nws, _stream(stream)),
            "moe_grouped_w2")
     return y
 

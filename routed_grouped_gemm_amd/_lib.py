@@ -45,10 +45,11 @@ SIGNATURES = {
     "moe_permute": (I32, [P, P, I32, I32, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_transposed_ld": (I32, [I32, I32]),
     "moe_grouped_workspace_size": (SZ, [I32, I32, I32, I32]),
-    "moe_grouped_w1": (I32, [WP, WP, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, U32, P, P, P, P, P, SZ,
-                             P]),
-    "moe_grouped_w2": (I32, [WP, WP, P, P, P, P, I32, I32, I32, I32, I32, P, P, SZ, P]),
+    "moe_grouped_w1": (I32, [WP, WP, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, U32, P, P, P,
+                             P, P, SZ, P]),
+    "moe_grouped_w2": (I32, [WP, WP, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, SZ, P]),
     "moe_layer_rows_hint": (I32, [I32, I32, I32]),
+    "moe_layer_active_hint": (I32, [I32, I32, I32, I32, I32]),
     "moe_combine": (I32, [P, P, P, I32, I32, I32, P, P]),
     "moe_layer_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, U32]),
     "moe_layer": (I32, [C.POINTER(moe_layer_args), P, SZ, P]),

@@ -7,173 +7,269 @@
 // from HBM into registers in one 1-2 KiB burst per wave) and 16 grouped token
 // rows are the B operand. A workgroup owns one 64-row weight unit of one group
 // (for W1: 32 gate + the matching 32 up rows) and a pass of up to 16*NTT rows
-// of that group; its 4 waves split K in runs of four 128-wide K-tiles and
-// their partial sums are added in LDS in a fixed order, so results do not
-// depend on scheduling. Group sizes are read from device memory: workgroups of
-// empty groups or of passes past a group's end exit at once (no host sync;
-// fusion blog, "Removing host-device synchronisation").
+// of that group; its KW waves split K into contiguous runs of 128-wide K-tiles
+// and their partial sums are added in LDS in a fixed tree order, so results do
+// not depend on scheduling. Group sizes are read from device memory:
+// workgroups of empty groups or of passes past a group's end exit at once (no
+// host sync; fusion blog, "Removing host-device synchronisation").
+//
+// Memory pipeline: every operand is read with buffer loads whose resource
+// bounds the region, so an access marked invalid (past the wave's K run, past
+// the pass's rows) returns zeros without a branch and without memory traffic.
+// A wave issues the loads of a batch of KB K-tiles (16 KiB of FP4 weights for
+// one token tile) before it waits, and the register budget stays at 128 VGPRs
+// so four waves per SIMD overlap one another's loads.
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr uint32_t kInvalid = 0x80000000u;  // offset past every bounded region
+constexpr int kNonTemporal = 2;             // cache policy of loads streamed once (weights)
+
+// K-tiles per load batch: four FP4 (two FP8) weight K-tiles for one token
+// tile, fewer when several token tiles share the batch.
+template <int WFMT, int NTT>
+constexpr int batch_kt() {
+    return ((WFMT == MFMA_FMT_FP4 ? 4 : 2) / NTT) > 0 ? (WFMT == MFMA_FMT_FP4 ? 4 : 2) / NTT : 1;
+}
 
 struct KParams {
     const uint8_t* wbase[2];
     size_t gstride, dpg, dpu, spu;   // group stride; data bytes per group; per unit data / scales
-    int E_loc, K, kt, kt4;
+    int E_loc, G, K, kt, kt4;
     const int32_t* counts;
     const int32_t* offsets;
     const int32_t* offsets32;
     const float* row_w;
     const uint8_t* aq;
     const uint8_t* as;
-    const int32_t* row_src;       // null: grouped row r is activation row r
-    int N;                        // W1: 2I ; W2: H (y row length)
+    uint32_t aq_bytes, as_bytes;      // sizes of the activation arrays (bounds of the loads)
+    const int32_t* row_src;           // null: grouped row r is activation row r
+    int N;                            // W1: 2I ; W2: H (y row length)
     int ceil_rule, transpose, use_w;
     uint8_t* hq; uint8_t* hs; uint8_t* hTq; uint8_t* hTs; int ldT;
     uint16_t* y;
 };
 
-// Load a 16x128 weight tile operand for this lane (bpl bytes).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+MOE_DEV rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
 template <int WFMT>
-MOE_DEV i32x8 load_w(const uint8_t* p) {
+struct ATile {                        // one lane's part of a 16x128 weight tile
+    i32x4 lo, hi;                     // hi used for FP8 only
+};
+
+template <int WFMT>
+MOE_DEV i32x8 a_operand(const ATile<WFMT>& t) {
     i32x8 r;
-    const i32x4 a = *(const i32x4*)p;
-    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-    if (WFMT == MFMA_FMT_FP8) {
-        const i32x4 b = *(const i32x4*)(p + 16);
-        r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-    } else {
-        r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
-    }
+    r[0] = t.lo[0]; r[1] = t.lo[1]; r[2] = t.lo[2]; r[3] = t.lo[3];
+    if (WFMT == MFMA_FMT_FP8) { r[4] = t.hi[0]; r[5] = t.hi[1]; r[6] = t.hi[2]; r[7] = t.hi[3]; }
+    else { r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0; }
     return r;
 }
 
-// B operand: one grouped FP8 row's 128-wide K-tile in the MFMA FP8 order.
-MOE_DEV i32x8 load_x(const uint8_t* row_kt, int grp) {
-    const i32x4 a = *(const i32x4*)(row_kt + 16 * grp);
-    const i32x4 b = *(const i32x4*)(row_kt + 64 + 16 * grp);
-    i32x8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-    return r;
-}
+// Operands of one batch of K-tiles for one wave.
+template <int WFMT, int NTT>
+struct Batch {
+    static constexpr int KB = batch_kt<WFMT, NTT>();
+    ATile<WFMT> A[KB][4];             // [kt][tile]
+    int sA[KB][4];                    // E8M0 of (tile row, kt) in the low byte after the shift
+    i32x4 Blo[NTT][KB], Bhi[NTT][KB];
+    int sB[NTT][KB];
+};
 
-// One K-tile (index kt, scale byte SEL of the packed dword) for all active
-// token tiles. xrow[tt] is this lane's activation row for token tile tt, or
-// -1 past the end of the pass.
-template <int WFMT, int NTT, int SEL>
-MOE_DEV void k_step(const KParams& p, const uint8_t* wunit, const int (&sA)[4], int kt, int lane,
-                    const long (&xrow)[NTT], int ntt_active, f32x4 (&acc)[NTT][4]) {
-    if (kt >= p.kt) return;
+template <int WFMT, int NTT>
+MOE_DEV void load_batch(Batch<WFMT, NTT>& b, int kt_first, int kt_end, int lane,
+                        rsrc_t rw, rsrc_t rs, rsrc_t rx, rsrc_t rxs, const uint32_t (&xoff)[NTT],
+                        const uint32_t (&xsoff)[NTT]) {
+    constexpr int BPL = WFMT == MFMA_FMT_FP4 ? 16 : 32;
+    constexpr int KB = Batch<WFMT, NTT>::KB;
     const int grp = lane >> 4;
-    i32x8 A[4];
+    // weight scales: batches never straddle a group of four K-tiles, so one
+    // dword per tile covers the batch
+    int sword[4];
     #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        A[t] = load_w<WFMT>(wunit + ((size_t)(kt * 4 + t) * 64 + lane) * (WFMT == MFMA_FMT_FP4 ? 16 : 32));
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t soff = kt_first < kt_end ? (uint32_t)((((kt_first >> 2) * 4 + t) * 64 + lane) * 4)
+                                                : kInvalid;
+        sword[t] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, kNonTemporal);
+    }
     #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-        if (tt < ntt_active) {
-            i32x8 B;
-            int sB = 127;
-            if (xrow[tt] >= 0) {
-                const size_t row = (size_t)xrow[tt];
-                B = load_x(p.aq + row * p.K + (size_t)kt * 128, grp);
-                sB = p.as[row * (p.K / 32) + kt * 4 + grp];
-            } else {
-                B = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-            #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                acc[tt][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, SEL, 0>(A[t], B, acc[tt][t], sA[t], sB);
+    for (int i = 0; i < KB; ++i) {
+        const int kt = kt_first + i;
+        const bool ok = kt < kt_end;                       // uniform
+        #pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t off = ok ? (uint32_t)(((kt * 4 + t) * 64 + lane) * BPL) : kInvalid;
+            b.A[i][t].lo = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kNonTemporal);
+            if (WFMT == MFMA_FMT_FP8)
+                b.A[i][t].hi = __builtin_amdgcn_raw_buffer_load_b128(rw, off + (ok ? 16u : 0u), 0, kNonTemporal);
+            b.sA[i][t] = sword[t] >> (8 * (kt & 3));
+        }
+        #pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+            const bool v = ok && xoff[tt] != kInvalid;
+            const uint32_t o = v ? xoff[tt] + (uint32_t)(kt * 128 + 16 * grp) : kInvalid;
+            b.Blo[tt][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
+            b.Bhi[tt][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, v ? o + 64u : kInvalid, 0, 0);
+            const uint32_t so = v ? xsoff[tt] + (uint32_t)(kt * 4 + grp) : kInvalid;
+            b.sB[tt][i] = (int)__builtin_amdgcn_raw_buffer_load_b8(rxs, so, 0, 0);
         }
     }
 }
 
-template <int WFMT, bool IS_W1, int NTT>
-__global__ __launch_bounds__(kThreads)
+template <int WFMT, int NTT>
+MOE_DEV void mma_batch(const Batch<WFMT, NTT>& b, int ntt_active, f32x4 (&acc)[NTT][4]) {
+    constexpr int KB = Batch<WFMT, NTT>::KB;
+    #pragma unroll
+    for (int i = 0; i < KB; ++i) {
+        #pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+            if (tt < ntt_active) {
+                i32x8 B;
+                B[0] = b.Blo[tt][i][0]; B[1] = b.Blo[tt][i][1]; B[2] = b.Blo[tt][i][2]; B[3] = b.Blo[tt][i][3];
+                B[4] = b.Bhi[tt][i][0]; B[5] = b.Bhi[tt][i][1]; B[6] = b.Bhi[tt][i][2]; B[7] = b.Bhi[tt][i][3];
+                #pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    acc[tt][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, 0, 0>(a_operand<WFMT>(b.A[i][t]), B,
+                                                                        acc[tt][t], b.sA[i][t], b.sB[tt][i]);
+            }
+        }
+    }
+}
+
+// Wave 0: pass_off[g] = sum over g' < g of ceil(counts[g'] / rpp), and
+// pass_off[G] = the total, in LDS.
+MOE_DEV void pass_prefix(const int32_t* __restrict__ counts, int G, int rpp, int lane,
+                         int* pass_off) {
+    const int per = (G + 63) / 64;
+    const int lo = min(G, lane * per), hi = min(G, lo + per);
+    int s = 0;
+    for (int i = lo; i < hi; ++i) s += (counts[i] + rpp - 1) / rpp;
+    int inc = s;
+    #pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int a = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += a;
+    }
+    int run = inc - s;
+    for (int i = lo; i < hi; ++i) {
+        pass_off[i] = run;
+        run += (counts[i] + rpp - 1) / rpp;
+    }
+    if (lane == 63) pass_off[G] = inc;
+}
+
+// Persistent grid: each workgroup walks the work items item = pass * units + u
+// (every pass of 16*NTT rows of every group, times the 64-row weight units),
+// striding by the grid size; empty groups contribute no items.
+template <int WFMT, bool IS_W1, int NTT, int KW>
+__global__ __launch_bounds__(64 * KW)
 void grouped_gemm_kernel(KParams p) {
-    const int u = blockIdx.x, g = blockIdx.y;
-    const int n_g = p.counts[g];
+    constexpr int NT = 64 * KW;
     const int rows_per_pass = 16 * NTT;
-    const int npass = (n_g + rows_per_pass - 1) / rows_per_pass;
-    if ((int)blockIdx.z >= npass) return;
+    const int G = p.G, units = p.N / 64;
 
     extern __shared__ float lds[];
-    float* red = lds;                                   // [2][NTT][4 tiles][4][64 lanes]
-    float* hbuf = lds + 2 * NTT * 1024;                 // [16*NTT][33]  (W1)
+    int* pass_off = (int*)lds;                          // [G + 1]
+    float* red = lds + ((G + 4) & ~3);                  // [KW/2][NTT][4 tiles][4][64 lanes]
+    float* hbuf = red + (KW / 2) * NTT * 1024;          // [16*NTT][33]  (W1)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int sel = g < p.E_loc ? 0 : 1;
-    const int gi = g < p.E_loc ? g : 0;
-    const uint8_t* wgrp = p.wbase[sel] + gi * p.gstride;
-    const uint8_t* wunit = wgrp + u * p.dpu;
-    const uint8_t* sunit = wgrp + p.dpg + u * p.spu;
-    const int row0 = p.offsets[g];
-    const int kg0 = (w * p.kt4) / kWaves, kg1 = ((w + 1) * p.kt4) / kWaves;
+    if (w == 0) pass_prefix(p.counts, G, rows_per_pass, lane, pass_off);
+    __syncthreads();
+    const int n_items = pass_off[G] * units;
 
-    for (int pass = blockIdx.z; pass < npass; pass += gridDim.z) {
-        const int rbase = row0 + pass * rows_per_pass;
+    const rsrc_t rx = make_rsrc(p.aq, p.aq_bytes);
+    const rsrc_t rxs = make_rsrc(p.as, p.as_bytes);
+    // this wave's contiguous run of K-tiles, in whole batches (batches of KB
+    // K-tiles start at multiples of KB, and KB divides 4)
+    constexpr int KB = Batch<WFMT, NTT>::KB;
+    const int nbt = (p.kt + KB - 1) / KB;
+    const int kt0 = ((w * nbt) / KW) * KB, kt1 = min(p.kt, (((w + 1) * nbt) / KW) * KB);
+
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int pg = item / units, u = item - pg * units;
+        int glo = 0, ghi = G;                           // largest g with pass_off[g] <= pg
+        while (ghi - glo > 1) {
+            const int mid = (glo + ghi) >> 1;
+            if (pass_off[mid] <= pg) glo = mid; else ghi = mid;
+        }
+        const int g = glo, pass = pg - pass_off[g];
+        const int n_g = p.counts[g];
+        const int sel = g < p.E_loc ? 0 : 1;
+        const int gi = g < p.E_loc ? g : 0;
+        const uint8_t* wgrp = p.wbase[sel] + gi * p.gstride;
+        const rsrc_t rw = make_rsrc(wgrp + u * p.dpu, (uint32_t)p.dpu);
+        const rsrc_t rs = make_rsrc(wgrp + p.dpg + u * p.spu, (uint32_t)p.spu);
+        const int rbase = p.offsets[g] + pass * rows_per_pass;
         const int nrows = min(rows_per_pass, n_g - pass * rows_per_pass);
         const int ntt_active = (nrows + 15) / 16;
 
         f32x4 acc[NTT][4];
-        long xrow[NTT];
+        uint32_t xoff[NTT], xsoff[NTT];
         #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
             #pragma unroll
             for (int t = 0; t < 4; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int r = tt * 16 + (lane & 15);
-            xrow[tt] = r < nrows ? (p.row_src ? (long)p.row_src[rbase + r] : (long)(rbase + r)) : -1;
+            const long xr = r < nrows ? (p.row_src ? (long)p.row_src[rbase + r] : (long)(rbase + r)) : -1;
+            xoff[tt] = xr >= 0 ? (uint32_t)(xr * p.K) : kInvalid;
+            xsoff[tt] = xr >= 0 ? (uint32_t)(xr * (p.K / 32)) : kInvalid;
         }
 
-        for (int kg = kg0; kg < kg1; ++kg) {
-            int sA[4];
-            #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                sA[t] = *(const int*)(sunit + ((size_t)(kg * 4 + t) * 64 + lane) * 4);
-            k_step<WFMT, NTT, 0>(p, wunit, sA, kg * 4 + 0, lane, xrow, ntt_active, acc);
-            k_step<WFMT, NTT, 1>(p, wunit, sA, kg * 4 + 1, lane, xrow, ntt_active, acc);
-            k_step<WFMT, NTT, 2>(p, wunit, sA, kg * 4 + 2, lane, xrow, ntt_active, acc);
-            k_step<WFMT, NTT, 3>(p, wunit, sA, kg * 4 + 3, lane, xrow, ntt_active, acc);
+        for (int ktb = kt0; ktb < kt1; ktb += KB) {
+            Batch<WFMT, NTT> b;
+            load_batch<WFMT, NTT>(b, ktb, kt1, lane, rw, rs, rx, rxs, xoff, xsoff);
+            mma_batch<WFMT, NTT>(b, ntt_active, acc);
         }
 
-        // Sum the four waves' partials in a fixed order, ((w0 + w2) + (w1 + w3)),
-        // through two LDS slots; the total ends up in slot 0.
-        auto store_acc = [&](int slot) {
+        // Sum the KW waves' partials in a fixed tree order through KW/2 LDS
+        // slots: in the round of half-width h, waves [h, 2h) store, waves
+        // [0, h) add; the total ends up in wave 0 and is stored to slot 0.
+        auto slot = [&](int s_, int tt, int t, int v) -> float& {
+            return red[(((s_ * NTT + tt) * 4 + t) * 4 + v) * 64 + lane];
+        };
+        #pragma unroll
+        for (int h = KW / 2; h >= 1; h >>= 1) {
+            if (w >= h && w < 2 * h) {
+                #pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+                    #pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        #pragma unroll
+                        for (int v = 0; v < 4; ++v) slot(w - h, tt, t, v) = acc[tt][t][v];
+            }
+            __syncthreads();
+            if (w < h) {
+                #pragma unroll
+                for (int tt = 0; tt < NTT; ++tt)
+                    #pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        #pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[tt][t][v] += slot(w, tt, t, v);
+            }
+            __syncthreads();
+        }
+        if (w == 0) {
             #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
                 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                     #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        red[(((slot * NTT + tt) * 4 + t) * 4 + v) * 64 + lane] = acc[tt][t][v];
-        };
-        auto add_acc = [&](int slot) {
-            #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt)
-                #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        acc[tt][t][v] += red[(((slot * NTT + tt) * 4 + t) * 4 + v) * 64 + lane];
-        };
-        if (w >= 2) store_acc(w - 2);
-        __syncthreads();
-        if (w < 2) add_acc(w);
-        __syncthreads();
-        if (w == 1) store_acc(0);
-        __syncthreads();
-        if (w == 0) { add_acc(0); store_acc(0); }
+                    for (int v = 0; v < 4; ++v) slot(0, tt, t, v) = acc[tt][t][v];
+        }
         __syncthreads();
 
         if (IS_W1) {
             const int I = p.N / 2;
             // gate/up pairs -> h (fp32) in LDS, [token][feature of this unit]
-            for (int e = tid; e < NTT * 512; e += kThreads) {
+            for (int e = tid; e < NTT * 512; e += NT) {
                 const int le = e & 63, v = (e >> 6) & 3, gt = (e >> 8) & 1, tt = e >> 9;
                 const int tok = tt * 16 + (le & 15);
                 if (tok >= nrows) continue;
@@ -185,7 +281,7 @@ void grouped_gemm_kernel(KParams p) {
             }
             __syncthreads();
             // row-wise MX-E4M3 quantisation: 32 threads per token (one 32-block)
-            for (int t0 = 0; t0 < rows_per_pass; t0 += kThreads / 32) {
+            for (int t0 = 0; t0 < rows_per_pass; t0 += NT / 32) {
                 const int tok = t0 + (tid >> 5), f = tid & 31;
                 const bool valid = tok < nrows;
                 const float h = valid ? hbuf[tok * 33 + f] : 0.f;
@@ -207,7 +303,7 @@ void grouped_gemm_kernel(KParams p) {
                 // columns of this pass: [offsets32[g] + pass*rows_per_pass, ...) ; blocks of 32 tokens
                 const int ncols = (nrows + 31) & ~31;
                 const int col0 = p.offsets32[g] + pass * rows_per_pass;
-                for (int it = 0; it < 32 * (rows_per_pass / 32); it += kThreads / 32) {
+                for (int it = 0; it < 32 * (rows_per_pass / 32); it += NT / 32) {
                     const int pr = it + (tid >> 5);
                     const int f = pr & 31, tb = pr >> 5;
                     const int tok = tb * 32 + (tid & 31);
@@ -217,7 +313,7 @@ void grouped_gemm_kernel(KParams p) {
                     for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
                     const uint32_t code = e4m3_scale_code(amax, p.ceil_rule);
                     const uint32_t qb = tok < nrows ? f32_to_e4m3(h * inv_scale(code)) : 0u;
-                    if (tb * 32 < ncols) {
+                    if (pr < 32 * (rows_per_pass / 32) && tb * 32 < ncols) {
                         const size_t frow = (size_t)(32 * u + f);
                         p.hTq[frow * p.ldT + col0 + tok] = (uint8_t)qb;
                         if ((tid & 31) == 0) p.hTs[frow * (p.ldT / 32) + (col0 >> 5) + tb] = (uint8_t)code;
@@ -226,7 +322,7 @@ void grouped_gemm_kernel(KParams p) {
             }
         } else {
             const int H = p.N;
-            for (int e = tid; e < NTT * 256; e += kThreads) {
+            for (int e = tid; e < NTT * 256; e += NT) {
                 const int le = e & 63, t = (e >> 6) & 3, tt = e >> 8;
                 const int tok = tt * 16 + (le & 15);
                 if (tok >= nrows) continue;
@@ -249,9 +345,11 @@ KParams make_params(const GemmArgs& a, bool w1) {
     for (int i = 0; i < 2; ++i) p.wbase[i] = a.w_base[i];
     p.gstride = geo.group_stride; p.dpg = geo.data_per_group;
     p.dpu = geo.data_per_unit;    p.spu = geo.scale_per_unit;
-    p.E_loc = a.E_loc; p.K = a.K; p.kt = geo.kt; p.kt4 = geo.kt4;
+    p.E_loc = a.E_loc; p.G = a.G; p.K = a.K; p.kt = geo.kt; p.kt4 = geo.kt4;
     p.counts = a.counts; p.offsets = a.offsets; p.offsets32 = a.offsets32;
     p.row_w = a.row_w; p.aq = a.aq; p.as = a.as; p.row_src = a.row_src; p.N = a.N;
+    p.aq_bytes = (uint32_t)((size_t)a.x_rows * a.K);
+    p.as_bytes = (uint32_t)((size_t)a.x_rows * (a.K / 32));
     p.ceil_rule = (a.flags & MOE_SCALE_RULE_CEIL) ? 1 : 0;
     p.transpose = (w1 && (a.flags & MOE_W1_WRITE_TRANSPOSE)) ? 1 : 0;
     p.use_w = (w1 && a.row_w && !(a.flags & MOE_WEIGHT_AT_COMBINE)) ? 1 : 0;
@@ -260,36 +358,64 @@ KParams make_params(const GemmArgs& a, bool w1) {
     return p;
 }
 
-// Token tiles per pass, from the expected rows per group (T*k spread over the groups).
-int pick_ntt(const GemmArgs& a, bool transpose) {
-    const int avg = a.rows_hint > 0 ? a.rows_hint : a.R_max / (a.G > 0 ? a.G : 1);
-    int ntt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
-    if (transpose && ntt < 2) ntt = 2;       // 32-token blocks must not straddle passes
-    return ntt;
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int WFMT, bool IS_W1, int NTT, int KW>
+int launch(const KParams& p, long max_items, hipStream_t stream) {
+    auto kern = grouped_gemm_kernel<WFMT, IS_W1, NTT, KW>;
+    const size_t lds = (size_t)((p.G + 4) & ~3) * 4 + (size_t)(KW / 2) * NTT * 1024 * 4 +
+                       (IS_W1 ? (size_t)16 * NTT * 33 * 4 : 0);
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * KW, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const long grid = std::max<long>(1, std::min<long>(max_items, (long)per_cu * device_cu_count()));
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * KW), lds, stream, p);
+    return (int)hipGetLastError();
 }
 
 template <int WFMT, bool IS_W1, int NTT>
-int launch(const KParams& p, int units, int G, int passes, hipStream_t stream) {
-    size_t lds = (size_t)2 * NTT * 1024 * 4 + (IS_W1 ? (size_t)16 * NTT * 33 * 4 : 0);
-    dim3 grid(units, G, passes);
-    hipLaunchKernelGGL((grouped_gemm_kernel<WFMT, IS_W1, NTT>), grid, dim3(kThreads), lds, stream, p);
-    return (int)hipGetLastError();
+int launch_kw(const KParams& p, int kw, long max_items, hipStream_t stream) {
+    if (kw >= 16) return launch<WFMT, IS_W1, NTT, 16>(p, max_items, stream);
+    if (kw >= 8) return launch<WFMT, IS_W1, NTT, 8>(p, max_items, stream);
+    return launch<WFMT, IS_W1, NTT, 4>(p, max_items, stream);
 }
 
 template <bool IS_W1>
 int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     if (a.G == 0 || a.R_max == 0) return 0;
     KParams p = make_params(a, IS_W1);
-    const int ntt = pick_ntt(a, p.transpose);
-    const int units = a.N / 64;
+    // token tiles per pass, from the expected rows per group
     const int avg = a.rows_hint > 0 ? a.rows_hint : a.R_max / a.G;
-    int passes = 2 * ((avg + 16 * ntt - 1) / (16 * ntt));
-    passes = passes < 1 ? 1 : (passes > 16 ? 16 : passes);
+    int ntt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
+    if (p.transpose && ntt < 2) ntt = 2;       // 32-token blocks must not straddle passes
+    const int units = a.N / 64;
+    const int rpp = 16 * ntt;
+    // items never exceed units * (R_max / rpp + G): each group adds at most one partial pass
+    const long max_items = (long)units * ((long)a.R_max / rpp + a.G);
+    // K-split waves per workgroup: at least ~2048 waves busy (two per SIMD)
+    // when few groups are active
+    const long active = a.active_hint > 0 ? a.active_hint
+                        : std::min<long>(a.G, std::max<long>(1, a.R_max / std::max(avg, 1)));
+    const long items = active * units * std::max(1, (avg + rpp - 1) / rpp);
+    int kw = items * 4 >= 2048 ? 4 : (items * 8 >= 2048 ? 8 : 16);
+    kw = std::min(kw, std::max(4, p.kt));       // no more waves than K-tiles
+    if (ntt > 1) kw = std::min(kw, 8);          // 1024-thread workgroups get 128 VGPRs: too few
     const bool fp4 = a.fmt == MOE_FMT_MXFP4;
-#define MOE_GEMM_CASE(N)                                                                      \
-    if (ntt == N)                                                                             \
-        return fp4 ? launch<MFMA_FMT_FP4, IS_W1, N>(p, units, a.G, passes, stream)            \
-                   : launch<MFMA_FMT_FP8, IS_W1, N>(p, units, a.G, passes, stream);
+#define MOE_GEMM_CASE(N)                                                                          \
+    if (ntt == N)                                                                                 \
+        return fp4 ? launch_kw<MFMA_FMT_FP4, IS_W1, N>(p, kw, max_items, stream)                  \
+                   : launch_kw<MFMA_FMT_FP8, IS_W1, N>(p, kw, max_items, stream);
     MOE_GEMM_CASE(1)
     MOE_GEMM_CASE(2)
     MOE_GEMM_CASE(4)

@@ -3,6 +3,7 @@
 // be checked on a machine without a GPU; nothing here allocates device memory,
 // synchronises or reads device data.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <string.h>
 
 #include "moe_internal.h"
@@ -189,10 +190,10 @@ static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shar
                                const int32_t* counts, const int32_t* offsets,
                                const int32_t* offsets32, const float* row_w,
                                const uint8_t* xq_perm, const uint8_t* xs_perm,
-                               const int32_t* row_src, int32_t R_max,
+                               const int32_t* row_src, int32_t x_rows, int32_t R_max,
                                int32_t H, int32_t I, int32_t G, uint32_t flags, uint8_t* hq,
                                uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes,
-                               int rows_hint, hipStream_t stream) {
+                               int rows_hint, hipStream_t stream, int active_hint = 0) {
     int32_t st = check_hi(H, I);
     if (st) return st;
     if (R_max < 0 || G < 1 || G > MOE_MAX_EXPERTS + 1) return MOE_ERR_SHAPE;
@@ -200,14 +201,16 @@ static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shar
     st = fill_gemm_args(a, w1, w1_shared, G, 2 * I, H, 1);
     if (st) return st;
     if (!counts || !offsets || !xq_perm || !xs_perm || !hq || !hs) return MOE_ERR_NULL;
+    if (x_rows < 1 || (int64_t)x_rows * H >= (1ll << 31)) return MOE_ERR_SHAPE;
+    if (!row_src && x_rows < R_max) return MOE_ERR_SHAPE;
     const bool transpose = (flags & MOE_W1_WRITE_TRANSPOSE) != 0;
     if (transpose && (!hTq || !hTs || !offsets32)) return MOE_ERR_NULL;
     if (!(flags & MOE_WEIGHT_AT_COMBINE) && !row_w) return MOE_ERR_NULL;
     const size_t need = moe_grouped_workspace_size(R_max, G, 2 * I, H);
     if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
     a.counts = counts; a.offsets = offsets; a.offsets32 = offsets32; a.row_w = row_w;
-    a.aq = xq_perm; a.as = xs_perm; a.row_src = row_src;
-    a.R_max = R_max; a.rows_hint = rows_hint; a.flags = flags;
+    a.aq = xq_perm; a.as = xs_perm; a.row_src = row_src; a.x_rows = x_rows;
+    a.R_max = R_max; a.rows_hint = rows_hint; a.active_hint = active_hint; a.flags = flags;
     a.hq = hq; a.hs = hs; a.hTq = hTq; a.hTs = hTs; a.ldT = moe_transposed_ld(R_max, G);
     return hip_status(moe_launch_grouped_w1(a, stream));
 }
@@ -216,20 +219,21 @@ MOE_EXPORT int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_s
                                   const int32_t* counts, const int32_t* offsets,
                                   const int32_t* offsets32, const float* row_w,
                                   const uint8_t* xq, const uint8_t* xs, const int32_t* row_src,
-                                  int32_t R_max, int32_t H, int32_t I, int32_t G,
-                                  int32_t rows_hint, uint32_t flags, uint8_t* hq, uint8_t* hs,
-                                  uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
-    if (rows_hint < 0) return MOE_ERR_SHAPE;
+                                  int32_t x_rows, int32_t R_max, int32_t H, int32_t I, int32_t G,
+                                  int32_t rows_hint, int32_t active_hint, uint32_t flags,
+                                  uint8_t* hq, uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    if (rows_hint < 0 || active_hint < 0) return MOE_ERR_SHAPE;
     return grouped_w1_impl(w1, w1_shared, counts, offsets, offsets32, row_w, xq, xs, row_src,
-                           R_max, H, I, G, flags, hq, hs, hTq, hTs, ws, ws_bytes, rows_hint, stream);
+                           x_rows, R_max, H, I, G, flags, hq, hs, hTq, hTs, ws, ws_bytes, rows_hint,
+                           stream, active_hint);
 }
 
 static int32_t grouped_w2_impl(const moe_weights* w2, const moe_weights* w2_shared,
                                const int32_t* counts, const int32_t* offsets, const uint8_t* hq,
                                const uint8_t* hs, int32_t R_max, int32_t H, int32_t I, int32_t G,
                                uint16_t* y, void* ws, size_t ws_bytes, int rows_hint,
-                               hipStream_t stream) {
+                               hipStream_t stream, int active_hint = 0) {
     int32_t st = check_hi(H, I);
     if (st) return st;
     if (R_max < 0 || G < 1 || G > MOE_MAX_EXPERTS + 1) return MOE_ERR_SHAPE;
@@ -237,21 +241,28 @@ static int32_t grouped_w2_impl(const moe_weights* w2, const moe_weights* w2_shar
     st = fill_gemm_args(a, w2, w2_shared, G, H, I, 0);
     if (st) return st;
     if (!counts || !offsets || !hq || !hs || !y) return MOE_ERR_NULL;
+    if ((int64_t)R_max * I >= (1ll << 31)) return MOE_ERR_SHAPE;
     const size_t need = moe_grouped_workspace_size(R_max, G, H, I);
     if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
-    a.counts = counts; a.offsets = offsets; a.aq = hq; a.as = hs; a.R_max = R_max;
-    a.rows_hint = rows_hint; a.y = y;
+    a.counts = counts; a.offsets = offsets; a.aq = hq; a.as = hs; a.x_rows = R_max; a.R_max = R_max;
+    a.rows_hint = rows_hint; a.active_hint = active_hint; a.y = y;
     return hip_status(moe_launch_grouped_w2(a, stream));
 }
 
 MOE_EXPORT int32_t moe_grouped_w2(const moe_weights* w2, const moe_weights* w2_shared,
                                   const int32_t* counts, const int32_t* offsets, const uint8_t* hq,
                                   const uint8_t* hs, int32_t R_max, int32_t H, int32_t I,
-                                  int32_t G, int32_t rows_hint, uint16_t* y, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
-    if (rows_hint < 0) return MOE_ERR_SHAPE;
+                                  int32_t G, int32_t rows_hint, int32_t active_hint, uint16_t* y,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (rows_hint < 0 || active_hint < 0) return MOE_ERR_SHAPE;
     return grouped_w2_impl(w2, w2_shared, counts, offsets, hq, hs, R_max, H, I, G, y, ws, ws_bytes,
-                           rows_hint, stream);
+                           rows_hint, stream, active_hint);
+}
+
+MOE_EXPORT int32_t moe_layer_active_hint(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
+                                         int32_t s) {
+    if (T <= 0 || E_tot <= 0 || k <= 0 || E_loc <= 0) return 0;
+    return (int32_t)ceil(E_loc * (1.0 - pow(1.0 - (double)k / E_tot, (double)T))) + (s ? 1 : 0);
 }
 
 MOE_EXPORT int32_t moe_layer_rows_hint(int32_t T, int32_t E_tot, int32_t k) {
@@ -349,12 +360,14 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     // expected rows of a routed group under uniform routing; the shared group
     // (T rows) gets more passes from the grid's pass dimension
     const int hint = moe_layer_rows_hint(T, E_tot, k);
+    // expected local experts with at least one token: E_loc (1 - (1 - k/E_tot)^T), plus the shared one
+    const int active = moe_layer_active_hint(T, E_tot, k, E_loc, s);
     st = grouped_w1_impl(a->w1, a->shared_w1, counts, offsets, offsets32, row_w, a->xq, a->xs,
-                         row_src, R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch,
-                         scratch_bytes, hint, stream);
+                         row_src, T, R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch,
+                         scratch_bytes, hint, stream, active);
     if (st) return st;
     st = grouped_w2_impl(a->w2, a->shared_w2, counts, offsets, hq, hs, R_max, H, I, G, y, scratch,
-                         scratch_bytes, hint, stream);
+                         scratch_bytes, hint, stream, active);
     if (st) return st;
     const bool wc = (a->flags & MOE_WEIGHT_AT_COMBINE) != 0;
     e = moe_launch_combine(y, slot_row, wc ? row_w : nullptr, T, k + s, H, a->out, stream);

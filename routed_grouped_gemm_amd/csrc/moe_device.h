@@ -154,57 +154,103 @@ MOE_DEV float wave_sum(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane
+// of the row receives the row's result.
+MOE_DEV float row16_max(float v) {
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_XOR1, 0xF));
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_XOR2, 0xF));
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_HALF_MIRROR, 0xF));
+    v = fmaxf(v, MOE_DPP(v, MOE_DPP_MIRROR, 0xF));
+    return v;
+}
+
+MOE_DEV float row16_sum(float v) {
+    v += MOE_DPP(v, MOE_DPP_XOR1, 0xF);
+    v += MOE_DPP(v, MOE_DPP_XOR2, 0xF);
+    v += MOE_DPP(v, MOE_DPP_HALF_MIRROR, 0xF);
+    v += MOE_DPP(v, MOE_DPP_MIRROR, 0xF);
+    return v;
+}
+
 // ---------------------------------------------------------------------------
-// Top-k softmax routing of one token by one wave (logits row of E <= 64*VPL
-// floats). Lane l holds experts [l*VPL, l*VPL + VPL): a lower lane holds lower
-// expert ids, so among lanes whose best remaining logit equals the wave
-// maximum, the lowest lane holds the lowest id, which resolves ties to the
-// lower expert id. Selection compares fp32 logits; the weight of a selected
-// expert is exp(l - max) / sum_e exp(l_e - max) in fp32. On return lane j < k
-// holds the j-th selection in (sel_e, sel_w); other lanes are unchanged.
+// Top-k softmax routing with LPT lanes per token (LPT = 64: one token per
+// wave; LPT = 16: one token per DPP row, four tokens per wave). Lane i of a
+// token's lane group holds experts [i*VPL, i*VPL + VPL), so among lanes whose
+// best remaining logit equals the group maximum, the lowest lane holds the
+// lowest expert id: ties resolve to the lower id. Selection compares fp32
+// logits; the weight of a selected expert is exp(l - max) / sum_e exp(l_e -
+// max) in fp32. On return, lane j < k of the group holds the token's j-th
+// selection in (sel_e, sel_w). E <= LPT*VPL, k <= LPT.
 // ---------------------------------------------------------------------------
-template <int VPL>
-MOE_DEV void wave_route_values(const float (&v)[VPL], int E, int k, bool renorm, int lane,
-                               int& sel_e, float& sel_w) {
-    const int base = lane * VPL;
+template <int LPT>
+MOE_DEV float group_max(float v) { return LPT == 64 ? wave_max(v) : row16_max(v); }
+template <int LPT>
+MOE_DEV float group_sum(float v) { return LPT == 64 ? wave_sum(v) : row16_sum(v); }
+
+template <int LPT, int VPL>
+MOE_DEV void route_values(const float (&v)[VPL], int E, int k, bool renorm, int lane,
+                          int& sel_e, float& sel_w) {
+    const int li = lane & (LPT - 1);
+    const int base = li * VPL;
     float lm = -INFINITY;
     #pragma unroll
     for (int i = 0; i < VPL; ++i) lm = (base + i < E) ? fmaxf(lm, v[i]) : lm;
-    const float m = wave_max(lm);
+    const float m = group_max<LPT>(lm);
     float ls = 0.f;
     #pragma unroll
-    for (int i = 0; i < VPL; ++i) ls += (base + i < E) ? expf(v[i] - m) : 0.f;
-    const float inv = 1.0f / wave_sum(ls);
+    for (int i = 0; i < VPL; ++i) ls += (base + i < E) ? __expf(v[i] - m) : 0.f;
+    const float inv = 1.0f / group_sum<LPT>(ls);
 
-    uint32_t taken = 0;
+    // Candidate values with taken / out-of-range entries at -inf (logits are
+    // finite, so -inf means "nothing left").
+    float c[VPL];
+    #pragma unroll
+    for (int i = 0; i < VPL; ++i) c[i] = (base + i < E) ? v[i] : -INFINITY;
+    const int gshift = LPT == 64 ? 0 : (lane & 48);
     float wsum = 0.f, my_w = 0.f;
     int my_e = -1;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = -1;
+        // lane-local best, branch-free; a strict compare in ascending order
+        // keeps the lower index on ties
+        float bv = c[0];
+        int bi = 0;
         #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const bool ok = (base + i < E) && !((taken >> i) & 1u);
-            if (ok && (bi < 0 || v[i] > bv)) { bv = v[i]; bi = i; }
+        for (int i = 1; i < VPL; ++i) {
+            const bool better = c[i] > bv;
+            bv = better ? c[i] : bv;
+            bi = better ? i : bi;
         }
-        const float mx = wave_max(bi >= 0 ? bv : -INFINITY);
-        const uint64_t hit = __ballot(bi >= 0 && bv == mx);
-        const int win = __ffsll((unsigned long long)hit) - 1;
-        const int e = __builtin_amdgcn_readlane(base + bi, win);
-        if (lane == win) taken |= 1u << bi;
-        const float w = expf(mx - m) * inv;
+        const float mx = group_max<LPT>(bv);
+        const uint64_t hit = __ballot(bv == mx && bv != -INFINITY);
+        const uint64_t ghit = LPT == 64 ? hit : ((hit >> gshift) & 0xFFFFull);
+        const int win = gshift + (ghit ? __ffsll((unsigned long long)ghit) - 1 : 0);
+        const int e = LPT == 64 ? __builtin_amdgcn_readlane(base + bi, win)
+                                : __shfl(base + bi, win, 64);
+        const bool pop = ghit && lane == win;
+        #pragma unroll
+        for (int i = 0; i < VPL; ++i) c[i] = (pop && i == bi) ? -INFINITY : c[i];
+        const float w = __expf(mx - m) * inv;
         wsum += w;
-        if (lane == j) { my_e = e; my_w = w; }
+        if (li == j) { my_e = e; my_w = w; }
     }
-    if (lane < k) {
+    if (li < k) {
         sel_e = my_e;
         sel_w = renorm ? my_w / wsum : my_w;
     }
 }
 
-template <int VPL>
+// This lane's VPL logits of a token row (E floats); -inf past E.
+template <int LPT, int VPL>
 MOE_DEV void load_logits(const float* __restrict__ row, int E, int lane, float (&v)[VPL]) {
-    const int base = lane * VPL;
-    #pragma unroll
-    for (int i = 0; i < VPL; ++i) v[i] = (base + i < E) ? row[base + i] : -INFINITY;
+    const int base = (lane & (LPT - 1)) * VPL;
+    if (VPL % 4 == 0 && base + VPL <= E && (E % 4) == 0) {      // whole run in bounds: 16-byte loads
+        #pragma unroll
+        for (int i = 0; i < VPL; i += 4) {
+            const float4 f = *(const float4*)(row + base + i);
+            v[i] = f.x; v[i + 1] = f.y; v[i + 2] = f.z; v[i + 3] = f.w;
+        }
+    } else {
+        #pragma unroll
+        for (int i = 0; i < VPL; ++i) v[i] = (base + i < E) ? row[base + i] : -INFINITY;
+    }
 }

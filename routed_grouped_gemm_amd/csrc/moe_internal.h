@@ -47,8 +47,10 @@ struct GemmArgs {
     const uint8_t* aq;           // activations [R_max, K] E4M3 (or [T, K] with row_src)
     const uint8_t* as;           // [R_max, K/32]               (or [T, K/32])
     const int32_t* row_src;      // null, or: grouped row r reads activation row row_src[r]
+    int x_rows;                  // rows of aq / as
     int R_max;
     int rows_hint;               // expected rows per group (0: R_max / G)
+    int active_hint;             // expected groups with rows (0: derived from rows_hint)
     uint32_t flags;
     uint8_t* hq; uint8_t* hs;    // W1 outputs
     uint8_t* hTq; uint8_t* hTs; int ldT;

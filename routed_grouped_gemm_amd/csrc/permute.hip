@@ -20,55 +20,48 @@ namespace {
 constexpr int kChunkThreads = 512;      // chunked path: one chunk = 512 assignments
 constexpr int kSmallMax = 4096;         // single-workgroup path up to this many assignments
 constexpr int kFusedThreads = 1024;     // route + permute in one workgroup
-constexpr int kFusedTPW = 4;            // tokens per wave in the fused kernel
-constexpr int kFusedMaxT = kFusedThreads / 64 * kFusedTPW;
+constexpr int kFusedMaxT = kFusedThreads / 64 * 4;   // four tokens per wave
 constexpr int kFusedMaxG = 513;
 
 MOE_DEV uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
 
-// Block-wide exclusive scan of n values in LDS (in place), n <= 4 * blockDim.
-// part: LDS scratch of blockDim ints. Returns the total to every thread.
-MOE_DEV int block_exclusive_scan(int* vals, int n, int* part) {
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int per = (n + nt - 1) / nt;
-    const int lo = tid * per, hi = min(n, lo + per);
-    int s = 0;
-    for (int i = lo; i < hi; ++i) s += vals[i];
-    part[tid] = s;
-    __syncthreads();
-    for (int off = 1; off < nt; off <<= 1) {
-        int add = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += add;
-        __syncthreads();
-    }
-    int run = part[tid] - s;            // exclusive prefix of this thread's segment
-    int total = part[nt - 1];
-    for (int i = lo; i < hi; ++i) { int v = vals[i]; vals[i] = run; run += v; }
-    __syncthreads();
-    return total;
-}
-
 // counts (LDS, G entries) -> counts/offsets/offsets32 in global memory; the
-// LDS array holds the offsets afterwards.
-MOE_DEV void write_offsets(int* lds_counts, int* lds_tmp, int G, int* part,
-                           int32_t* counts, int32_t* offsets, int32_t* offsets32) {
-    const int tid = threadIdx.x, nt = blockDim.x;
-    for (int g = tid; g < G; g += nt) {
-        counts[g] = lds_counts[g];
-        lds_tmp[g] = (lds_counts[g] + 31) & ~31;
-    }
+// LDS array holds the offsets afterwards. Wave 0 scans: each lane takes a run
+// of ceil(G/64) consecutive groups, the lanes' run totals are scanned with
+// shuffles, then each lane writes its run.
+MOE_DEV void write_offsets(int* lds_counts, int G, int32_t* counts, int32_t* offsets,
+                           int32_t* offsets32) {
     __syncthreads();
-    int total = block_exclusive_scan(lds_counts, G, part);
-    int total32 = 0;
-    if (offsets32) total32 = block_exclusive_scan(lds_tmp, G, part);
-    for (int g = tid; g < G; g += nt) {
-        offsets[g] = lds_counts[g];
-        if (offsets32) offsets32[g] = lds_tmp[g];
-    }
-    if (tid == 0) {
-        offsets[G] = total;
-        if (offsets32) offsets32[G] = total32;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int per = (G + 63) / 64;
+        const int lo = min(G, lane * per), hi = min(G, lo + per);
+        int s = 0, s32 = 0;
+        for (int i = lo; i < hi; ++i) {
+            const int c = lds_counts[i];
+            s += c;
+            s32 += (c + 31) & ~31;
+        }
+        int inc = s, inc32 = s32;                  // inclusive scan over lanes
+        #pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int a = __shfl_up(inc, d, 64), b = __shfl_up(inc32, d, 64);
+            if (lane >= d) { inc += a; inc32 += b; }
+        }
+        int run = inc - s, run32 = inc32 - s32;
+        for (int i = lo; i < hi; ++i) {
+            const int c = lds_counts[i];
+            counts[i] = c;
+            offsets[i] = run;
+            if (offsets32) offsets32[i] = run32;
+            lds_counts[i] = run;
+            run += c;
+            run32 += (c + 31) & ~31;
+        }
+        if (lane == 63) {
+            offsets[G] = inc;
+            if (offsets32) offsets32[G] = inc32;
+        }
     }
     __syncthreads();
 }
@@ -129,7 +122,7 @@ MOE_DEV void write_shared_rows(int t0, int t1, int T, int k, int ks, int base,
 
 // LDS ints needed by permute_in_block.
 constexpr size_t block_lds_ints(int NW, int G, int E_loc) {
-    return (size_t)3 * G + (size_t)NW * 64 + ((size_t)NW * E_loc * 2 + 3) / 4;
+    return (size_t)3 * G + ((size_t)NW * E_loc * 2 + 3) / 4;
 }
 
 // The whole S2/S3 computation of up to 4096 assignments in one workgroup of
@@ -141,10 +134,9 @@ MOE_DEV void permute_in_block(IdxF idx_of, WF w_of, int T, int k, int e0, int E_
     constexpr int NT = NW * 64;
     const int G = E_loc + s;
     int* hist = lds;                       // [G]   counts, then offsets
-    int* tmp = hist + G;                   // [G]   roundup counts / chunk totals
+    int* tmp = hist + G;                   // [G]   chunk totals
     int* base = tmp + G;                   // [G]   running row of each group
-    int* part = base + G;                  // [NT]
-    uint16_t* cnt = (uint16_t*)(part + NT);    // [NW][E_loc]
+    uint16_t* cnt = (uint16_t*)(base + G);     // [NW][E_loc]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int Tk = T * k, ks = k + s;
 
@@ -157,7 +149,7 @@ MOE_DEV void permute_in_block(IdxF idx_of, WF w_of, int T, int k, int e0, int E_
     __syncthreads();
     if (s && tid == 0) hist[E_loc] = T;
     __syncthreads();
-    write_offsets(hist, tmp, G, part, counts, offsets, offsets32);
+    write_offsets(hist, G, counts, offsets, offsets32);
     for (int g = tid; g < G; g += NT) base[g] = hist[g];
     __syncthreads();
 
@@ -198,7 +190,9 @@ void permute_small_kernel(const int32_t* __restrict__ topk_idx, const float* __r
 }
 
 // ---- router + single-workgroup permute in one launch (few tokens) -------
-template <int VPL>
+// LPT lanes per token: 64 (one token per wave, T <= 16) or 16 (four tokens
+// per wave, T <= 64), so all tokens are routed in one pass of the 16 waves.
+template <int LPT, int VPL>
 __global__ __launch_bounds__(kFusedThreads)
 void route_permute_kernel(const float* __restrict__ logits, int T, int E, int k, int renorm,
                           int e0, int E_loc, int s, int32_t* __restrict__ topk_idx,
@@ -207,27 +201,26 @@ void route_permute_kernel(const float* __restrict__ logits, int T, int E, int k,
     extern __shared__ int lds[];
     int* sidx = lds;                        // [T*k]
     float* sw = (float*)(lds + T * k);      // [T*k]
+    constexpr int TPW = 64 / LPT;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     constexpr int NW = kFusedThreads / 64;
-    float v[kFusedTPW][VPL];
-    #pragma unroll
-    for (int i = 0; i < kFusedTPW; ++i) {       // issue every token's loads first
-        const int t = w + NW * i;
-        if (t < T) load_logits<VPL>(logits + (size_t)t * E, E, lane, v[i]);
-    }
-    #pragma unroll
-    for (int i = 0; i < kFusedTPW; ++i) {
-        const int t = w + NW * i;
-        if (t < T) {
-            int e = 0;
-            float wt = 0.f;
-            wave_route_values<VPL>(v[i], E, k, renorm != 0, lane, e, wt);
-            if (lane < k) {
-                sidx[t * k + lane] = e;
-                sw[t * k + lane] = wt;
-                topk_idx[(size_t)t * k + lane] = e;
-                topk_w[(size_t)t * k + lane] = wt;
-            }
+    const int t = TPW * w + lane / LPT;
+    if (TPW * w < T) {                      // waves past the tokens skip routing
+        float v[VPL];
+        if (t < T) load_logits<LPT, VPL>(logits + (size_t)t * E, E, lane, v);
+        else {
+            #pragma unroll
+            for (int i = 0; i < VPL; ++i) v[i] = -INFINITY;
+        }
+        int e = 0;
+        float wt = 0.f;
+        route_values<LPT, VPL>(v, t < T ? E : 0, k, renorm != 0, lane, e, wt);
+        const int j = lane & (LPT - 1);
+        if (t < T && j < k) {
+            sidx[t * k + j] = e;
+            sw[t * k + j] = wt;
+            topk_idx[(size_t)t * k + j] = e;
+            topk_w[(size_t)t * k + j] = wt;
         }
     }
     __syncthreads();
@@ -272,9 +265,7 @@ void permute_scan_kernel(int32_t* __restrict__ chunk_hist, int nchunks, int T, i
     extern __shared__ int lds[];
     const int G = E_loc + s;
     int* cnt = lds;                     // [G]  counts, then offsets
-    int* tmp = cnt + G;                 // [G]
-    int* part = tmp + G;                // [kScanThreads] block-scan scratch
-    int* psum = part + kScanThreads;    // [kScanThreads] per-thread run sums
+    int* psum = cnt + G;                // [kScanThreads] per-thread run sums
     const int tid = threadIdx.x;
     const int seg = (nchunks + P - 1) / P;
     const int gpp = kScanThreads / P;
@@ -294,7 +285,7 @@ void permute_scan_kernel(int32_t* __restrict__ chunk_hist, int nchunks, int T, i
     }
     if (s && tid == 0) cnt[E_loc] = T;
     __syncthreads();
-    write_offsets(cnt, tmp, G, part, counts, offsets, offsets32);
+    write_offsets(cnt, G, counts, offsets, offsets32);
 
     for (int g0 = 0; g0 < E_loc; g0 += gpp) {          // chunk bases
         const int g = g0 + tid / P;
@@ -415,7 +406,7 @@ int moe_launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int 
         int P = 1;
         while (P * 2 <= kScanThreads / E_loc && P * 2 <= nchunks) P *= 2;
         hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads),
-                           (size_t)(2 * G + 2 * kScanThreads) * 4, stream, chunk_hist, nchunks, T,
+                           (size_t)(G + kScanThreads) * 4, stream, chunk_hist, nchunks, T,
                            E_loc, s, P, counts, offsets, offsets32);
         hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(kChunkThreads),
                            (size_t)(kChunkThreads / 64) * E_loc * 2 + 4, stream, topk_idx, topk_w,
@@ -428,7 +419,7 @@ int moe_launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int 
 }
 
 bool moe_route_permute_fusable(int T, int E, int k, int E_loc, int s) {
-    return T <= kFusedMaxT && E <= 2048 && E_loc + s <= kFusedMaxG && T * k <= kSmallMax;
+    return T <= kFusedMaxT && E <= 256 && k <= 16 && E_loc + s <= kFusedMaxG && T * k <= kSmallMax;
 }
 
 int moe_launch_route_permute(const float* logits, int T, int E, int k, uint32_t flags, int e0,
@@ -438,20 +429,24 @@ int moe_launch_route_permute(const float* logits, int T, int E, int k, uint32_t 
     const int G = E_loc + s;
     const int renorm = (flags & MOE_ROUTE_RENORM) ? 1 : 0;
     const size_t lds = ((size_t)2 * T * k + block_lds_ints(kFusedThreads / 64, G, E_loc)) * 4;
-    const int vpl = (E + 63) / 64;
-#define MOE_RP_CASE(N)                                                                         \
+#define MOE_RP_CASE(L, N)                                                                      \
     if (vpl <= N) {                                                                            \
-        hipLaunchKernelGGL(route_permute_kernel<N>, dim3(1), dim3(kFusedThreads), lds, stream, \
-                           logits, T, E, k, renorm, e0, E_loc, s, topk_idx, topk_w, counts,    \
-                           offsets, offsets32, row_src, row_w, slot_row);                      \
+        hipLaunchKernelGGL((route_permute_kernel<L, N>), dim3(1), dim3(kFusedThreads), lds,      \
+                           stream, logits, T, E, k, renorm, e0, E_loc, s, topk_idx, topk_w,    \
+                           counts, offsets, offsets32, row_src, row_w, slot_row);              \
         return (int)hipGetLastError();                                                         \
     }
-    MOE_RP_CASE(1)
-    MOE_RP_CASE(2)
-    MOE_RP_CASE(4)
-    MOE_RP_CASE(8)
-    MOE_RP_CASE(16)
-    MOE_RP_CASE(32)
+    if (T <= kFusedThreads / 64) {          // a whole wave per token
+        const int vpl = (E + 63) / 64;
+        MOE_RP_CASE(64, 1)
+        MOE_RP_CASE(64, 2)
+        MOE_RP_CASE(64, 4)
+    } else {
+        const int vpl = (E + 15) / 16;
+        MOE_RP_CASE(16, 4)
+        MOE_RP_CASE(16, 8)
+        MOE_RP_CASE(16, 16)
+    }
 #undef MOE_RP_CASE
     return -1;
 }

@@ -12,21 +12,29 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-template <int VPL>
+// LPT lanes per token, 64 / LPT tokens per wave.
+template <int LPT, int VPL>
 __global__ __launch_bounds__(64 * kWavesPerBlock)
 void route_kernel(const float* __restrict__ logits, int T, int E, int k, int renorm,
                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    constexpr int TPW = 64 / LPT;
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (t >= T) return;
+    const int t0 = (blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)) * TPW;
+    if (t0 >= T) return;
+    const int t = t0 + lane / LPT;
+    float v[VPL];
+    if (t < T) load_logits<LPT, VPL>(logits + (size_t)t * E, E, lane, v);
+    else {
+        #pragma unroll
+        for (int i = 0; i < VPL; ++i) v[i] = -INFINITY;
+    }
     int e = 0;
     float w = 0.f;
-    float v[VPL];
-    load_logits<VPL>(logits + (size_t)t * E, E, lane, v);
-    wave_route_values<VPL>(v, E, k, renorm != 0, lane, e, w);
-    if (lane < k) {
-        topk_idx[(size_t)t * k + lane] = e;
-        topk_w[(size_t)t * k + lane] = w;
+    route_values<LPT, VPL>(v, t < T ? E : 0, k, renorm != 0, lane, e, w);
+    const int j = lane & (LPT - 1);
+    if (t < T && j < k) {
+        topk_idx[(size_t)t * k + j] = e;
+        topk_w[(size_t)t * k + j] = w;
     }
 }
 
@@ -35,14 +43,29 @@ void route_kernel(const float* __restrict__ logits, int T, int E, int k, int ren
 int moe_launch_route(const float* logits, int T, int E, int k, uint32_t flags,
                      int32_t* topk_idx, float* topk_w, hipStream_t stream) {
     if (T == 0) return 0;
-    dim3 grid((T + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
-    int renorm = (flags & MOE_ROUTE_RENORM) ? 1 : 0;
-    int vpl = (E + 63) / 64;
-#define MOE_ROUTE_CASE(N)                                                              \
-    if (vpl <= N) {                                                                    \
-        hipLaunchKernelGGL(route_kernel<N>, grid, block, 0, stream, logits, T, E, k,   \
-                           renorm, topk_idx, topk_w);                                  \
-        return (int)hipGetLastError();                                                 \
+    const int renorm = (flags & MOE_ROUTE_RENORM) ? 1 : 0;
+    const dim3 block(64 * kWavesPerBlock);
+    if (E <= 256 && k <= 16) {                       // four tokens per wave
+        const dim3 grid((T + 4 * kWavesPerBlock - 1) / (4 * kWavesPerBlock));
+        const int vpl = (E + 15) / 16;
+#define MOE_ROUTE16_CASE(N)                                                                     \
+        if (vpl <= N) {                                                                         \
+            hipLaunchKernelGGL((route_kernel<16, N>), grid, block, 0, stream, logits, T, E, k,  \
+                               renorm, topk_idx, topk_w);                                       \
+            return (int)hipGetLastError();                                                      \
+        }
+        MOE_ROUTE16_CASE(4)
+        MOE_ROUTE16_CASE(8)
+        MOE_ROUTE16_CASE(16)
+#undef MOE_ROUTE16_CASE
+    }
+    const dim3 grid((T + kWavesPerBlock - 1) / kWavesPerBlock);
+    const int vpl = (E + 63) / 64;
+#define MOE_ROUTE_CASE(N)                                                                       \
+    if (vpl <= N) {                                                                             \
+        hipLaunchKernelGGL((route_kernel<64, N>), grid, block, 0, stream, logits, T, E, k,      \
+                           renorm, topk_idx, topk_w);                                           \
+        return (int)hipGetLastError();                                                          \
     }
     MOE_ROUTE_CASE(1)
     MOE_ROUTE_CASE(2)
