@@ -23,40 +23,15 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "gemm_common.h"
 
 namespace {
-
-constexpr uint32_t kInvalid = 0x80000000u;  // offset past every bounded region
-constexpr int kNonTemporal = 2;             // cache policy of loads streamed once (weights)
 
 // K-tiles per load batch: four FP4 (two FP8) weight K-tiles for one token
 // tile, fewer when several token tiles share the batch.
 template <int WFMT, int NTT>
 constexpr int batch_kt() {
     return ((WFMT == MFMA_FMT_FP4 ? 4 : 2) / NTT) > 0 ? (WFMT == MFMA_FMT_FP4 ? 4 : 2) / NTT : 1;
-}
-
-struct KParams {
-    const uint8_t* wbase[2];
-    size_t gstride, dpg, dpu, spu;   // group stride; data bytes per group; per unit data / scales
-    int E_loc, G, K, kt, kt4;
-    const int32_t* counts;
-    const int32_t* offsets;
-    const int32_t* offsets32;
-    const float* row_w;
-    const uint8_t* aq;
-    const uint8_t* as;
-    uint32_t aq_bytes, as_bytes;      // sizes of the activation arrays (bounds of the loads)
-    const int32_t* row_src;           // null: grouped row r is activation row r
-    int N;                            // W1: 2I ; W2: H (y row length)
-    int ceil_rule, transpose, use_w;
-    uint8_t* hq; uint8_t* hs; uint8_t* hTq; uint8_t* hTs; int ldT;
-    uint16_t* y;
-};
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-MOE_DEV rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 
 template <int WFMT>
@@ -105,10 +80,11 @@ MOE_DEV void load_batch(Batch<WFMT, NTT>& b, int kt_first, int kt_end, int lane,
         const bool ok = kt < kt_end;                       // uniform
         #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint32_t off = ok ? (uint32_t)(((kt * 4 + t) * 64 + lane) * BPL) : kInvalid;
+            // FP4: lane's 16 B at lane*16; FP8: the two 16 B halves at lane*16 and 1024 + lane*16
+            const uint32_t off = ok ? (uint32_t)((kt * 4 + t) * 64 * BPL + lane * 16) : kInvalid;
             b.A[i][t].lo = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kNonTemporal);
             if (WFMT == MFMA_FMT_FP8)
-                b.A[i][t].hi = __builtin_amdgcn_raw_buffer_load_b128(rw, off + (ok ? 16u : 0u), 0, kNonTemporal);
+                b.A[i][t].hi = __builtin_amdgcn_raw_buffer_load_b128(rw, off + (ok ? 1024u : 0u), 0, kNonTemporal);
             b.sA[i][t] = sword[t] >> (8 * (kt & 3));
         }
         #pragma unroll
@@ -141,28 +117,6 @@ MOE_DEV void mma_batch(const Batch<WFMT, NTT>& b, int ntt_active, f32x4 (&acc)[N
             }
         }
     }
-}
-
-// Wave 0: pass_off[g] = sum over g' < g of ceil(counts[g'] / rpp), and
-// pass_off[G] = the total, in LDS.
-MOE_DEV void pass_prefix(const int32_t* __restrict__ counts, int G, int rpp, int lane,
-                         int* pass_off) {
-    const int per = (G + 63) / 64;
-    const int lo = min(G, lane * per), hi = min(G, lo + per);
-    int s = 0;
-    for (int i = lo; i < hi; ++i) s += (counts[i] + rpp - 1) / rpp;
-    int inc = s;
-    #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int a = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += a;
-    }
-    int run = inc - s;
-    for (int i = lo; i < hi; ++i) {
-        pass_off[i] = run;
-        run += (counts[i] + rpp - 1) / rpp;
-    }
-    if (lane == 63) pass_off[G] = inc;
 }
 
 // Persistent grid: each workgroup walks the work items item = pass * units + u
@@ -339,38 +293,6 @@ void grouped_gemm_kernel(KParams p) {
     }
 }
 
-KParams make_params(const GemmArgs& a, bool w1) {
-    KParams p{};
-    PackGeom geo = moe_pack_geom(1, a.N, a.K, a.fmt);
-    for (int i = 0; i < 2; ++i) p.wbase[i] = a.w_base[i];
-    p.gstride = geo.group_stride; p.dpg = geo.data_per_group;
-    p.dpu = geo.data_per_unit;    p.spu = geo.scale_per_unit;
-    p.E_loc = a.E_loc; p.G = a.G; p.K = a.K; p.kt = geo.kt; p.kt4 = geo.kt4;
-    p.counts = a.counts; p.offsets = a.offsets; p.offsets32 = a.offsets32;
-    p.row_w = a.row_w; p.aq = a.aq; p.as = a.as; p.row_src = a.row_src; p.N = a.N;
-    p.aq_bytes = (uint32_t)((size_t)a.x_rows * a.K);
-    p.as_bytes = (uint32_t)((size_t)a.x_rows * (a.K / 32));
-    p.ceil_rule = (a.flags & MOE_SCALE_RULE_CEIL) ? 1 : 0;
-    p.transpose = (w1 && (a.flags & MOE_W1_WRITE_TRANSPOSE)) ? 1 : 0;
-    p.use_w = (w1 && a.row_w && !(a.flags & MOE_WEIGHT_AT_COMBINE)) ? 1 : 0;
-    p.hq = a.hq; p.hs = a.hs; p.hTq = a.hTq; p.hTs = a.hTs; p.ldT = a.ldT;
-    p.y = a.y;
-    return p;
-}
-
-int device_cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 template <int WFMT, bool IS_W1, int NTT, int KW>
 int launch(const KParams& p, long max_items, hipStream_t stream) {
     auto kern = grouped_gemm_kernel<WFMT, IS_W1, NTT, KW>;
@@ -391,12 +313,17 @@ int launch_kw(const KParams& p, int kw, long max_items, hipStream_t stream) {
     return launch<WFMT, IS_W1, NTT, 4>(p, max_items, stream);
 }
 
+constexpr int kTiledMinRows = 96;   // expected rows per group from which the tiled kernel runs
+
 template <bool IS_W1>
 int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     if (a.G == 0 || a.R_max == 0) return 0;
-    KParams p = make_params(a, IS_W1);
     // token tiles per pass, from the expected rows per group
     const int avg = a.rows_hint > 0 ? a.rows_hint : a.R_max / a.G;
+    // many rows per group: the weights are reused across many token tiles and
+    // the MFMA, not HBM, is the bound -> the LDS-tiled kernel
+    if (avg >= kTiledMinRows) return IS_W1 ? moe_launch_tiled_w1(a, stream) : moe_launch_tiled_w2(a, stream);
+    KParams p = make_params(a, IS_W1);
     int ntt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
     if (p.transpose && ntt < 2) ntt = 2;       // 32-token blocks must not straddle passes
     const int units = a.N / 64;

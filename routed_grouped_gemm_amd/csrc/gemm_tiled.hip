@@ -1,0 +1,407 @@
+// S4-S6 for groups with many rows (prefill and training-forward shapes, where
+// the grouped GEMMs are bound by the matrix cores, not by HBM; GC-MoE page,
+// "Limitations": at large token counts the compute partition is the
+// bottleneck).
+//
+// A workgroup of 8 waves (two per SIMD) computes 256 x 256 output tiles of
+// one group: four prepacked 64-row weight units (for W1: 32 gate rows and the
+// matching 32 up rows each) against 256 of the group's token rows, over the
+// whole K. Wave w owns weight unit w % 4 and token half w / 4: 64 x 128
+// outputs = 4 x 8 tiles of the 16x16x128 scaled MFMA, 32 MFMAs per 128-wide
+// K-tile.
+//
+// The tile size is set by L2 traffic: every operand byte is fetched into the
+// CU once per workgroup tile (no wave loads what another already loaded), so
+// a 128-wide K-tile moves 64 KiB for 16.8 MFLOP.
+//
+//  - Both operands of a K-tile (the 256 weight rows of the four units, the
+//    256 token rows, and their E8M0 words) are staged in LDS by buffer loads
+//    that write LDS directly, double-buffered: the next K-tile is in flight
+//    while this one is multiplied. The prepacked weight tiles are copied
+//    verbatim (1 KiB contiguous per load instruction) and are already in the
+//    A operand's lane order. Token rows are copied as whole 128-byte lines
+//    (8 rows per instruction), their 16-byte chunks XOR-swizzled by row so
+//    that the B operand reads (16 rows, one chunk each) hit 16 distinct bank
+//    groups. Rows past the group's end read as zero.
+//  - One barrier per K-tile. The loop runs over the workgroup's whole
+//    sequence of (item, K-tile) steps, so the next item's first K-tile is in
+//    flight while an item's epilogue runs.
+//  - Epilogues run on the accumulators. W1: gate and up of the same feature
+//    sit in the same lane (the prepacked units pair them), so
+//    h = SiLU(gate) * up * w is formed in place; the 32 features of a unit are
+//    one MX block along I (4 lanes x 8 values) and go out as one dword per
+//    lane; the transposed copy (32-token blocks along the group's rows) is
+//    transposed through LDS and leaves as 16-byte row stores. W2: BF16 rows.
+//    Conversions use the hardware's round-to-nearest-even converters.
+//
+// Work items are (group, 256-row pass, 256-row weight tile), weight tile
+// fastest; a persistent grid walks them, with item order swizzled so the
+// workgroups that run together on one XCD (blockIdx % 8) take consecutive
+// items and share operands in that XCD's L2.
+#include <algorithm>
+
+#include "gemm_common.h"
+
+namespace {
+
+constexpr int kRows = 256;                  // token rows per workgroup tile
+constexpr int kUnits = 4;                   // 64-row weight units per workgroup tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBT = 8;                      // 16-row token tiles per wave
+constexpr int kAT = 4;                      // 16-row weight tiles per wave (one unit)
+constexpr int kTStride = 136;               // bytes per feature row of the transposed staging
+constexpr int kTWave = 32 * kTStride;       // per-wave staging of the transposed copy
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One LDS stage (one K-tile of both operands):
+//   B  [256 token rows][8 chunks of 16 B], chunk c of row at slot c ^ bswz(row)   32 KiB
+//   A  [16 weight tiles][(half)][lane][16 B]        32 KiB (FP8) / 16 KiB (FP4)
+//   BS [256 token rows] E8M0 words                   1 KiB
+//   AS [16 weight tiles][lane] E8M0 words            4 KiB (byte kt % 4 is this K-tile's)
+template <int WFMT>
+struct Stage {
+    static constexpr int kBPL = WFMT == MFMA_FMT_FP4 ? 16 : 32;    // bytes per lane per tile
+    static constexpr int B = 0;
+    static constexpr int A = kRows * 128;
+    static constexpr int BS = A + 16 * 64 * kBPL;
+    static constexpr int AS = BS + kRows * 4;
+    static constexpr int Bytes = AS + 16 * 64 * 4;
+};
+
+MOE_DEV int bswz(int row) { return (row >> 1) & 7; }
+
+// One work item as seen by this lane.
+struct Ctx {
+    int g, pass, wt, rbase, nrows;
+    const uint8_t* wgrp;                    // prepacked group base
+    uint32_t xoff[4];                       // staged token rows 32 w + 8 i + lane / 8: byte offset of the row
+    uint32_t xsoff;                         // E8M0 row 64 w + lane (waves 0-3)
+};
+
+MOE_DEV Ctx decode(const KParams& p, const int* pass_off, int item, int wtiles, int w, int lane) {
+    Ctx c;
+    const int pg = item / wtiles;
+    c.wt = item - pg * wtiles;
+    int glo = 0, ghi = p.G;                 // largest g with pass_off[g] <= pg
+    while (ghi - glo > 1) {
+        const int mid = (glo + ghi) >> 1;
+        if (pass_off[mid] <= pg) glo = mid; else ghi = mid;
+    }
+    c.g = __builtin_amdgcn_readfirstlane(glo);
+    c.pass = pg - __builtin_amdgcn_readfirstlane(pass_off[c.g]);
+    const int n_g = p.counts[c.g];
+    c.rbase = p.offsets[c.g] + c.pass * kRows;
+    c.nrows = min(kRows, n_g - c.pass * kRows);
+    const int sel = c.g < p.E_loc ? 0 : 1;
+    const int gi = c.g < p.E_loc ? c.g : 0;
+    c.wgrp = p.wbase[sel] + gi * p.gstride;
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * w + 8 * i + (lane >> 3);
+        c.xoff[i] = kInvalid;
+        if (row < c.nrows) {
+            const long xr = p.row_src ? (long)p.row_src[c.rbase + row] : (long)(c.rbase + row);
+            c.xoff[i] = (uint32_t)(xr * p.K);
+        }
+    }
+    c.xsoff = kInvalid;
+    if (w < 4 && 64 * w + lane < c.nrows) {
+        const int row = 64 * w + lane;
+        const long xr = p.row_src ? (long)p.row_src[c.rbase + row] : (long)(c.rbase + row);
+        c.xsoff = (uint32_t)(xr * (p.K / 32));
+    }
+    return c;
+}
+
+// Stage K-tile kt of an item into one LDS stage with buffer loads that write
+// LDS directly (each lane's bytes land at the wave's LDS base + size * lane).
+// Wave w stages token rows [32w, 32w + 32) (lane l of instruction i: row
+// 32w + 8i + l/8, LDS slot l%8 holding chunk (l%8) ^ bswz(row)), the E8M0
+// words of token rows [64w, 64w + 64) (waves 0-3), and the weight tiles 2w,
+// 2w+1 of the four units with their E8M0 words (copied verbatim). With
+// valid == false every load is out of range: zeros land and no memory is
+// read.
+template <int WFMT>
+MOE_DEV void stage_all(const KParams& p, rsrc_t rx, rsrc_t rxs, const Ctx& c, int kt, bool valid,
+                       uint8_t* st, int w, int lane) {
+    using S = Stage<WFMT>;
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * w + 8 * i + (lane >> 3);
+        const int chunk = (lane & 7) ^ bswz(row);
+        const uint32_t xo = c.xoff[i];
+        const uint32_t o = (xo == kInvalid || !valid) ? kInvalid : xo + (uint32_t)(kt * 128 + 16 * chunk);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(st + S::B + (32 * w + 8 * i) * 128), 16, o, 0, 0, 0);
+    }
+    if (w < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rxs, (lds_void_t*)(st + S::BS + 256 * w), 4,
+            (c.xsoff == kInvalid || !valid) ? kInvalid : c.xsoff + (uint32_t)(kt * 4), 0, 0, 0);
+    #pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int T = 2 * w + i;                // weight tile within the workgroup tile
+        const int u = c.wt * kUnits + (T >> 2), t = T & 3;
+        const rsrc_t rw = make_rsrc(c.wgrp + (size_t)u * p.dpu, valid ? (uint32_t)p.dpu : 0u);
+        const rsrc_t rs = make_rsrc(c.wgrp + p.dpg + (size_t)u * p.spu, valid ? (uint32_t)p.spu : 0u);
+        #pragma unroll
+        for (int half = 0; half < S::kBPL / 16; ++half)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (lds_void_t*)(st + S::A + T * 64 * S::kBPL + half * 1024), 16,
+                (uint32_t)((kt * 4 + t) * 64 * S::kBPL + half * 1024 + lane * 16), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void_t*)(st + S::AS + T * 256), 4,
+            (uint32_t)((((kt >> 2) * 4 + t) * 64 + lane) * 4), 0, 0, 0);
+    }
+}
+
+// Quad transpose of bytes: lane k of each group of 4 lanes receives byte k of
+// the dword `x` of every lane of its quad, lane i's byte in byte i.
+MOE_DEV uint32_t quad_byte_transpose(uint32_t x, int lane) {
+    const uint32_t q0 = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x00, 0xF, 0xF, false);  // quad_perm(0,0,0,0)
+    const uint32_t q1 = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x55, 0xF, 0xF, false);  // (1,1,1,1)
+    const uint32_t q2 = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xAA, 0xF, 0xF, false);  // (2,2,2,2)
+    const uint32_t q3 = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xFF, 0xF, 0xF, false);  // (3,3,3,3)
+    const uint32_t k = (uint32_t)(lane & 3);
+    // v_perm_b32(a, b, sel): selector byte values 0-3 pick bytes of b, 4-7 bytes of a
+    const uint32_t sel01 = (k) | ((k + 4) << 8);                        // byte0 = b[k], byte1 = a[k]
+    const uint32_t lo = __builtin_amdgcn_perm(q1, q0, sel01 | (sel01 << 16));
+    const uint32_t hi = __builtin_amdgcn_perm(q3, q2, sel01 | (sel01 << 16));
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                  // lo bytes 0,1 then hi bytes 0,1
+}
+
+MOE_DEV uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+template <int WFMT, bool IS_W1>
+__global__ __launch_bounds__(kThreads, 1)
+void tiled_gemm_kernel(KParams p) {
+    using S = Stage<WFMT>;
+    const int G = p.G, units = p.N / 64;
+    const int wtiles = units / kUnits;       // units is a multiple of 4 (N % 256 == 0)
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t* ring = smem;                                               // [2][S::Bytes]
+    int* pass_off = (int*)(smem + 2 * S::Bytes);                        // [G + 1]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = lane >> 4, r = lane & 15;
+    const int wi = w & 3, ti = w >> 2;       // weight unit, token half
+    if (w == 0) pass_prefix(p.counts, G, kRows, lane, pass_off);
+    __syncthreads();
+    const int n_items = pass_off[G] * wtiles;
+    const int grid = gridDim.x;
+    const int slot = (grid % 8 == 0) ? (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8 : blockIdx.x;
+    if (slot >= n_items) return;
+    const int n_my = (n_items - slot + grid - 1) / grid;                 // this workgroup's items
+    const int nkt = p.kt;
+    const int total = n_my * nkt;
+
+    const rsrc_t rx = make_rsrc(p.aq, p.aq_bytes);
+    const rsrc_t rxs = make_rsrc(p.as, p.as_bytes);
+
+    Ctx cur = decode(p, pass_off, slot, wtiles, w, lane);
+    Ctx nxt = n_my > 1 ? decode(p, pass_off, slot + grid, wtiles, w, lane) : cur;
+
+    stage_all<WFMT>(p, rx, rxs, cur, 0, true, ring, w, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // B operand addresses of this lane's 8 token tiles within a stage: row
+    // 16 j + r, chunks q (bytes 0-15) and 4 + q (bytes 16-31), swizzled
+    int boff_lo[kBT], boff_hi[kBT];
+    #pragma unroll
+    for (int j = 0; j < kBT; ++j) {
+        const int row = ti * 128 + 16 * j + r;
+        boff_lo[j] = S::B + row * 128 + 16 * (q ^ bswz(row));
+        boff_hi[j] = S::B + row * 128 + 16 * ((4 + q) ^ bswz(row));
+    }
+
+    f32x4 acc[kBT][kAT];
+    for (int it = 0; it < n_my; ++it) {
+        #pragma unroll
+        for (int j = 0; j < kBT; ++j)
+            #pragma unroll
+            for (int t = 0; t < kAT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        int s = it * nkt;
+        for (int kt = 0; kt < nkt; ++kt, ++s) {
+            // prefetch step s + 1 into the other stage (zeros past the last step)
+            {
+                const bool same = kt + 1 < nkt;
+                stage_all<WFMT>(p, rx, rxs, same ? cur : nxt, same ? kt + 1 : 0, s + 1 < total,
+                                ring + ((s + 1) & 1) * S::Bytes, w, lane);
+            }
+            const uint8_t* st = ring + (s & 1) * S::Bytes;
+            // this wave's 4 weight tiles stay in registers for the K-tile; its
+            // 8 token tiles stream from LDS, each against all 4
+            const int ash = 8 * (kt & 3);
+            i32x8 A[kAT];
+            int sa[kAT];
+            #pragma unroll
+            for (int t = 0; t < kAT; ++t) {
+                const int T = wi * kAT + t;
+                const uint8_t* ap = st + S::A + T * 64 * S::kBPL + lane * 16;
+                const i32x4 alo = *(const i32x4*)ap;
+                const i32x4 ahi = WFMT == MFMA_FMT_FP8 ? *(const i32x4*)(ap + 1024) : i32x4{0, 0, 0, 0};
+                A[t] = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
+                sa[t] = ((const int*)(st + S::AS))[T * 64 + lane] >> ash;
+            }
+            #pragma unroll
+            for (int j = 0; j < kBT; ++j) {
+                const i32x4 blo = *(const i32x4*)(st + boff_lo[j]);
+                const i32x4 bhi = *(const i32x4*)(st + boff_hi[j]);
+                const i32x8 B = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+                const int bs = ((const int*)(st + S::BS))[ti * 128 + 16 * j + r] >> (8 * q);
+                #pragma unroll
+                for (int t = 0; t < kAT; ++t)
+                    acc[j][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, 0, 0>(A[t], B, acc[j][t], sa[t], bs);
+            }
+            __builtin_amdgcn_s_waitcnt(0);       // the next step's operands have landed
+            __syncthreads();
+        }
+
+        // ---------------------------------------------------- epilogue
+        const int tok0 = ti * (kBT * 16);
+        const int uu = cur.wt * kUnits + wi;                    // this wave's unit
+        if (IS_W1) {
+            // the stage just consumed serves as scratch; the next step's
+            // prefetch lands in it only after the barrier below
+            uint8_t* scratch = ring + ((s - 1) & 1) * S::Bytes;
+            uint8_t* tw = scratch + w * kTWave;
+            uint8_t* tsw = scratch + kWaves * kTWave + w * 128;
+            const int I = p.N / 2;
+            #pragma unroll
+            for (int jp = 0; jp < kBT / 2; ++jp) {
+                float h[2][2][4];                               // [j in pair][gate tile][v]
+                #pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j = 2 * jp + jj;
+                    const int tok = tok0 + 16 * j + r;
+                    const bool valid = tok < cur.nrows;
+                    const float wgt = (p.use_w && valid) ? p.row_w[cur.rbase + tok] : 1.0f;
+                    uint32_t am = 0;
+                    #pragma unroll
+                    for (int a = 0; a < 2; ++a)
+                        #pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const float hv = valid ? silu_fast(acc[j][a][v]) * acc[j][a + 2][v] * wgt : 0.f;
+                            h[jj][a][v] = hv;
+                            am = max(am, abs_bits(hv));
+                        }
+                    // the unit's 32 features of this token: 4 lanes (q) x 8 values
+                    am = max(am, (uint32_t)__shfl_xor((int)am, 16, 64));
+                    am = max(am, (uint32_t)__shfl_xor((int)am, 32, 64));
+                    const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
+                    const float inv = inv_scale(code);
+                    if (valid) {
+                        const size_t row = (size_t)(cur.rbase + tok);
+                        #pragma unroll
+                        for (int a = 0; a < 2; ++a)
+                            *(uint32_t*)(p.hq + row * I + 32 * uu + 16 * a + 4 * q) =
+                                e4m3x4(h[jj][a][0] * inv, h[jj][a][1] * inv, h[jj][a][2] * inv, h[jj][a][3] * inv);
+                        if (q == 0) p.hs[row * (I / 32) + uu] = (uint8_t)code;
+                    }
+                }
+                if (p.transpose) {
+                    // 32-token block jp of this wave (tokens tok0 + 32 jp + [0, 32)):
+                    // per feature, amax over its 16 lanes x 2 tiles; codes go to the
+                    // wave's LDS staging as [feature][token], 4 tokens per dword
+                    #pragma unroll
+                    for (int a = 0; a < 2; ++a) {
+                        float sc[2][4];
+                        #pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const uint32_t am = row16_umax(max(abs_bits(h[0][a][v]), abs_bits(h[1][a][v])));
+                            const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
+                            const float inv = inv_scale(code);
+                            sc[0][v] = h[0][a][v] * inv;
+                            sc[1][v] = h[1][a][v] * inv;
+                            if (r == 0) tsw[(16 * a + 4 * q + v) * 4 + jp] = (uint8_t)code;
+                        }
+                        // lane 4m + k: feature 16a + 4q + k, tokens 16 j + 4m .. +3
+                        #pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            const uint32_t pk = e4m3x4(sc[jj][0], sc[jj][1], sc[jj][2], sc[jj][3]);
+                            const uint32_t tr = quad_byte_transpose(pk, lane);
+                            const int fl = 16 * a + 4 * q + (lane & 3);
+                            *(uint32_t*)(tw + fl * kTStride + 16 * (2 * jp + jj) + 4 * ((lane >> 2) & 3)) = tr;
+                        }
+                    }
+                }
+            }
+            if (p.transpose) {
+                // LDS -> hT rows: feature rows of 128 token bytes, 16 bytes per lane;
+                // only 32-token blocks that start inside the group's rows
+                const int col0 = p.offsets32[cur.g] + cur.pass * kRows + tok0;
+                const int fbase = 32 * uu;
+                #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int fl = 8 * i + (lane >> 3), c = lane & 7;
+                    if (tok0 + 32 * (c >> 1) < cur.nrows) {
+                        const i32x4 d = *(const i32x4*)(tw + fl * kTStride + 16 * c);
+                        *(i32x4*)(p.hTq + (size_t)(fbase + fl) * p.ldT + col0 + 16 * c) = d;
+                    }
+                }
+                // scales: feature lane (< 32), 4 blocks -> bytes [col0/32, +4) of its hT scale row
+                if (lane < 32) {
+                    const uint32_t sw = *(const uint32_t*)(tsw + lane * 4);
+                    uint8_t* srow = p.hTs + (size_t)(fbase + lane) * (p.ldT / 32) + (col0 >> 5);
+                    #pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        if (tok0 + 32 * b < cur.nrows) srow[b] = (uint8_t)(sw >> (8 * b));
+                }
+            }
+            __syncthreads();                 // scratch free before the next prefetch lands in it
+        } else {
+            const int H = p.N;
+            #pragma unroll
+            for (int j = 0; j < kBT; ++j) {
+                const int tok = tok0 + 16 * j + r;
+                if (tok < cur.nrows) {
+                    uint16_t* yrow = p.y + (size_t)(cur.rbase + tok) * H + 64 * uu + 4 * q;
+                    #pragma unroll
+                    for (int t = 0; t < kAT; ++t) {
+                        uint2 o;
+                        o.x = bf16x2(acc[j][t][0], acc[j][t][1]);
+                        o.y = bf16x2(acc[j][t][2], acc[j][t][3]);
+                        *(uint2*)(yrow + 16 * t) = o;
+                    }
+                }
+            }
+        }
+        cur = nxt;
+        if (it + 2 < n_my) nxt = decode(p, pass_off, slot + (it + 2) * grid, wtiles, w, lane);
+    }
+}
+
+template <int WFMT, bool IS_W1>
+int launch_tiled(const KParams& p, int R_max, hipStream_t stream) {
+    auto kern = tiled_gemm_kernel<WFMT, IS_W1>;
+    const size_t lds = 2 * (size_t)Stage<WFMT>::Bytes + (size_t)(p.G + 1) * 4;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const long wtiles = p.N / 64 / kUnits;
+    // passes never exceed R_max / 256 + G: each group adds at most one partial pass
+    const long max_items = wtiles * ((long)R_max / kRows + p.G);
+    const long grid = std::max<long>(1, std::min<long>(max_items, (long)per_cu * device_cu_count()));
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream) {
+    if (a.G == 0 || a.R_max == 0) return 0;
+    const KParams p = make_params(a, true);
+    return a.fmt == MOE_FMT_MXFP4 ? launch_tiled<MFMA_FMT_FP4, true>(p, a.R_max, stream)
+                                  : launch_tiled<MFMA_FMT_FP8, true>(p, a.R_max, stream);
+}
+
+int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream) {
+    if (a.G == 0 || a.R_max == 0) return 0;
+    const KParams p = make_params(a, false);
+    return a.fmt == MOE_FMT_MXFP4 ? launch_tiled<MFMA_FMT_FP4, false>(p, a.R_max, stream)
+                                  : launch_tiled<MFMA_FMT_FP8, false>(p, a.R_max, stream);
+}

@@ -115,6 +115,31 @@ MOE_DEV uint32_t f64_to_bf16(double d) {
 
 MOE_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// Hardware conversions for the epilogues. Each gives the same bits as the
+// software conversions above for every finite input (checked on 2^21 random
+// and tie-case pairs): v_cvt_pk_fp8_f32 rounds to nearest even into OCP E4M3,
+// and the clamp to +-448 first makes it saturate; v_cvt_pk_bf16_f32 rounds to
+// nearest even.
+MOE_DEV float e4m3_clamp(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+// codes of a, b in bytes 0, 1
+MOE_DEV uint32_t e4m3x2(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false) & 0xFFFFu;
+}
+// codes of a, b, c, d in bytes 0..3
+MOE_DEV uint32_t e4m3x4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true);
+}
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
+// bf16 bits of a (low half) and b (high half)
+MOE_DEV uint32_t bf16x2(float a, float b) {
+    const moe_f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, moe_bf16x2));
+}
+// SiLU with the hardware reciprocal (1 ulp) instead of a full division
+MOE_DEV float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
 // Wave-wide helpers (wave64).
 MOE_DEV float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 
@@ -161,6 +186,16 @@ MOE_DEV float row16_max(float v) {
     v = fmaxf(v, MOE_DPP(v, MOE_DPP_XOR2, 0xF));
     v = fmaxf(v, MOE_DPP(v, MOE_DPP_HALF_MIRROR, 0xF));
     v = fmaxf(v, MOE_DPP(v, MOE_DPP_MIRROR, 0xF));
+    return v;
+}
+
+// max over the 16 lanes of a DPP row of non-negative floats given as their
+// bit patterns (integer order = float order for them): one fused DPP max each
+MOE_DEV uint32_t row16_umax(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_XOR1, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_XOR2, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_HALF_MIRROR, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_MIRROR, 0xF, 0xF, true));
     return v;
 }
 

@@ -58,6 +58,9 @@ struct GemmArgs {
 };
 int moe_launch_grouped_w1(const GemmArgs& a, hipStream_t stream);
 int moe_launch_grouped_w2(const GemmArgs& a, hipStream_t stream);
+// LDS-tiled variants for groups with many rows (256 x 256 workgroup tiles)
+int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream);
+int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream);
 
 int moe_launch_combine(const uint16_t* y, const int32_t* slot_row, const float* row_w, int T,
                        int ks, int H, uint16_t* out, hipStream_t stream);

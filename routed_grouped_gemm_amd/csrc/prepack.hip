@@ -8,10 +8,12 @@
 //            workgroup owns gate row n and up row n (the fusion blog's gate/up
 //            repack for a fused GLU epilogue, done at load time)
 //   tile   = 16 rows x 128 K of a unit (4 tiles per unit per K-tile)
-//   data   [g][unit][kt][tile][lane 0..63][bpl bytes], lane l holding row l%16
-//          of the tile and lane group q = l/16 in MFMA operand order:
-//            FP4 (bpl 16): K [kt*128 + 32q, +32), element 2i in the low nibble
-//            FP8 (bpl 32): K [kt*128 + 16q, +16) then K [kt*128 + 64 + 16q, +16)
+//   data   [g][unit][kt][tile][...], lane l holding row l%16 of the tile and
+//          lane group q = l/16 in MFMA operand order:
+//            FP4: [lane][16 B], K [kt*128 + 32q, +32), element 2i in the low nibble
+//            FP8: [half][lane][16 B], half 0 = K [kt*128 + 16q, +16),
+//                 half 1 = K [kt*128 + 64 + 16q, +16)
+//          so every 16-byte load of a wave reads 1 KiB contiguous
 //   scales [g][unit][kt/4][tile][lane][kt%4]: the E8M0 byte of row l%16,
 //          K-block kt*4 + q; one dword per lane covers four K-tiles.
 // A 16x128 tile is one contiguous 1 KiB (FP4) / 2 KiB (FP8) burst.
@@ -55,7 +57,7 @@ __global__ void prepack_data_kernel(const uint8_t* __restrict__ q, int G, int N,
     const int row = logical_row(u, tile, lane % 16, is_w1, N / 2);
     const int grp = lane / 16;
     uint8_t* out = dst + g * p.group_stride + u * p.data_per_unit +
-                   ((size_t)(kt * 4 + tile) * 64 + lane) * p.bpl;
+                   (size_t)(kt * 4 + tile) * 64 * p.bpl + lane * 16;
     if (fmt == MOE_FMT_MXFP4) {
         const size_t rowb = (size_t)K / 2;
         const uint8_t* src = q + ((size_t)g * N + row) * rowb + kt * 64 + 16 * grp;
@@ -63,7 +65,7 @@ __global__ void prepack_data_kernel(const uint8_t* __restrict__ q, int G, int N,
     } else {
         const uint8_t* src = q + ((size_t)g * N + row) * (size_t)K + kt * 128;
         *(uint4*)out = *(const uint4*)(src + 16 * grp);
-        *(uint4*)(out + 16) = *(const uint4*)(src + 64 + 16 * grp);
+        *(uint4*)(out + 1024) = *(const uint4*)(src + 64 + 16 * grp);
     }
 }
 

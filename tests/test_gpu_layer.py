@@ -56,6 +56,9 @@ SMALL = [
     ("renorm-ceil", dict(T=24, E=16, k=4, n_local=16), moe.MOE_ROUTE_RENORM | moe.MOE_SCALE_RULE_CEIL),
     ("weight-at-combine", dict(T=20, E=8, k=3, n_local=8), moe.MOE_WEIGHT_AT_COMBINE),
     ("ragged-passes", dict(T=200, H=768, I=256, E=4, k=2, n_local=4, shared=True), 0),
+    # about 275 rows per expert: the LDS-tiled GEMMs, with the transposed copy
+    ("tiled-mxfp8-transpose", dict(T=1100, H=512, I=384, E=8, k=2, n_local=8, w_fmt="e4m3",
+                                   transpose=True), moe.MOE_W1_WRITE_TRANSPOSE),
 ]
 
 

@@ -138,12 +138,23 @@ W1_CASES = [
     ([45, 0, 100, 32, 1], 512, 384, "e4m3", moe.MOE_W1_WRITE_TRANSPOSE),
     ([7, 90], 768, 256, "e2m1", moe.MOE_SCALE_RULE_CEIL | moe.MOE_W1_WRITE_TRANSPOSE),
     ([5, 12, 0, 40], 512, 256, "e2m1", moe.MOE_WEIGHT_AT_COMBINE),
+    # several 256-row passes, ragged tails, empty groups
+    ([0, 1, 255, 256, 257, 600, 33], 512, 256, "e4m3", (1 << 31) | moe.MOE_W1_WRITE_TRANSPOSE),
+    ([300, 17, 513], 1024, 512, "e2m1", 0),
+    ([520, 0, 64], 512, 384, "e4m3", moe.MOE_SCALE_RULE_CEIL | moe.MOE_W1_WRITE_TRANSPOSE),
 ]
 
+# rows_hint picks the kernel: few expected rows per group -> the decode-shaped
+# kernel (weights streamed once, K split across waves); many -> the LDS-tiled
+# kernel (256 x 256 workgroup tiles). Both must give the same answers.
+KERNELS = {"decode": 1, "tiled": 4096}
 
+
+@pytest.mark.parametrize("kernel", list(KERNELS))
 @pytest.mark.parametrize("counts,H,I,fmt,flags", W1_CASES)
-def test_grouped_w1_parity(counts, H, I, fmt, flags):
-    banner(f"grouped_w1 counts={counts} H={H} I={I} fmt={fmt} flags={flags}")
+def test_grouped_w1_parity(counts, H, I, fmt, flags, kernel):
+    banner(f"grouped_w1 {kernel} counts={counts} H={H} I={I} fmt={fmt} flags={flags}")
+    hint = KERNELS[kernel]
     gather = bool(flags & (1 << 31))
     flags &= ~(1 << 31)
     offsets, xq, xs, row_w, w1, _ = _grouped_problem(counts, H, I, fmt, 5 + H + I)
@@ -168,10 +179,11 @@ def test_grouped_w1_parity(counts, H, I, fmt, flags):
     off32[1:] = np.cumsum((np.array(counts) + 31) // 32 * 32)
     if gather:
         hq, hs, hTq, hTs = moe.moe_grouped_w1(pw, counts_d, dev(offsets), dev(row_w), dev(tq), dev(ts), I,
-                                              flags, offsets32=dev(off32), row_src=dev(row_src), R_max=R)
+                                              flags, offsets32=dev(off32), row_src=dev(row_src), R_max=R,
+                                              rows_hint=hint)
     else:
         hq, hs, hTq, hTs = moe.moe_grouped_w1(pw, counts_d, dev(offsets), dev(row_w), dev(xq), dev(xs), I,
-                                              flags, offsets32=dev(off32))
+                                              flags, offsets32=dev(off32), rows_hint=hint)
     dh = _h_error_bound(xq, xs, offsets, w1, fmt, I, ref, wts)
     assert_mx_within_1ulp(host(hq)[:R], host(hs)[:R], ref.hq, ref.hs, "h", extra_tol=dh)
     if transpose:
@@ -205,19 +217,23 @@ W2_CASES = [
     ([0, 1, 17, 70, 33, 5], 1024, 512, "e2m1"),
     ([3, 0, 64, 129], 512, 256, "e4m3"),
     ([200], 768, 384, "e2m1"),
+    ([0, 1, 255, 256, 257, 600, 33], 512, 256, "e4m3"),
+    ([300, 17, 513], 1024, 512, "e2m1"),
 ]
 
 
+@pytest.mark.parametrize("kernel", list(KERNELS))
 @pytest.mark.parametrize("counts,H,I,fmt", W2_CASES)
-def test_grouped_w2_parity(counts, H, I, fmt):
-    banner(f"grouped_w2 counts={counts} H={H} I={I} fmt={fmt}")
+def test_grouped_w2_parity(counts, H, I, fmt, kernel):
+    banner(f"grouped_w2 {kernel} counts={counts} H={H} I={I} fmt={fmt}")
     offsets, _, _, _, _, w2 = _grouped_problem(counts, H, I, fmt, 9 + H + I)
     R = int(offsets[-1])
     rng = np.random.default_rng(1)
     hq, hs = mx.quantize_mx(rng.standard_normal((R, I)) * 0.1, mx.FMT_E4M3)
     y_ref = omoe.grouped_w2(hq, hs, offsets, [a[0] for a in w2], [a[1] for a in w2], fmt)
     pw = _packed(w2, fmt, False)
-    y = moe.moe_grouped_w2(pw, dev(np.array(counts, np.int32)), dev(offsets), dev(hq), dev(hs), H)
+    y = moe.moe_grouped_w2(pw, dev(np.array(counts, np.int32)), dev(offsets), dev(hq), dev(hs), H,
+                           rows_hint=KERNELS[kernel])
     # tolerance: one BF16 step, plus the scaled-MFMA inner-sum bound for
     # outputs that cancel
     hd = mx.dequantize_mx(hq, hs, mx.FMT_E4M3)
