@@ -17,9 +17,11 @@ logits, x codes + scales, the W1 and W2 codes + scales of the experts that
 received at least one token, and the BF16 output. The "roofline" object is
 for the dominant kernel (the grouped W1 GEMM), timed with HIP events around
 its launches on the launching stream; "cpu_baseline" times the CPU oracle on
-a bounded sample (the T=8 call of one routing draw).
+a bounded sample (the T=8 call of one routing draw). "other_workloads"
+gives the layer latency, TB/s, TFLOP/s and roofline fraction of the tiny,
+full-expert, 16K-token prefill and shared-expert workloads (graph replay).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-other-workloads]
 """
 from __future__ import annotations
 
@@ -87,6 +89,85 @@ def cpu_baseline(c8, moe_bytes_fn):
                       f"{dt:.2f} s wall on the host CPU, fp64 NumPy"}, dt
 
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0
+
+
+def other_workloads(torch, moe, synth, device, names, reps=4):
+    """Layer latency of the other workloads (one GPU, graph replay, HIP events
+    on the replay stream): the tiny case, the full-expert case, the 16K-token
+    prefill case (MXFP8 weights, transposed copy of h) and the decode share
+    at T = 32 with a shared expert. Each call alternates between two routing
+    draws and two weight copies, so weights stream from HBM as in a model.
+    Algorithmic bytes and FLOPs as for the decode bench; roofline: HBM for
+    the bandwidth-bound shapes, dense FP8 MFMA for prefill."""
+    out = {}
+    for name in names:
+        c = synth.config(name)
+        flags = moe.MOE_W1_WRITE_TRANSPOSE if c.transpose else 0
+        dw = device.build_weights(c)
+        copies = [dw]
+        w1 = moe.PackedWeights.empty(c.n_local, 2 * c.I, c.H, dw.w1.fmt, True)
+        w2 = moe.PackedWeights.empty(c.n_local, c.H, c.I, dw.w2.fmt, False)
+        w1.buf.copy_(dw.w1.buf)
+        w2.buf.copy_(dw.w2.buf)
+        copies.append(device.DeviceWeights(w1, w2, dw.shared))
+        ins = [device.build_inputs(c, v) for v in range(2)]
+        ws = moe.LayerWorkspace(c.T, c.E, c.k, c.n_local, c.H, c.I, bool(c.shared), flags)
+        hT = (None, None)
+        if c.transpose:
+            ld = moe.moe_transposed_ld(c.R_max, c.G)
+            hT = (torch.empty((c.I, ld), dtype=torch.uint8, device="cuda"),
+                  torch.empty((c.I, ld // 32), dtype=torch.uint8, device="cuda"))
+        res = torch.empty((c.T, c.H), dtype=torch.uint16, device="cuda")
+
+        def call(v, wcopy):
+            lg, xq, xs = ins[v]
+            moe.moe_layer(lg, xq, xs, wcopy.w1, wcopy.w2, c.k, c.e0, c.n_local, wcopy.shared, flags,
+                          out=res, ws=ws, hTq=hT[0], hTs=hT[1])
+
+        stats = []
+        for v in range(2):
+            call(v, dw)
+            cnt = ws.view("counts").cpu()
+            stats.append((int((cnt[:c.n_local] > 0).sum()), int(cnt.sum())))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(4):
+                call(i % 2, copies[(i // 2) % 2])
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (4 * reps)
+        fp4 = c.w_fmt == "e2m1"
+        bw = 0.5 if fp4 else 1.0
+        nbytes, flops = 0.0, 0.0
+        for active, R in stats:
+            act = active + (1 if c.shared else 0)
+            nbytes += (4 * c.T * c.E + c.T * c.H * (1 + 1 / 32) + act * 3 * c.I * c.H * (bw + 1 / 32)
+                       + 2 * c.T * c.H) / 2
+            flops += 6.0 * R * c.H * c.I / 2
+        tbps = nbytes / us / 1e6
+        tflops = flops / us / 1e6
+        bound = "mfma" if name == "prefill" else "hbm"
+        frac = tflops / MFMA_FP8_PEAK_TFLOPS if bound == "mfma" else tbps * 1e3 / HBM_PEAK_GBS
+        out[name] = {"T": c.T, "H": c.H, "I": c.I, "E": c.E, "k": c.k, "local": c.n_local,
+                     "shared": bool(c.shared), "weights": "MXFP4" if fp4 else "MXFP8",
+                     "latency_us": round(us, 2), "TBps": round(tbps, 3), "TFLOPs": round(tflops, 1),
+                     "bound": bound, "roofline_frac": round(frac, 4),
+                     "active_groups": [a for a, _ in stats], "rows": [R for _, R in stats]}
+        log(f"{name}: {out[name]}")
+        del dw, copies, w1, w2, ws, hT, res, g
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +175,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated between calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the latency lines of the tiny, full-expert, prefill and shared-expert workloads")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -254,6 +337,10 @@ def main():
                 "kernel": "grouped_gemm_kernel (W1, MXFP4)",
                 "avg_launch_us": round(w1_ms * 1e3 / nlaunch, 2), "launches": nlaunch}
 
+    others = None
+    if not args.no_other_workloads:
+        others = other_workloads(torch, moe, synth, device, ["tiny", "full", "prefill", "shared"])
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu, _ = cpu_baseline(cfg[8], lambda T, act: layer_bytes(T, c.E, c.H, c.I, act, fp4))
@@ -278,6 +365,7 @@ def main():
         "eager_TBps": round(eager_tbps, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "other_workloads": others,
     }
     print(json.dumps(line), flush=True)
 
