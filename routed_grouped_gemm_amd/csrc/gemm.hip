@@ -123,7 +123,7 @@ MOE_DEV void mma_batch(const Batch<WFMT, NTT>& b, int ntt_active, f32x4 (&acc)[N
 // (every pass of 16*NTT rows of every group, times the 64-row weight units),
 // striding by the grid size; empty groups contribute no items.
 template <int WFMT, bool IS_W1, int NTT, int KW>
-__global__ __launch_bounds__(64 * KW)
+__global__ __launch_bounds__(64 * KW, NTT == 1 ? 4 : 2)   // waves per SIMD: 4 (128 VGPRs) for one token tile
 void grouped_gemm_kernel(KParams p) {
     constexpr int NT = 64 * KW;
     const int rows_per_pass = 16 * NTT;
