@@ -16,7 +16,10 @@ of the step's layer calls / wall time of the steps, in TB/s. Algorithmic bytes p
 logits, x codes + scales, the W1 and W2 codes + scales of the experts that
 received at least one token, and the BF16 output. The "roofline" object is
 for the dominant kernel (the grouped W1 GEMM), timed with HIP events around
-its launches on the launching stream; "cpu_baseline" times the CPU oracle on
+its launches on the launching stream, with "traffic" the HBM bytes per launch
+measured by hardware counters (profiles/decode_w1_hbm_traffic.txt; null once
+the kernel sources differ from those the counters were taken with);
+"cpu_baseline" times the CPU oracle on
 a bounded sample (the T=8 call of one routing draw). "other_workloads"
 gives the layer latency, TB/s, TFLOP/s and roofline fraction of the tiny,
 full-expert, 16K-token prefill and shared-expert workloads (graph replay).
@@ -90,6 +93,30 @@ def cpu_baseline(c8, moe_bytes_fn):
 
 
 MFMA_FP8_PEAK_TFLOPS = 5000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_w1_hbm_traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per W1 launch from the committed counter runs (FETCH_SIZE and
+    WRITE_SIZE, calibrated on a 1 GiB copy), or None when the kernel sources
+    changed since they were taken."""
+    import hashlib
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for name in kv["kernel_sources"].split():
+            with open(os.path.join(ROOT, "routed_grouped_gemm_amd", "csrc", name), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != kv["kernel_sources_sha256"]:
+            return None
+        return float(kv["bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def other_workloads(torch, moe, synth, device, names, reps=4):
@@ -333,7 +360,7 @@ def main():
             nlaunch += 1
     w1_gbs = w1_b / (w1_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(w1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(w1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(w1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "grouped_gemm_kernel (W1, MXFP4)",
                 "avg_launch_us": round(w1_ms * 1e3 / nlaunch, 2), "launches": nlaunch}
 
