@@ -52,8 +52,10 @@ constexpr int kBT = 8;                      // 16-row token tiles per wave
 constexpr int kAT = 4;                      // 16-row weight tiles per wave (one unit)
 constexpr int kTStride = 136;               // bytes per feature row of the transposed staging
 constexpr int kTWave = 32 * kTStride;       // per-wave staging of the transposed copy
+constexpr int kYStride = 144;               // bytes per token row of the BF16 output staging (conflict-free)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // One LDS stage (one K-tile of both operands):
 //   B  [256 token rows][8 chunks of 16 B], chunk c of row at slot c ^ bswz(row)   32 KiB
@@ -97,20 +99,23 @@ MOE_DEV Ctx decode(const KParams& p, const int* pass_off, int item, int wtiles, 
     const int sel = c.g < p.E_loc ? 0 : 1;
     const int gi = c.g < p.E_loc ? c.g : 0;
     c.wgrp = p.wbase[sel] + gi * p.gstride;
+    // source rows of the item's grouped rows (branch-free: rows past the
+    // item read as 0 through the bounded resource and are marked invalid)
+    const rsrc_t rsrcs = make_rsrc(p.row_src + c.rbase, p.row_src ? (uint32_t)(c.nrows * 4) : 0u);
+    auto src_row = [&](int row) -> uint32_t {
+        return p.row_src ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrcs, (uint32_t)(row * 4), 0, 0)
+                         : (uint32_t)(c.rbase + row);
+    };
     #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 32 * w + 8 * i + (lane >> 3);
-        c.xoff[i] = kInvalid;
-        if (row < c.nrows) {
-            const long xr = p.row_src ? (long)p.row_src[c.rbase + row] : (long)(c.rbase + row);
-            c.xoff[i] = (uint32_t)(xr * p.K);
-        }
+        const uint32_t xr = src_row(row);
+        c.xoff[i] = row < c.nrows ? xr * (uint32_t)p.K : kInvalid;
     }
-    c.xsoff = kInvalid;
-    if (w < 4 && 64 * w + lane < c.nrows) {
+    {
         const int row = 64 * w + lane;
-        const long xr = p.row_src ? (long)p.row_src[c.rbase + row] : (long)(c.rbase + row);
-        c.xsoff = (uint32_t)(xr * (p.K / 32));
+        const uint32_t xr = src_row(row);
+        c.xsoff = (w < 4 && row < c.nrows) ? xr * (uint32_t)(p.K / 32) : kInvalid;
     }
     return c;
 }
@@ -271,6 +276,10 @@ void tiled_gemm_kernel(KParams p) {
             uint8_t* tw = scratch + w * kTWave;
             uint8_t* tsw = scratch + kWaves * kTWave + w * 128;
             const int I = p.N / 2;
+            // the item's rows of h, its scales and its routing weights
+            const rsrc_t rhq = make_rsrc(p.hq + (size_t)cur.rbase * I, (uint32_t)(cur.nrows * I));
+            const rsrc_t rhs = make_rsrc(p.hs + (size_t)cur.rbase * (I / 32), (uint32_t)(cur.nrows * (I / 32)));
+            const rsrc_t rw_w = make_rsrc(p.row_w + cur.rbase, p.use_w ? (uint32_t)(cur.nrows * 4) : 0u);
             #pragma unroll
             for (int jp = 0; jp < kBT / 2; ++jp) {
                 float h[2][2][4];                               // [j in pair][gate tile][v]
@@ -278,14 +287,14 @@ void tiled_gemm_kernel(KParams p) {
                 for (int jj = 0; jj < 2; ++jj) {
                     const int j = 2 * jp + jj;
                     const int tok = tok0 + 16 * j + r;
-                    const bool valid = tok < cur.nrows;
-                    const float wgt = (p.use_w && valid) ? p.row_w[cur.rbase + tok] : 1.0f;
+                    // rows past the item have zero token rows, so zero sums and h = 0
+                    const float wgt = p.use_w ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw_w, (uint32_t)(tok * 4), 0, 0)) : 1.0f;
                     uint32_t am = 0;
                     #pragma unroll
                     for (int a = 0; a < 2; ++a)
                         #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            const float hv = valid ? silu_fast(acc[j][a][v]) * acc[j][a + 2][v] * wgt : 0.f;
+                            const float hv = silu_fast(acc[j][a][v]) * acc[j][a + 2][v] * wgt;
                             h[jj][a][v] = hv;
                             am = max(am, abs_bits(hv));
                         }
@@ -294,14 +303,14 @@ void tiled_gemm_kernel(KParams p) {
                     am = max(am, (uint32_t)__shfl_xor((int)am, 32, 64));
                     const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
                     const float inv = inv_scale(code);
-                    if (valid) {
-                        const size_t row = (size_t)(cur.rbase + tok);
-                        #pragma unroll
-                        for (int a = 0; a < 2; ++a)
-                            *(uint32_t*)(p.hq + row * I + 32 * uu + 16 * a + 4 * q) =
-                                e4m3x4(h[jj][a][0] * inv, h[jj][a][1] * inv, h[jj][a][2] * inv, h[jj][a][3] * inv);
-                        if (q == 0) p.hs[row * (I / 32) + uu] = (uint8_t)code;
-                    }
+                    // rows past the item fall outside the resources' range: dropped
+                    #pragma unroll
+                    for (int a = 0; a < 2; ++a)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            e4m3x4(h[jj][a][0] * inv, h[jj][a][1] * inv, h[jj][a][2] * inv, h[jj][a][3] * inv),
+                            rhq, (uint32_t)(tok * I + 32 * uu + 16 * a + 4 * q), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, rhs,
+                                                         q == 0 ? (uint32_t)(tok * (I / 32) + uu) : kInvalid, 0, 0);
                 }
                 if (p.transpose) {
                     // 32-token block jp of this wave (tokens tok0 + 32 jp + [0, 32)):
@@ -317,7 +326,7 @@ void tiled_gemm_kernel(KParams p) {
                             const float inv = inv_scale(code);
                             sc[0][v] = h[0][a][v] * inv;
                             sc[1][v] = h[1][a][v] * inv;
-                            if (r == 0) tsw[(16 * a + 4 * q + v) * 4 + jp] = (uint8_t)code;
+                            tsw[(16 * a + 4 * q + v) * 4 + jp] = (uint8_t)code;   // same value from all 16 lanes
                         }
                         // lane 4m + k: feature 16a + 4q + k, tokens 16 j + 4m .. +3
                         #pragma unroll
@@ -335,40 +344,54 @@ void tiled_gemm_kernel(KParams p) {
                 // only 32-token blocks that start inside the group's rows
                 const int col0 = p.offsets32[cur.g] + cur.pass * kRows + tok0;
                 const int fbase = 32 * uu;
+                const rsrc_t rhT = make_rsrc(p.hTq, (uint32_t)((size_t)I * p.ldT));
+                const rsrc_t rhTs = make_rsrc(p.hTs, (uint32_t)((size_t)I * (p.ldT / 32)));
                 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int fl = 8 * i + (lane >> 3), c = lane & 7;
-                    if (tok0 + 32 * (c >> 1) < cur.nrows) {
-                        const i32x4 d = *(const i32x4*)(tw + fl * kTStride + 16 * c);
-                        *(i32x4*)(p.hTq + (size_t)(fbase + fl) * p.ldT + col0 + 16 * c) = d;
-                    }
+                    const i32x4 d = *(const i32x4*)(tw + fl * kTStride + 16 * c);
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        d, rhT, tok0 + 32 * (c >> 1) < cur.nrows ? (uint32_t)((fbase + fl) * p.ldT + col0 + 16 * c) : kInvalid, 0, 0);
                 }
                 // scales: feature lane (< 32), 4 blocks -> bytes [col0/32, +4) of its hT scale row
-                if (lane < 32) {
-                    const uint32_t sw = *(const uint32_t*)(tsw + lane * 4);
-                    uint8_t* srow = p.hTs + (size_t)(fbase + lane) * (p.ldT / 32) + (col0 >> 5);
+                {
+                    const uint32_t sw = *(const uint32_t*)(tsw + (lane & 31) * 4);
+                    const uint32_t so = (uint32_t)((fbase + (lane & 31)) * (p.ldT / 32) + (col0 >> 5));
                     #pragma unroll
                     for (int b = 0; b < 4; ++b)
-                        if (tok0 + 32 * b < cur.nrows) srow[b] = (uint8_t)(sw >> (8 * b));
+                        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(sw >> (8 * b)), rhTs,
+                                                             (lane < 32 && tok0 + 32 * b < cur.nrows) ? so + b : kInvalid, 0, 0);
                 }
             }
             __syncthreads();                 // scratch free before the next prefetch lands in it
         } else {
+            // BF16 rows through LDS, 32 tokens at a time, so that each store
+            // instruction writes whole 128-byte lines (8 rows x 64 features)
             const int H = p.N;
+            uint8_t* ys = ring + ((s - 1) & 1) * S::Bytes + w * (32 * kYStride);
             #pragma unroll
-            for (int j = 0; j < kBT; ++j) {
-                const int tok = tok0 + 16 * j + r;
-                if (tok < cur.nrows) {
-                    uint16_t* yrow = p.y + (size_t)(cur.rbase + tok) * H + 64 * uu + 4 * q;
+            for (int c = 0; c < kBT / 2; ++c) {
+                #pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j = 2 * c + jj;
                     #pragma unroll
                     for (int t = 0; t < kAT; ++t) {
                         uint2 o;
                         o.x = bf16x2(acc[j][t][0], acc[j][t][1]);
                         o.y = bf16x2(acc[j][t][2], acc[j][t][3]);
-                        *(uint2*)(yrow + 16 * t) = o;
+                        *(uint2*)(ys + (16 * jj + r) * kYStride + (16 * t + 4 * q) * 2) = o;
                     }
                 }
+                #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 8 * i + (lane >> 3), k16 = lane & 7;
+                    const i32x4 d = *(const i32x4*)(ys + row * kYStride + 16 * k16);
+                    const int tok = tok0 + 32 * c + row;
+                    if (tok < cur.nrows)
+                        *(i32x4*)(p.y + (size_t)(cur.rbase + tok) * H + 64 * uu + 8 * k16) = d;
+                }
             }
+            __syncthreads();                 // scratch free before the next prefetch lands in it
         }
         cur = nxt;
         if (it + 2 < n_my) nxt = decode(p, pass_off, slot + (it + 2) * grid, wtiles, w, lane);
