@@ -8,7 +8,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVec = 8;                 // bf16 per thread per pass (16 bytes)
+constexpr int kSlotBatch = 8;           // slots whose rows are requested together
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// One workgroup per (token, 2048-column block). The token's slot rows are
+// read first (the same for every lane), then one 16-byte load per slot is
+// issued before any is used, each through a resource over that slot's row
+// (empty for slots that are not local, which then read zeros without a
+// branch); the sum runs in slot order in fp64.
 __global__ __launch_bounds__(kThreads)
 void combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ slot_row,
                     const float* __restrict__ row_w, int ks, int H, uint16_t* __restrict__ out) {
@@ -19,16 +27,29 @@ void combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ 
     #pragma unroll
     for (int i = 0; i < kVec; ++i) acc[i] = 0.0;
     const int32_t* sr = slot_row + (size_t)t * ks;
-    for (int j = 0; j < ks; ++j) {
-        const int r = sr[j];
-        if (r < 0) continue;
-        const double w = row_w ? (double)row_w[r] : 1.0;
-        const uint4 v = *(const uint4*)(y + (size_t)r * H + h0);
-        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+    for (int j0 = 0; j0 < ks; j0 += kSlotBatch) {
+        int r[kSlotBatch];
         #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i]     += (double)bf16_to_f32(p[i] & 0xFFFFu) * w;
-            acc[2 * i + 1] += (double)bf16_to_f32(p[i] >> 16) * w;
+        for (int j = 0; j < kSlotBatch; ++j)
+            r[j] = __builtin_amdgcn_readfirstlane(j0 + j < ks ? sr[j0 + j] : -1);
+        uint4 v[kSlotBatch];
+        #pragma unroll
+        for (int j = 0; j < kSlotBatch; ++j) {
+            const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(y) + (size_t)(r[j] < 0 ? 0 : r[j]) * H, 0, r[j] < 0 ? 0 : H * 2, 0x00020000);
+            const i32x4 d = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(h0 * 2), 0, 0);
+            v[j] = make_uint4((uint32_t)d[0], (uint32_t)d[1], (uint32_t)d[2], (uint32_t)d[3]);
+        }
+        #pragma unroll
+        for (int j = 0; j < kSlotBatch; ++j) {
+            if (r[j] < 0) continue;                // uniform: the same slot for every lane
+            const double w = row_w ? (double)row_w[r[j]] : 1.0;
+            const uint32_t pw[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i]     += (double)bf16_to_f32(pw[i] & 0xFFFFu) * w;
+                acc[2 * i + 1] += (double)bf16_to_f32(pw[i] >> 16) * w;
+            }
         }
     }
     uint4 o;

@@ -314,6 +314,54 @@ void permute_scan_kernel(int32_t* __restrict__ chunk_hist, int nchunks, int T, i
     }
 }
 
+// The same scan with the whole chunk histogram held in LDS (rows padded to
+// E_loc + 1 ints so that a wave reading one group's column hits 64 distinct
+// banks): one coalesced pass in, a per-group wave scan (each lane a run of
+// chunks), one coalesced pass out.
+constexpr int kLdsScanMaxBytes = 120 * 1024;
+
+__global__ __launch_bounds__(kScanThreads)
+void permute_scan_lds_kernel(int32_t* __restrict__ chunk_hist, int nchunks, int T, int E_loc, int s,
+                             int32_t* counts, int32_t* offsets, int32_t* offsets32) {
+    extern __shared__ int lds[];
+    constexpr int NW = kScanThreads / 64;
+    const int G = E_loc + s, ld = E_loc + 1;
+    int* h = lds;                                  // [nchunks][ld]
+    int* cnt = h + nchunks * ld;                   // [G]: counts, then offsets
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < nchunks * E_loc; i += kScanThreads) {
+        const int c = i / E_loc;
+        h[c * ld + (i - c * E_loc)] = chunk_hist[i];
+    }
+    __syncthreads();
+    const int per = (nchunks + 63) / 64;
+    const int c0 = min(nchunks, lane * per), c1 = min(nchunks, c0 + per);
+    for (int g = w; g < E_loc; g += NW) {
+        int sum = 0;
+        for (int c = c0; c < c1; ++c) sum += h[c * ld + g];
+        int inc = sum;                             // inclusive scan over the lanes' runs
+        #pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int a = __shfl_up(inc, d, 64);
+            if (lane >= d) inc += a;
+        }
+        int run = inc - sum;
+        for (int c = c0; c < c1; ++c) {
+            const int v = h[c * ld + g];
+            h[c * ld + g] = run;
+            run += v;
+        }
+        if (lane == 63) cnt[g] = inc;
+    }
+    if (s && tid == 0) cnt[E_loc] = T;
+    write_offsets(cnt, G, counts, offsets, offsets32);
+    __syncthreads();
+    for (int i = tid; i < nchunks * E_loc; i += kScanThreads) {
+        const int c = i / E_loc, g = i - c * E_loc;
+        chunk_hist[i] = cnt[g] + h[c * ld + g];
+    }
+}
+
 __global__ __launch_bounds__(kChunkThreads)
 void permute_scatter_kernel(const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
                             int T, int k, int e0, int E_loc, int s,
@@ -405,9 +453,14 @@ int moe_launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int 
                            (size_t)E_loc * 4, stream, topk_idx, Tk, e0, E_loc, chunk_hist);
         int P = 1;
         while (P * 2 <= kScanThreads / E_loc && P * 2 <= nchunks) P *= 2;
-        hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads),
-                           (size_t)(G + kScanThreads) * 4, stream, chunk_hist, nchunks, T,
-                           E_loc, s, P, counts, offsets, offsets32);
+        const size_t lds_scan = ((size_t)nchunks * (E_loc + 1) + G) * 4;
+        if (lds_scan <= (size_t)kLdsScanMaxBytes)
+            hipLaunchKernelGGL(permute_scan_lds_kernel, dim3(1), dim3(kScanThreads), lds_scan, stream,
+                               chunk_hist, (int)nchunks, T, E_loc, s, counts, offsets, offsets32);
+        else
+            hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads),
+                               (size_t)(G + kScanThreads) * 4, stream, chunk_hist, nchunks, T,
+                               E_loc, s, P, counts, offsets, offsets32);
         hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(kChunkThreads),
                            (size_t)(kChunkThreads / 64) * E_loc * 2 + 4, stream, topk_idx, topk_w,
                            T, k, e0, E_loc, s, chunk_hist, offsets, row_src, row_w, slot_row);
