@@ -58,7 +58,10 @@ struct Batch {
     int sB[NTT][KB];
 };
 
-template <int WFMT, int NTT>
+// CP: cache policy of the weight loads (kNonTemporal when no other pass of
+// the group reads the same weights, 0 when other passes do and can find them
+// in L2)
+template <int WFMT, int NTT, int CP>
 MOE_DEV void load_batch(Batch<WFMT, NTT>& b, int kt_first, int kt_end, int lane,
                         rsrc_t rw, rsrc_t rs, rsrc_t rx, rsrc_t rxs, const uint32_t (&xoff)[NTT],
                         const uint32_t (&xsoff)[NTT]) {
@@ -72,7 +75,7 @@ MOE_DEV void load_batch(Batch<WFMT, NTT>& b, int kt_first, int kt_end, int lane,
     for (int t = 0; t < 4; ++t) {
         const uint32_t soff = kt_first < kt_end ? (uint32_t)((((kt_first >> 2) * 4 + t) * 64 + lane) * 4)
                                                 : kInvalid;
-        sword[t] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, kNonTemporal);
+        sword[t] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, CP);
     }
     #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -82,9 +85,9 @@ MOE_DEV void load_batch(Batch<WFMT, NTT>& b, int kt_first, int kt_end, int lane,
         for (int t = 0; t < 4; ++t) {
             // FP4: lane's 16 B at lane*16; FP8: the two 16 B halves at lane*16 and 1024 + lane*16
             const uint32_t off = ok ? (uint32_t)((kt * 4 + t) * 64 * BPL + lane * 16) : kInvalid;
-            b.A[i][t].lo = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kNonTemporal);
+            b.A[i][t].lo = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, CP);
             if (WFMT == MFMA_FMT_FP8)
-                b.A[i][t].hi = __builtin_amdgcn_raw_buffer_load_b128(rw, off + (ok ? 1024u : 0u), 0, kNonTemporal);
+                b.A[i][t].hi = __builtin_amdgcn_raw_buffer_load_b128(rw, off + (ok ? 1024u : 0u), 0, CP);
             b.sA[i][t] = sword[t] >> (8 * (kt & 3));
         }
         #pragma unroll
@@ -121,8 +124,11 @@ MOE_DEV void mma_batch(const Batch<WFMT, NTT>& b, int ntt_active, f32x4 (&acc)[N
 
 // Persistent grid: each workgroup walks the work items item = pass * units + u
 // (every pass of 16*NTT rows of every group, times the 64-row weight units),
-// striding by the grid size; empty groups contribute no items.
-template <int WFMT, bool IS_W1, int NTT, int KW>
+// striding by the grid size; empty groups contribute no items. CP is the
+// cache policy of the weight loads: non-temporal when groups mostly fit one
+// pass (each weight byte is read once), cached when a group's passes re-read
+// its units and can find them in L2.
+template <int WFMT, bool IS_W1, int NTT, int KW, int CP>
 __global__ __launch_bounds__(64 * KW, NTT == 1 ? 4 : 2)   // waves per SIMD: 4 (128 VGPRs) for one token tile
 void grouped_gemm_kernel(KParams p) {
     constexpr int NT = 64 * KW;
@@ -179,7 +185,7 @@ void grouped_gemm_kernel(KParams p) {
 
         for (int ktb = kt0; ktb < kt1; ktb += KB) {
             Batch<WFMT, NTT> b;
-            load_batch<WFMT, NTT>(b, ktb, kt1, lane, rw, rs, rx, rxs, xoff, xsoff);
+            load_batch<WFMT, NTT, CP>(b, ktb, kt1, lane, rw, rs, rx, rxs, xoff, xsoff);
             mma_batch<WFMT, NTT>(b, ntt_active, acc);
         }
 
@@ -293,9 +299,9 @@ void grouped_gemm_kernel(KParams p) {
     }
 }
 
-template <int WFMT, bool IS_W1, int NTT, int KW>
+template <int WFMT, bool IS_W1, int NTT, int KW, int CP>
 int launch(const KParams& p, long max_items, hipStream_t stream) {
-    auto kern = grouped_gemm_kernel<WFMT, IS_W1, NTT, KW>;
+    auto kern = grouped_gemm_kernel<WFMT, IS_W1, NTT, KW, CP>;
     const size_t lds = (size_t)((p.G + 4) & ~3) * 4 + (size_t)(KW / 2) * NTT * 1024 * 4 +
                        (IS_W1 ? (size_t)16 * NTT * 33 * 4 : 0);
     int per_cu = 0;
@@ -306,11 +312,14 @@ int launch(const KParams& p, long max_items, hipStream_t stream) {
     return (int)hipGetLastError();
 }
 
-template <int WFMT, bool IS_W1, int NTT>
+// 16 K-split waves only with one token tile: 1024-thread workgroups get 128
+// VGPRs, too few for more
+template <int WFMT, bool IS_W1, int NTT, int CP>
 int launch_kw(const KParams& p, int kw, long max_items, hipStream_t stream) {
-    if (kw >= 16) return launch<WFMT, IS_W1, NTT, 16>(p, max_items, stream);
-    if (kw >= 8) return launch<WFMT, IS_W1, NTT, 8>(p, max_items, stream);
-    return launch<WFMT, IS_W1, NTT, 4>(p, max_items, stream);
+    if constexpr (NTT == 1)
+        if (kw >= 16) return launch<WFMT, IS_W1, NTT, 16, CP>(p, max_items, stream);
+    if (kw >= 8) return launch<WFMT, IS_W1, NTT, 8, CP>(p, max_items, stream);
+    return launch<WFMT, IS_W1, NTT, 4, CP>(p, max_items, stream);
 }
 
 constexpr int kTiledMinRows = 96;   // expected rows per group from which the tiled kernel runs
@@ -338,16 +347,21 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     int kw = items * 4 >= 2048 ? 4 : (items * 8 >= 2048 ? 8 : 16);
     kw = std::min(kw, std::max(4, p.kt));       // no more waves than K-tiles
     if (ntt > 1) kw = std::min(kw, 8);          // 1024-thread workgroups get 128 VGPRs: too few
+    // weights stay in L2 (cached loads) when a typical group needs more than
+    // one pass, so that its other passes re-read them there; otherwise they
+    // stream through non-temporally
+    const bool reread = ntt > 1 || avg >= rpp;
     const bool fp4 = a.fmt == MOE_FMT_MXFP4;
-#define MOE_GEMM_CASE(N)                                                                          \
-    if (ntt == N)                                                                                 \
-        return fp4 ? launch_kw<MFMA_FMT_FP4, IS_W1, N>(p, kw, max_items, stream)                  \
-                   : launch_kw<MFMA_FMT_FP8, IS_W1, N>(p, kw, max_items, stream);
-    MOE_GEMM_CASE(1)
-    MOE_GEMM_CASE(2)
-    MOE_GEMM_CASE(4)
+#define MOE_GEMM_CASE(N, CP)                                                                      \
+    return fp4 ? launch_kw<MFMA_FMT_FP4, IS_W1, N, CP>(p, kw, max_items, stream)                  \
+               : launch_kw<MFMA_FMT_FP8, IS_W1, N, CP>(p, kw, max_items, stream);
+    if (ntt == 1) {
+        if (reread) { MOE_GEMM_CASE(1, 0) }
+        MOE_GEMM_CASE(1, kNonTemporal)
+    }
+    if (ntt == 2) { MOE_GEMM_CASE(2, 0) }
+    MOE_GEMM_CASE(4, 0)
 #undef MOE_GEMM_CASE
-    return -1;
 }
 
 }  // namespace

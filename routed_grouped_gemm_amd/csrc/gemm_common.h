@@ -26,6 +26,9 @@ struct KParams {
     int ceil_rule, transpose, use_w;
     uint8_t* hq; uint8_t* hs; uint8_t* hTq; uint8_t* hTs; int ldT;
     uint16_t* y;
+    const uint32_t* bst;              // tiled kernels: activation scales per K-tile and pass
+    uint32_t bst_bytes;
+    int npass;                        // passes the scale tiles are laid out for
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;

@@ -23,6 +23,10 @@
 //    (8 rows per instruction), their 16-byte chunks XOR-swizzled by row so
 //    that the B operand reads (16 rows, one chunk each) hit 16 distinct bank
 //    groups. Rows past the group's end read as zero.
+//  - The token rows' E8M0 words are read from scale tiles that a small kernel
+//    writes first: per K-tile and 256-row pass, the 256 rows' 4-byte words
+//    side by side (zero past the group's end), so one 1 KiB load stages them
+//    instead of 256 scattered 4-byte reads.
 //  - One barrier per K-tile. The loop runs over the workgroup's whole
 //    sequence of (item, K-tile) steps, so the next item's first K-tile is in
 //    flight while an item's epilogue runs.
@@ -79,7 +83,7 @@ struct Ctx {
     int g, pass, wt, rbase, nrows;
     const uint8_t* wgrp;                    // prepacked group base
     uint32_t xoff[4];                       // staged token rows 32 w + 8 i + lane / 8: byte offset of the row
-    uint32_t xsoff;                         // E8M0 row 64 w + lane (waves 0-3)
+    int pidx;                               // pass index over all groups (scale tile column)
 };
 
 MOE_DEV Ctx decode(const KParams& p, const int* pass_off, int item, int wtiles, int w, int lane) {
@@ -92,6 +96,7 @@ MOE_DEV Ctx decode(const KParams& p, const int* pass_off, int item, int wtiles, 
         if (pass_off[mid] <= pg) glo = mid; else ghi = mid;
     }
     c.g = __builtin_amdgcn_readfirstlane(glo);
+    c.pidx = pg;
     c.pass = pg - __builtin_amdgcn_readfirstlane(pass_off[c.g]);
     const int n_g = p.counts[c.g];
     c.rbase = p.offsets[c.g] + c.pass * kRows;
@@ -112,22 +117,17 @@ MOE_DEV Ctx decode(const KParams& p, const int* pass_off, int item, int wtiles, 
         const uint32_t xr = src_row(row);
         c.xoff[i] = row < c.nrows ? xr * (uint32_t)p.K : kInvalid;
     }
-    {
-        const int row = 64 * w + lane;
-        const uint32_t xr = src_row(row);
-        c.xsoff = (w < 4 && row < c.nrows) ? xr * (uint32_t)(p.K / 32) : kInvalid;
-    }
     return c;
 }
 
 // Stage K-tile kt of an item into one LDS stage with buffer loads that write
 // LDS directly (each lane's bytes land at the wave's LDS base + size * lane).
 // Wave w stages token rows [32w, 32w + 32) (lane l of instruction i: row
-// 32w + 8i + l/8, LDS slot l%8 holding chunk (l%8) ^ bswz(row)), the E8M0
-// words of token rows [64w, 64w + 64) (waves 0-3), and the weight tiles 2w,
-// 2w+1 of the four units with their E8M0 words (copied verbatim). With
-// valid == false every load is out of range: zeros land and no memory is
-// read.
+// 32w + 8i + l/8, LDS slot l%8 holding chunk (l%8) ^ bswz(row)) and the
+// weight tiles 2w, 2w+1 of the four units with their E8M0 words (copied
+// verbatim); wave 0 also stages the E8M0 words of the 256 token rows (one
+// 1 KiB scale tile). With valid == false every load is out of range: zeros
+// land and no memory is read.
 template <int WFMT>
 MOE_DEV void stage_all(const KParams& p, rsrc_t rx, rsrc_t rxs, const Ctx& c, int kt, bool valid,
                        uint8_t* st, int w, int lane) {
@@ -140,10 +140,10 @@ MOE_DEV void stage_all(const KParams& p, rsrc_t rx, rsrc_t rxs, const Ctx& c, in
         const uint32_t o = (xo == kInvalid || !valid) ? kInvalid : xo + (uint32_t)(kt * 128 + 16 * chunk);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(st + S::B + (32 * w + 8 * i) * 128), 16, o, 0, 0, 0);
     }
-    if (w < 4)
+    if (w == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rxs, (lds_void_t*)(st + S::BS + 256 * w), 4,
-            (c.xsoff == kInvalid || !valid) ? kInvalid : c.xsoff + (uint32_t)(kt * 4), 0, 0, 0);
+            rxs, (lds_void_t*)(st + S::BS), 16,
+            valid ? (uint32_t)((kt * p.npass + c.pidx) * (kRows * 4) + lane * 16) : kInvalid, 0, 0, 0);
     #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int T = 2 * w + i;                // weight tile within the workgroup tile
@@ -204,7 +204,7 @@ void tiled_gemm_kernel(KParams p) {
     const int total = n_my * nkt;
 
     const rsrc_t rx = make_rsrc(p.aq, p.aq_bytes);
-    const rsrc_t rxs = make_rsrc(p.as, p.as_bytes);
+    const rsrc_t rxs = make_rsrc(p.bst, p.bst_bytes);
 
     Ctx cur = decode(p, pass_off, slot, wtiles, w, lane);
     Ctx nxt = n_my > 1 ? decode(p, pass_off, slot + grid, wtiles, w, lane) : cur;
@@ -224,47 +224,49 @@ void tiled_gemm_kernel(KParams p) {
     }
 
     f32x4 acc[kBT][kAT];
+    // one K-tile of the item: step s of the workgroup's sequence
+    auto kstep = [&](int kt, int s) {
+        // prefetch step s + 1 into the other stage (zeros past the last step)
+        {
+            const bool same = kt + 1 < nkt;
+            stage_all<WFMT>(p, rx, rxs, same ? cur : nxt, same ? kt + 1 : 0, s + 1 < total,
+                            ring + ((s + 1) & 1) * S::Bytes, w, lane);
+        }
+        const uint8_t* st = ring + (s & 1) * S::Bytes;
+        // this wave's 4 weight tiles stay in registers for the K-tile; its
+        // 8 token tiles stream from LDS, each against all 4
+        const int ash = 8 * (kt & 3);
+        i32x8 A[kAT];
+        int sa[kAT];
+        #pragma unroll
+        for (int t = 0; t < kAT; ++t) {
+            const int T = wi * kAT + t;
+            const uint8_t* ap = st + S::A + T * 64 * S::kBPL + lane * 16;
+            const i32x4 alo = *(const i32x4*)ap;
+            const i32x4 ahi = WFMT == MFMA_FMT_FP8 ? *(const i32x4*)(ap + 1024) : i32x4{0, 0, 0, 0};
+            A[t] = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
+            sa[t] = ((const int*)(st + S::AS))[T * 64 + lane] >> ash;
+        }
+        #pragma unroll
+        for (int j = 0; j < kBT; ++j) {
+            const i32x4 blo = *(const i32x4*)(st + boff_lo[j]);
+            const i32x4 bhi = *(const i32x4*)(st + boff_hi[j]);
+            const i32x8 B = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const int bs = ((const int*)(st + S::BS))[ti * 128 + 16 * j + r] >> (8 * q);
+            #pragma unroll
+            for (int t = 0; t < kAT; ++t)
+                acc[j][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, 0, 0>(A[t], B, acc[j][t], sa[t], bs);
+        }
+        __builtin_amdgcn_s_waitcnt(0);       // the next step's operands have landed
+        __syncthreads();
+    };
     for (int it = 0; it < n_my; ++it) {
+        int s = it * nkt;
         #pragma unroll
         for (int j = 0; j < kBT; ++j)
             #pragma unroll
             for (int t = 0; t < kAT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        int s = it * nkt;
-        for (int kt = 0; kt < nkt; ++kt, ++s) {
-            // prefetch step s + 1 into the other stage (zeros past the last step)
-            {
-                const bool same = kt + 1 < nkt;
-                stage_all<WFMT>(p, rx, rxs, same ? cur : nxt, same ? kt + 1 : 0, s + 1 < total,
-                                ring + ((s + 1) & 1) * S::Bytes, w, lane);
-            }
-            const uint8_t* st = ring + (s & 1) * S::Bytes;
-            // this wave's 4 weight tiles stay in registers for the K-tile; its
-            // 8 token tiles stream from LDS, each against all 4
-            const int ash = 8 * (kt & 3);
-            i32x8 A[kAT];
-            int sa[kAT];
-            #pragma unroll
-            for (int t = 0; t < kAT; ++t) {
-                const int T = wi * kAT + t;
-                const uint8_t* ap = st + S::A + T * 64 * S::kBPL + lane * 16;
-                const i32x4 alo = *(const i32x4*)ap;
-                const i32x4 ahi = WFMT == MFMA_FMT_FP8 ? *(const i32x4*)(ap + 1024) : i32x4{0, 0, 0, 0};
-                A[t] = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
-                sa[t] = ((const int*)(st + S::AS))[T * 64 + lane] >> ash;
-            }
-            #pragma unroll
-            for (int j = 0; j < kBT; ++j) {
-                const i32x4 blo = *(const i32x4*)(st + boff_lo[j]);
-                const i32x4 bhi = *(const i32x4*)(st + boff_hi[j]);
-                const i32x8 B = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
-                const int bs = ((const int*)(st + S::BS))[ti * 128 + 16 * j + r] >> (8 * q);
-                #pragma unroll
-                for (int t = 0; t < kAT; ++t)
-                    acc[j][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, 0, 0>(A[t], B, acc[j][t], sa[t], bs);
-            }
-            __builtin_amdgcn_s_waitcnt(0);       // the next step's operands have landed
-            __syncthreads();
-        }
+        for (int kt = 0; kt < nkt; ++kt, ++s) kstep(kt, s);
 
         // ---------------------------------------------------- epilogue
         const int tok0 = ti * (kBT * 16);
@@ -398,6 +400,42 @@ void tiled_gemm_kernel(KParams p) {
     }
 }
 
+// Scale tiles: out[(kt * npass + pass) * 256 + i] = the 4 E8M0 bytes of
+// K-tile kt of row i of pass `pass` (passes numbered over all groups, as the
+// GEMM numbers them), 0 for rows past the group's end. One workgroup per pass
+// and 4 K-tiles; passes past the total are left unwritten (the GEMM never
+// reads them).
+__global__ __launch_bounds__(kRows)
+void scale_tiles_kernel(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int G,
+                        const int32_t* __restrict__ row_src, const uint8_t* as, uint32_t as_bytes,
+                        int K, int npass, uint32_t* __restrict__ out) {
+    extern __shared__ int pass_off[];                                   // [G + 1]
+    const int tid = threadIdx.x;
+    if (tid < 64) pass_prefix(counts, G, kRows, tid, pass_off);
+    __syncthreads();
+    const int b = blockIdx.x;
+    if (b >= pass_off[G]) return;
+    int glo = 0, ghi = G;                   // largest g with pass_off[g] <= b
+    while (ghi - glo > 1) {
+        const int mid = (glo + ghi) >> 1;
+        if (pass_off[mid] <= b) glo = mid; else ghi = mid;
+    }
+    const int row = (b - pass_off[glo]) * kRows + tid;
+    const bool valid = row < counts[glo];
+    const int r = offsets[glo] + row;
+    const uint32_t src = valid ? (uint32_t)(row_src ? row_src[r] : r) : 0u;
+    const rsrc_t rs = make_rsrc(as, valid ? as_bytes : 0u);
+    const int nkt = K / 128, kt0 = 4 * blockIdx.y;
+    const uint32_t base = src * (uint32_t)(K / 32);
+    uint32_t v[4];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i)
+        v[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, base + 4u * (kt0 + i), 0, 0);
+    #pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (kt0 + i < nkt) out[((size_t)(kt0 + i) * npass + b) * kRows + tid] = v[i];
+}
+
 template <int WFMT, bool IS_W1>
 int launch_tiled(const KParams& p, int R_max, hipStream_t stream) {
     auto kern = tiled_gemm_kernel<WFMT, IS_W1>;
@@ -413,18 +451,40 @@ int launch_tiled(const KParams& p, int R_max, hipStream_t stream) {
     return (int)hipGetLastError();
 }
 
+// The activation scales as scale tiles in the workspace; fills p.bst.
+int launch_scale_tiles(const GemmArgs& a, KParams& p, hipStream_t stream) {
+    const int npass = a.R_max / kRows + a.G;
+    const size_t need = moe_tiled_scale_bytes(a.R_max, a.G, a.K);
+    if (!a.ws || a.ws_bytes < need || need > 0x7FFFFFFFu) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(scale_tiles_kernel, dim3((unsigned)npass, (unsigned)(a.K / 128 + 3) / 4), dim3(kRows),
+                       (size_t)(a.G + 1) * 4, stream,
+                       a.counts, a.offsets, a.G, a.row_src, a.as, p.as_bytes, a.K, npass, (uint32_t*)a.ws);
+    p.bst = (const uint32_t*)a.ws;
+    p.bst_bytes = (uint32_t)need;
+    p.npass = npass;
+    return (int)hipGetLastError();
+}
+
 }  // namespace
+
+// passes never exceed R_max / 256 + G (each group adds at most one partial
+// pass); one 4-byte word per row, pass and K-tile
+size_t moe_tiled_scale_bytes(int R_max, int G, int K) {
+    return ((size_t)R_max / kRows + G) * kRows * (size_t)(K / 128) * 4;
+}
 
 int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream) {
     if (a.G == 0 || a.R_max == 0) return 0;
-    const KParams p = make_params(a, true);
+    KParams p = make_params(a, true);
+    if (int e = launch_scale_tiles(a, p, stream)) return e;
     return a.fmt == MOE_FMT_MXFP4 ? launch_tiled<MFMA_FMT_FP4, true>(p, a.R_max, stream)
                                   : launch_tiled<MFMA_FMT_FP8, true>(p, a.R_max, stream);
 }
 
 int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream) {
     if (a.G == 0 || a.R_max == 0) return 0;
-    const KParams p = make_params(a, false);
+    KParams p = make_params(a, false);
+    if (int e = launch_scale_tiles(a, p, stream)) return e;
     return a.fmt == MOE_FMT_MXFP4 ? launch_tiled<MFMA_FMT_FP4, false>(p, a.R_max, stream)
                                   : launch_tiled<MFMA_FMT_FP8, false>(p, a.R_max, stream);
 }

@@ -159,8 +159,9 @@ MOE_EXPORT int32_t moe_transposed_ld(int32_t R_max, int32_t G) {
 }
 
 MOE_EXPORT size_t moe_grouped_workspace_size(int32_t R_max, int32_t G, int32_t N, int32_t K) {
-    (void)R_max; (void)G; (void)N; (void)K;
-    return 0;
+    (void)N;
+    if (R_max < 0 || G < 1 || K <= 0 || K % 128) return 0;
+    return moe_tiled_scale_bytes(R_max, G, K);
 }
 
 static int32_t fill_gemm_args(GemmArgs& a, const moe_weights* w, const moe_weights* wsh, int G,
@@ -212,6 +213,7 @@ static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shar
     a.aq = xq_perm; a.as = xs_perm; a.row_src = row_src; a.x_rows = x_rows;
     a.R_max = R_max; a.rows_hint = rows_hint; a.active_hint = active_hint; a.flags = flags;
     a.hq = hq; a.hs = hs; a.hTq = hTq; a.hTs = hTs; a.ldT = moe_transposed_ld(R_max, G);
+    a.ws = ws; a.ws_bytes = ws_bytes;
     return hip_status(moe_launch_grouped_w1(a, stream));
 }
 
@@ -246,6 +248,7 @@ static int32_t grouped_w2_impl(const moe_weights* w2, const moe_weights* w2_shar
     if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
     a.counts = counts; a.offsets = offsets; a.aq = hq; a.as = hs; a.x_rows = R_max; a.R_max = R_max;
     a.rows_hint = rows_hint; a.active_hint = active_hint; a.y = y;
+    a.ws = ws; a.ws_bytes = ws_bytes;
     return hip_status(moe_launch_grouped_w2(a, stream));
 }
 

@@ -55,12 +55,16 @@ struct GemmArgs {
     uint8_t* hq; uint8_t* hs;    // W1 outputs
     uint8_t* hTq; uint8_t* hTs; int ldT;
     uint16_t* y;                 // W2 output
+    void* ws; size_t ws_bytes;   // workspace (moe_grouped_workspace_size bytes)
 };
 int moe_launch_grouped_w1(const GemmArgs& a, hipStream_t stream);
 int moe_launch_grouped_w2(const GemmArgs& a, hipStream_t stream);
 // LDS-tiled variants for groups with many rows (256 x 256 workgroup tiles)
 int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream);
 int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream);
+// Workspace of the tiled kernels: the activation scales rearranged per K-tile
+// and 256-row pass (see gemm_tiled.hip).
+size_t moe_tiled_scale_bytes(int R_max, int G, int K);
 
 int moe_launch_combine(const uint16_t* y, const int32_t* slot_row, const float* row_w, int T,
                        int ks, int H, uint16_t* out, hipStream_t stream);
