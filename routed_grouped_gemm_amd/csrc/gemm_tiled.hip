@@ -176,8 +176,6 @@ MOE_DEV uint32_t quad_byte_transpose(uint32_t x, int lane) {
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                  // lo bytes 0,1 then hi bytes 0,1
 }
 
-MOE_DEV uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
-
 template <int WFMT, bool IS_W1>
 __global__ __launch_bounds__(kThreads, 1)
 void tiled_gemm_kernel(KParams p) {
@@ -291,18 +289,17 @@ void tiled_gemm_kernel(KParams p) {
                     const int tok = tok0 + 16 * j + r;
                     // rows past the item have zero token rows, so zero sums and h = 0
                     const float wgt = p.use_w ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw_w, (uint32_t)(tok * 4), 0, 0)) : 1.0f;
-                    uint32_t am = 0;
+                    float amf = 0.f;
                     #pragma unroll
                     for (int a = 0; a < 2; ++a)
                         #pragma unroll
                         for (int v = 0; v < 4; ++v) {
                             const float hv = silu_fast(acc[j][a][v]) * acc[j][a + 2][v] * wgt;
                             h[jj][a][v] = hv;
-                            am = max(am, abs_bits(hv));
+                            amf = fmaxf(amf, fabsf(hv));
                         }
                     // the unit's 32 features of this token: 4 lanes (q) x 8 values
-                    am = max(am, (uint32_t)__shfl_xor((int)am, 16, 64));
-                    am = max(am, (uint32_t)__shfl_xor((int)am, 32, 64));
+                    const uint32_t am = rows4_umax(__float_as_uint(amf));
                     const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
                     const float inv = inv_scale(code);
                     // rows past the item fall outside the resources' range: dropped
@@ -316,20 +313,23 @@ void tiled_gemm_kernel(KParams p) {
                 }
                 if (p.transpose) {
                     // 32-token block jp of this wave (tokens tok0 + 32 jp + [0, 32)):
-                    // per feature, amax over its 16 lanes x 2 tiles; codes go to the
-                    // wave's LDS staging as [feature][token], 4 tokens per dword
+                    // per feature, amax over its 16 lanes x 2 tiles; the codes go
+                    // to the wave's LDS staging as [block][feature] bytes, the 4
+                    // features of a lane in one dword (written by lane r = 0)
                     #pragma unroll
                     for (int a = 0; a < 2; ++a) {
                         float sc[2][4];
+                        uint32_t cw = 0;
                         #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            const uint32_t am = row16_umax(max(abs_bits(h[0][a][v]), abs_bits(h[1][a][v])));
+                            const uint32_t am = row16_umax(__float_as_uint(fmaxf(fabsf(h[0][a][v]), fabsf(h[1][a][v]))));
                             const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
                             const float inv = inv_scale(code);
                             sc[0][v] = h[0][a][v] * inv;
                             sc[1][v] = h[1][a][v] * inv;
-                            tsw[(16 * a + 4 * q + v) * 4 + jp] = (uint8_t)code;   // same value from all 16 lanes
+                            cw |= code << (8 * v);
                         }
+                        if (r == 0) *(uint32_t*)(tsw + jp * 32 + 16 * a + 4 * q) = cw;
                         // lane 4m + k: feature 16a + 4q + k, tokens 16 j + 4m .. +3
                         #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
@@ -357,11 +357,10 @@ void tiled_gemm_kernel(KParams p) {
                 }
                 // scales: feature lane (< 32), 4 blocks -> bytes [col0/32, +4) of its hT scale row
                 {
-                    const uint32_t sw = *(const uint32_t*)(tsw + (lane & 31) * 4);
                     const uint32_t so = (uint32_t)((fbase + (lane & 31)) * (p.ldT / 32) + (col0 >> 5));
                     #pragma unroll
                     for (int b = 0; b < 4; ++b)
-                        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(sw >> (8 * b)), rhTs,
+                        __builtin_amdgcn_raw_buffer_store_b8(tsw[b * 32 + (lane & 31)], rhTs,
                                                              (lane < 32 && tok0 + 32 * b < cur.nrows) ? so + b : kInvalid, 0, 0);
                 }
             }

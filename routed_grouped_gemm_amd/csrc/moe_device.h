@@ -71,7 +71,7 @@ template <int EMAX, uint32_t MAXMANT>
 MOE_DEV uint32_t mx_scale_code(float amax, bool ceil_rule) {
     uint32_t u = __float_as_uint(amax);
     int e32 = (int)(u >> 23);                      // biased exponent; 0 for zero/subnormal
-    if (e32 == 0) return 0u;
+    // e32 == 0 gives code <= 1 - EMAX <= 0, clamped to 0 below (no branch)
     int code = e32 - EMAX;                         // (e32 - 127 - EMAX) + 127
     if (ceil_rule) {
         // amax <= max_finite * 2^(e-emax) iff its mantissa <= the max element's mantissa
@@ -197,6 +197,16 @@ MOE_DEV uint32_t row16_umax(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_HALF_MIRROR, 0xF, 0xF, true));
     v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_MIRROR, 0xF, 0xF, true));
     return v;
+}
+
+// Unsigned max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the same lane
+// of each row of the wave), returned to all four: row-pair swaps of the value
+// with itself.
+MOE_DEV uint32_t rows4_umax(uint32_t v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(b[0], b[1]);
 }
 
 MOE_DEV float row16_sum(float v) {
