@@ -67,20 +67,24 @@ MOE_DEV void write_offsets(int* lds_counts, int G, int32_t* counts, int32_t* off
 }
 
 // One wave: rank of each lane's group among the lanes below it with the same
-// group, and the per-group lane count written by the group's leader lane.
-MOE_DEV int wave_match_rank(int g, int lane, uint16_t* wave_cnt /* [E_loc] of this wave */) {
-    uint64_t rem = __ballot(g >= 0);
-    int rank = 0;
-    while (rem) {
-        int leader = __ffsll((unsigned long long)rem) - 1;
-        int lg = __shfl(g, leader, 64);
-        uint64_t m = __ballot(g == lg) & rem;
-        if (g == lg) rank = __popcll(m & lanemask_lt(lane));
-        if (lane == leader) wave_cnt[lg] = (uint16_t)__popcll(m);
-        rem &= ~m;
+// group, and the per-group lane count written by the group's lowest lane.
+// The lanes sharing a lane's group are found with one ballot per bit of the
+// group index (gbits bits), in constant time however many groups the wave
+// holds. Lanes with g < 0 take no part; their rank is meaningless.
+MOE_DEV int wave_match_rank(int g, int lane, int gbits, uint16_t* wave_cnt /* [E_loc] of this wave */) {
+    uint64_t same = __ballot(g >= 0);
+    for (int b = 0; b < gbits; ++b) {
+        const bool bit = (g >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
     }
+    const int rank = __popcll(same & lanemask_lt(lane));
+    if (g >= 0 && rank == 0) wave_cnt[g] = (uint16_t)__popcll(same);
     return rank;
 }
+
+// Bits of a group index in [0, E_loc).
+__host__ __device__ inline int group_bits(int E_loc) { return E_loc > 1 ? 32 - __builtin_clz((unsigned)(E_loc - 1)) : 0; }
 
 // Per-wave lane counts of one chunk -> per-wave exclusive prefix (in place),
 // and the chunk totals in tot (if non-null).
@@ -139,6 +143,7 @@ MOE_DEV void permute_in_block(IdxF idx_of, WF w_of, int T, int k, int e0, int E_
     uint16_t* cnt = (uint16_t*)(base + G);     // [NW][E_loc]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int Tk = T * k, ks = k + s;
+    const int gbits = group_bits(E_loc);
 
     for (int g = tid; g < G; g += NT) hist[g] = 0;
     __syncthreads();
@@ -162,7 +167,7 @@ MOE_DEV void permute_in_block(IdxF idx_of, WF w_of, int T, int k, int e0, int E_
             int gg = idx_of(a) - e0;
             if (gg >= 0 && gg < E_loc) g = gg;
         }
-        const int rank = wave_match_rank(g, lane, cnt + w * E_loc);
+        const int rank = wave_match_rank(g, lane, gbits, cnt + w * E_loc);
         __syncthreads();
         scan_waves<NW>(cnt, E_loc, tmp);
         __syncthreads();
@@ -178,13 +183,13 @@ MOE_DEV void permute_in_block(IdxF idx_of, WF w_of, int T, int k, int e0, int E_
 }
 
 // ---- single-workgroup path ---------------------------------------------
-__global__ __launch_bounds__(kChunkThreads)
+__global__ __launch_bounds__(kFusedThreads)
 void permute_small_kernel(const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
                           int T, int k, int e0, int E_loc, int s,
                           int32_t* counts, int32_t* offsets, int32_t* offsets32,
                           int32_t* row_src, float* row_w, int32_t* slot_row) {
     extern __shared__ int lds[];
-    permute_in_block<kChunkThreads / 64>(
+    permute_in_block<kFusedThreads / 64>(
         [&](int a) { return topk_idx[a]; }, [&](int a) { return topk_w[a]; },
         T, k, e0, E_loc, s, counts, offsets, offsets32, row_src, row_w, slot_row, lds);
 }
@@ -372,6 +377,7 @@ void permute_scatter_kernel(const int32_t* __restrict__ topk_idx, const float* _
     uint16_t* cnt = (uint16_t*)lds;          // [NW][E_loc]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = blockIdx.x;
     const int Tk = T * k, ks = k + s;
+    const int gbits = group_bits(E_loc);
     for (int i = tid; i < NW * E_loc; i += kChunkThreads) cnt[i] = 0;
     __syncthreads();
     int a = c * kChunkThreads + tid;
@@ -380,7 +386,7 @@ void permute_scatter_kernel(const int32_t* __restrict__ topk_idx, const float* _
         int gg = topk_idx[a] - e0;
         if (gg >= 0 && gg < E_loc) g = gg;
     }
-    int rank = wave_match_rank(g, lane, cnt + w * E_loc);
+    int rank = wave_match_rank(g, lane, gbits, cnt + w * E_loc);
     __syncthreads();
     scan_waves<NW>(cnt, E_loc, nullptr);
     __syncthreads();
@@ -442,8 +448,8 @@ int moe_launch_permute(const int32_t* topk_idx, const float* topk_w, int T, int 
     const int Tk = T * k;
     hipError_t e;
     if (Tk <= kSmallMax) {
-        size_t lds = block_lds_ints(kChunkThreads / 64, G, E_loc) * 4;
-        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kChunkThreads), lds, stream,
+        size_t lds = block_lds_ints(kFusedThreads / 64, G, E_loc) * 4;
+        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kFusedThreads), lds, stream,
                            topk_idx, topk_w, T, k, e0, E_loc, s, counts, offsets, offsets32,
                            row_src, row_w, slot_row);
     } else {
