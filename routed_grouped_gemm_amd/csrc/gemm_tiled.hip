@@ -367,7 +367,9 @@ void tiled_gemm_kernel(KParams p) {
             __syncthreads();                 // scratch free before the next prefetch lands in it
         } else {
             // BF16 rows through LDS, 32 tokens at a time, so that each store
-            // instruction writes whole 128-byte lines (8 rows x 64 features)
+            // instruction writes whole 128-byte lines (8 rows x 64 features),
+            // streamed out non-temporally: the burst of stores at the end of
+            // an item then drains sooner, before the next K-tile's wait
             const int H = p.N;
             uint8_t* ys = ring + ((s - 1) & 1) * S::Bytes + w * (32 * kYStride);
             #pragma unroll
@@ -389,7 +391,7 @@ void tiled_gemm_kernel(KParams p) {
                     const i32x4 d = *(const i32x4*)(ys + row * kYStride + 16 * k16);
                     const int tok = tok0 + 32 * c + row;
                     if (tok < cur.nrows)
-                        *(i32x4*)(p.y + (size_t)(cur.rbase + tok) * H + 64 * uu + 8 * k16) = d;
+                        __builtin_nontemporal_store(d, (i32x4*)(p.y + (size_t)(cur.rbase + tok) * H + 64 * uu + 8 * k16));
                 }
             }
             __syncthreads();                 // scratch free before the next prefetch lands in it
