@@ -24,6 +24,7 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "gemm_common.h"
+#include "permute_block.h"
 
 namespace {
 
@@ -127,8 +128,11 @@ MOE_DEV void mma_batch(const Batch<WFMT, NTT>& b, int ntt_active, f32x4 (&acc)[N
 // striding by the grid size; empty groups contribute no items. CP is the
 // cache policy of the weight loads: non-temporal when groups mostly fit one
 // pass (each weight byte is read once), cached when a group's passes re-read
-// its units and can find them in L2.
-template <int WFMT, bool IS_W1, int NTT, int KW, int CP>
+// its units and can find them in L2. RT (W1 at decode shapes): 0, or the
+// lanes per token with which every workgroup first routes and groups the
+// tokens itself in LDS (one launch fewer per layer); workgroup 0 also writes
+// the routing results to device memory for W2 and the combine.
+template <int WFMT, bool IS_W1, int NTT, int KW, int CP, int RT = 0>
 __global__ __launch_bounds__(64 * KW, NTT == 1 ? 4 : 2)   // waves per SIMD: 4 (128 VGPRs) for one token tile
 void grouped_gemm_kernel(KParams p) {
     constexpr int NT = 64 * KW;
@@ -141,7 +145,47 @@ void grouped_gemm_kernel(KParams p) {
     float* hbuf = red + (KW / 2) * NTT * 1024;          // [16*NTT][33]  (W1)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (w == 0) pass_prefix(p.counts, G, rows_per_pass, lane, pass_off);
+    // group sizes, offsets, source rows and routing weights: the inputs, or
+    // the LDS tables this workgroup builds from the logits
+    const int32_t* cnt_tab = p.counts;
+    const int32_t* off_tab = p.offsets;
+    const int32_t* rsrc_tab = p.row_src;
+    const float* roww_tab = p.row_w;
+    if constexpr (RT != 0) {
+        const int Tk = p.T * p.k_top, s_sh = G - p.E_loc, ks = p.k_top + s_sh;
+        int* sidx = (int*)(hbuf + (IS_W1 ? 16 * NTT * 33 : 0));    // [T*k]
+        float* sw = (float*)(sidx + Tk);                          // [T*k]
+        int* cnt_l = (int*)(sw + Tk);                             // [G]
+        int* off_l = cnt_l + G;                                   // [G + 1]
+        int* off32_l = off_l + G + 1;                             // [G + 1]
+        int* rsrc_l = off32_l + G + 1;                            // [R_max]
+        float* roww_l = (float*)(rsrc_l + p.R_max);               // [R_max]
+        int* slot_l = (int*)(roww_l + p.R_max);                   // [T * (k + s)]
+        int* scr = slot_l + p.T * ks;                             // permute scratch
+        const bool lead = blockIdx.x == 0;
+        route_block<KW, RT, 256 / RT>(p.logits, p.T, p.E_tot, p.k_top, p.renorm != 0, sidx, sw,
+                                      lead ? p.topk_idx : nullptr, p.topk_w);
+        __syncthreads();
+        permute_in_block<KW>([&](int a) { return sidx[a]; }, [&](int a) { return sw[a]; },
+                             p.T, p.k_top, p.e0, p.E_loc, s_sh, cnt_l, off_l, off32_l, rsrc_l, roww_l,
+                             slot_l, scr);
+        __syncthreads();
+        if (lead) {
+            const int R = off_l[G];
+            for (int i = tid; i < G; i += NT) const_cast<int32_t*>(p.counts)[i] = cnt_l[i];
+            for (int i = tid; i <= G; i += NT) {
+                const_cast<int32_t*>(p.offsets)[i] = off_l[i];
+                if (p.offsets32) const_cast<int32_t*>(p.offsets32)[i] = off32_l[i];
+            }
+            for (int i = tid; i < R; i += NT) {
+                const_cast<int32_t*>(p.row_src)[i] = rsrc_l[i];
+                const_cast<float*>(p.row_w)[i] = roww_l[i];
+            }
+            for (int i = tid; i < p.T * ks; i += NT) p.slot_row[i] = slot_l[i];
+        }
+        cnt_tab = cnt_l; off_tab = off_l; rsrc_tab = rsrc_l; roww_tab = roww_l;
+    }
+    if (w == 0) pass_prefix(cnt_tab, G, rows_per_pass, lane, pass_off);
     __syncthreads();
     const int n_items = pass_off[G] * units;
 
@@ -161,13 +205,13 @@ void grouped_gemm_kernel(KParams p) {
             if (pass_off[mid] <= pg) glo = mid; else ghi = mid;
         }
         const int g = glo, pass = pg - pass_off[g];
-        const int n_g = p.counts[g];
+        const int n_g = cnt_tab[g];
         const int sel = g < p.E_loc ? 0 : 1;
         const int gi = g < p.E_loc ? g : 0;
         const uint8_t* wgrp = p.wbase[sel] + gi * p.gstride;
         const rsrc_t rw = make_rsrc(wgrp + u * p.dpu, (uint32_t)p.dpu);
         const rsrc_t rs = make_rsrc(wgrp + p.dpg + u * p.spu, (uint32_t)p.spu);
-        const int rbase = p.offsets[g] + pass * rows_per_pass;
+        const int rbase = off_tab[g] + pass * rows_per_pass;
         const int nrows = min(rows_per_pass, n_g - pass * rows_per_pass);
         const int ntt_active = (nrows + 15) / 16;
 
@@ -178,7 +222,7 @@ void grouped_gemm_kernel(KParams p) {
             #pragma unroll
             for (int t = 0; t < 4; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int r = tt * 16 + (lane & 15);
-            const long xr = r < nrows ? (p.row_src ? (long)p.row_src[rbase + r] : (long)(rbase + r)) : -1;
+            const long xr = r < nrows ? (rsrc_tab ? (long)rsrc_tab[rbase + r] : (long)(rbase + r)) : -1;
             xoff[tt] = xr >= 0 ? (uint32_t)(xr * p.K) : kInvalid;
             xsoff[tt] = xr >= 0 ? (uint32_t)(xr * (p.K / 32)) : kInvalid;
         }
@@ -236,7 +280,7 @@ void grouped_gemm_kernel(KParams p) {
                 const float gsum = red[((tt * 4 + gt) * 4 + v) * 64 + le];
                 const float usum = red[((tt * 4 + gt + 2) * 4 + v) * 64 + le];
                 const int f = gt * 16 + 4 * (le >> 4) + v;
-                const float wgt = p.use_w ? p.row_w[rbase + tok] : 1.0f;
+                const float wgt = p.use_w ? roww_tab[rbase + tok] : 1.0f;
                 hbuf[tok * 33 + f] = silu(gsum) * usum * wgt;
             }
             __syncthreads();
@@ -299,11 +343,18 @@ void grouped_gemm_kernel(KParams p) {
     }
 }
 
-template <int WFMT, bool IS_W1, int NTT, int KW, int CP>
+// LDS ints of the routing tables of a W1 launch that routes its own tokens
+inline size_t route_lds_ints(const KParams& p, int KW) {
+    const int s = p.G - p.E_loc, Tk = p.T * p.k_top;
+    return (size_t)2 * Tk + p.G + 2 * (p.G + 1) + 2 * (size_t)p.R_max + (size_t)p.T * (p.k_top + s) +
+           block_lds_ints(KW, p.G, p.E_loc);
+}
+
+template <int WFMT, bool IS_W1, int NTT, int KW, int CP, int RT = 0>
 int launch(const KParams& p, long max_items, hipStream_t stream) {
-    auto kern = grouped_gemm_kernel<WFMT, IS_W1, NTT, KW, CP>;
+    auto kern = grouped_gemm_kernel<WFMT, IS_W1, NTT, KW, CP, RT>;
     const size_t lds = (size_t)((p.G + 4) & ~3) * 4 + (size_t)(KW / 2) * NTT * 1024 * 4 +
-                       (IS_W1 ? (size_t)16 * NTT * 33 * 4 : 0);
+                       (IS_W1 ? (size_t)16 * NTT * 33 * 4 : 0) + (RT ? route_lds_ints(p, KW) * 4 : 0);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * KW, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
@@ -314,21 +365,27 @@ int launch(const KParams& p, long max_items, hipStream_t stream) {
 
 // 16 K-split waves only with one token tile: 1024-thread workgroups get 128
 // VGPRs, too few for more
-template <int WFMT, bool IS_W1, int NTT, int CP>
+template <int WFMT, bool IS_W1, int NTT, int CP, int RT = 0>
 int launch_kw(const KParams& p, int kw, long max_items, hipStream_t stream) {
     if constexpr (NTT == 1)
-        if (kw >= 16) return launch<WFMT, IS_W1, NTT, 16, CP>(p, max_items, stream);
-    if (kw >= 8) return launch<WFMT, IS_W1, NTT, 8, CP>(p, max_items, stream);
-    return launch<WFMT, IS_W1, NTT, 4, CP>(p, max_items, stream);
+        if (kw >= 16) return launch<WFMT, IS_W1, NTT, 16, CP, RT>(p, max_items, stream);
+    if (kw >= 8) return launch<WFMT, IS_W1, NTT, 8, CP, RT>(p, max_items, stream);
+    return launch<WFMT, IS_W1, NTT, 4, CP, RT>(p, max_items, stream);
 }
 
 constexpr int kTiledMinRows = 96;   // expected rows per group from which the tiled kernel runs
+// tokens a W1 launch routes itself, at most: every workgroup routes all of
+// them, so the saving of a launch turns into a loss from about 32 tokens on
+constexpr int kRouteMaxT = 8;
+
+// expected rows per group, as the launch sees them
+inline int expected_rows(int rows_hint, int R_max, int G) { return rows_hint > 0 ? rows_hint : R_max / G; }
 
 template <bool IS_W1>
 int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     if (a.G == 0 || a.R_max == 0) return 0;
     // token tiles per pass, from the expected rows per group
-    const int avg = a.rows_hint > 0 ? a.rows_hint : a.R_max / a.G;
+    const int avg = expected_rows(a.rows_hint, a.R_max, a.G);
     // many rows per group: the weights are reused across many token tiles and
     // the MFMA, not HBM, is the bound -> the LDS-tiled kernel
     if (avg >= kTiledMinRows) return IS_W1 ? moe_launch_tiled_w1(a, stream) : moe_launch_tiled_w2(a, stream);
@@ -352,6 +409,16 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     // stream through non-temporally
     const bool reread = ntt > 1 || avg >= rpp;
     const bool fp4 = a.fmt == MOE_FMT_MXFP4;
+    if constexpr (IS_W1) if (a.route) {
+        // the layer skipped its routing launches: moe_w1_can_route held, so
+        // ntt == 1 and the weights stream non-temporally
+        if (ntt != 1 || reread) return (int)hipErrorInvalidValue;
+        const bool wide = a.route->T <= kw;     // one token per wave per round
+        if (fp4) return wide ? launch_kw<MFMA_FMT_FP4, IS_W1, 1, kNonTemporal, 64>(p, kw, max_items, stream)
+                             : launch_kw<MFMA_FMT_FP4, IS_W1, 1, kNonTemporal, 16>(p, kw, max_items, stream);
+        return wide ? launch_kw<MFMA_FMT_FP8, IS_W1, 1, kNonTemporal, 64>(p, kw, max_items, stream)
+                    : launch_kw<MFMA_FMT_FP8, IS_W1, 1, kNonTemporal, 16>(p, kw, max_items, stream);
+    }
 #define MOE_GEMM_CASE(N, CP)                                                                      \
     return fp4 ? launch_kw<MFMA_FMT_FP4, IS_W1, N, CP>(p, kw, max_items, stream)                  \
                : launch_kw<MFMA_FMT_FP8, IS_W1, N, CP>(p, kw, max_items, stream);
@@ -367,4 +434,17 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
 }  // namespace
 
 int moe_launch_grouped_w1(const GemmArgs& a, hipStream_t stream) { return launch_grouped<true>(a, stream); }
+
+// The conditions under which launch_grouped<true> takes the one-token-tile,
+// non-temporal path, plus the limits of the in-workgroup routing (at most
+// 256 experts, k <= 16, T <= 8 tokens, at most 513 groups).
+bool moe_w1_can_route(int T, int E_tot, int k, int E_loc, int s, int R_max, int H, int I,
+                      int rows_hint, uint32_t flags) {
+    (void)H; (void)I;
+    const int G = E_loc + s;
+    if (T < 1 || T > kRouteMaxT || E_tot > 256 || k > 16 || G > 513 || G < 1) return false;
+    if (flags & MOE_W1_WRITE_TRANSPOSE) return false;
+    const int avg = expected_rows(rows_hint, R_max, G);
+    return avg < 16;
+}
 int moe_launch_grouped_w2(const GemmArgs& a, hipStream_t stream) { return launch_grouped<false>(a, stream); }

@@ -29,6 +29,12 @@ struct KParams {
     const uint32_t* bst;              // tiled kernels: activation scales per K-tile and pass
     uint32_t bst_bytes;
     int npass;                        // passes the scale tiles are laid out for
+    // decode W1 that routes its own tokens (logits non-null): every workgroup
+    // routes and groups the T tokens in LDS, workgroup 0 writes the results
+    // to the routing outputs and to counts .. row_w above
+    const float* logits;
+    int T, E_tot, k_top, renorm, e0, R_max;
+    int32_t* topk_idx; float* topk_w; int32_t* slot_row;
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -74,6 +80,13 @@ inline KParams make_params(const GemmArgs& a, bool w1) {
     p.use_w = (w1 && a.row_w && !(a.flags & MOE_WEIGHT_AT_COMBINE)) ? 1 : 0;
     p.hq = a.hq; p.hs = a.hs; p.hTq = a.hTq; p.hTs = a.hTs; p.ldT = a.ldT;
     p.y = a.y;
+    if (a.route) {
+        p.logits = a.route->logits;
+        p.T = a.route->T; p.E_tot = a.route->E_tot; p.k_top = a.route->k; p.e0 = a.route->e0;
+        p.renorm = (a.route->flags & MOE_ROUTE_RENORM) ? 1 : 0;
+        p.topk_idx = a.route->topk_idx; p.topk_w = a.route->topk_w; p.slot_row = a.route->slot_row;
+    }
+    p.R_max = a.R_max;
     return p;
 }
 

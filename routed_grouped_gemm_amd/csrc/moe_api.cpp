@@ -194,7 +194,8 @@ static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shar
                                const int32_t* row_src, int32_t x_rows, int32_t R_max,
                                int32_t H, int32_t I, int32_t G, uint32_t flags, uint8_t* hq,
                                uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes,
-                               int rows_hint, hipStream_t stream, int active_hint = 0) {
+                               int rows_hint, hipStream_t stream, int active_hint = 0,
+                               const RouteArgs* route = nullptr) {
     int32_t st = check_hi(H, I);
     if (st) return st;
     if (R_max < 0 || G < 1 || G > MOE_MAX_EXPERTS + 1) return MOE_ERR_SHAPE;
@@ -214,6 +215,7 @@ static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shar
     a.R_max = R_max; a.rows_hint = rows_hint; a.active_hint = active_hint; a.flags = flags;
     a.hq = hq; a.hs = hs; a.hTq = hTq; a.hTs = hTs; a.ldT = moe_transposed_ld(R_max, G);
     a.ws = ws; a.ws_bytes = ws_bytes;
+    a.route = route;
     return hip_status(moe_launch_grouped_w1(a, stream));
 }
 
@@ -346,8 +348,19 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     const size_t scratch_bytes = L.total - L.off[11];
     const int R_max = T * k + s * T;
 
+    // expected rows of a routed group under uniform routing; the shared group
+    // (T rows) gets more passes from the grid's pass dimension
+    const int hint = moe_layer_rows_hint(T, E_tot, k);
+    // expected local experts with at least one token: E_loc (1 - (1 - k/E_tot)^T), plus the shared one
+    const int active = moe_layer_active_hint(T, E_tot, k, E_loc, s);
+    // few tokens: the W1 launch routes and groups them itself
+    const bool self_route = moe_w1_can_route(T, E_tot, k, E_loc, s, R_max, H, I, hint, a->flags);
+    const RouteArgs ra{a->logits, T, E_tot, k, e0, a->flags, topk_idx, topk_w, slot_row};
+
     int e;
-    if (moe_route_permute_fusable(T, E_tot, k, E_loc, s)) {
+    if (self_route) {
+        // routing and grouping happen inside the W1 launch below
+    } else if (moe_route_permute_fusable(T, E_tot, k, E_loc, s)) {
         e = moe_launch_route_permute(a->logits, T, E_tot, k, a->flags, e0, E_loc, s, topk_idx,
                                      topk_w, counts, offsets, offsets32, row_src, row_w, slot_row,
                                      stream);
@@ -360,14 +373,9 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
                                scratch, stream);
         if (e) return MOE_ERR_HIP;
     }
-    // expected rows of a routed group under uniform routing; the shared group
-    // (T rows) gets more passes from the grid's pass dimension
-    const int hint = moe_layer_rows_hint(T, E_tot, k);
-    // expected local experts with at least one token: E_loc (1 - (1 - k/E_tot)^T), plus the shared one
-    const int active = moe_layer_active_hint(T, E_tot, k, E_loc, s);
     st = grouped_w1_impl(a->w1, a->shared_w1, counts, offsets, offsets32, row_w, a->xq, a->xs,
                          row_src, T, R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch,
-                         scratch_bytes, hint, stream, active);
+                         scratch_bytes, hint, stream, active, self_route ? &ra : nullptr);
     if (st) return st;
     st = grouped_w2_impl(a->w2, a->shared_w2, counts, offsets, hq, hs, R_max, H, I, G, y, scratch,
                          scratch_bytes, hint, stream, active);

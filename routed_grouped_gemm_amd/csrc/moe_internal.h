@@ -36,6 +36,14 @@ int moe_launch_route_permute(const float* logits, int T, int E, int k, uint32_t 
                              int32_t* offsets, int32_t* offsets32, int32_t* row_src, float* row_w,
                              int32_t* slot_row, hipStream_t stream);
 
+// Routing inputs and outputs for a W1 launch that routes its own tokens.
+struct RouteArgs {
+    const float* logits;
+    int T, E_tot, k, e0;
+    uint32_t flags;
+    int32_t* topk_idx; float* topk_w; int32_t* slot_row;
+};
+
 struct GemmArgs {
     const uint8_t* w_base[2];    // prepacked routed groups, shared group
     int E_loc;                   // groups < E_loc use [0], group E_loc uses [1]
@@ -56,8 +64,15 @@ struct GemmArgs {
     uint8_t* hTq; uint8_t* hTs; int ldT;
     uint16_t* y;                 // W2 output
     void* ws; size_t ws_bytes;   // workspace (moe_grouped_workspace_size bytes)
+    // W1 only, optional: route and group the tokens inside the W1 launch
+    // (counts, offsets, offsets32, row_src and row_w are then written, not
+    // read); only when moe_w1_can_route says so
+    const RouteArgs* route;
 };
 int moe_launch_grouped_w1(const GemmArgs& a, hipStream_t stream);
+// Whether the W1 launch for these shapes can route its own tokens.
+bool moe_w1_can_route(int T, int E_tot, int k, int E_loc, int s, int R_max, int H, int I,
+                      int rows_hint, uint32_t flags);
 int moe_launch_grouped_w2(const GemmArgs& a, hipStream_t stream);
 // LDS-tiled variants for groups with many rows (256 x 256 workgroup tiles)
 int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream);

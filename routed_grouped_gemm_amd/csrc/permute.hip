@@ -12,8 +12,7 @@
 // Paths: up to 4096 assignments a single workgroup does everything; for a few
 // tokens the router runs in that same workgroup (one launch for S1-S3). Larger
 // inputs use three kernels: per-chunk histograms, a scan, a scatter.
-#include "moe_device.h"
-#include "moe_internal.h"
+#include "permute_block.h"
 
 namespace {
 
@@ -22,165 +21,6 @@ constexpr int kSmallMax = 4096;         // single-workgroup path up to this many
 constexpr int kFusedThreads = 1024;     // route + permute in one workgroup
 constexpr int kFusedMaxT = kFusedThreads / 64 * 4;   // four tokens per wave
 constexpr int kFusedMaxG = 513;
-
-MOE_DEV uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : (~0ull >> (64 - lane)); }
-
-// counts (LDS, G entries) -> counts/offsets/offsets32 in global memory; the
-// LDS array holds the offsets afterwards. Wave 0 scans: each lane takes a run
-// of ceil(G/64) consecutive groups, the lanes' run totals are scanned with
-// shuffles, then each lane writes its run.
-MOE_DEV void write_offsets(int* lds_counts, int G, int32_t* counts, int32_t* offsets,
-                           int32_t* offsets32) {
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        const int per = (G + 63) / 64;
-        const int lo = min(G, lane * per), hi = min(G, lo + per);
-        int s = 0, s32 = 0;
-        for (int i = lo; i < hi; ++i) {
-            const int c = lds_counts[i];
-            s += c;
-            s32 += (c + 31) & ~31;
-        }
-        int inc = s, inc32 = s32;                  // inclusive scan over lanes
-        #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int a = __shfl_up(inc, d, 64), b = __shfl_up(inc32, d, 64);
-            if (lane >= d) { inc += a; inc32 += b; }
-        }
-        int run = inc - s, run32 = inc32 - s32;
-        for (int i = lo; i < hi; ++i) {
-            const int c = lds_counts[i];
-            counts[i] = c;
-            offsets[i] = run;
-            if (offsets32) offsets32[i] = run32;
-            lds_counts[i] = run;
-            run += c;
-            run32 += (c + 31) & ~31;
-        }
-        if (lane == 63) {
-            offsets[G] = inc;
-            if (offsets32) offsets32[G] = inc32;
-        }
-    }
-    __syncthreads();
-}
-
-// One wave: rank of each lane's group among the lanes below it with the same
-// group, and the per-group lane count written by the group's lowest lane.
-// The lanes sharing a lane's group are found with one ballot per bit of the
-// group index (gbits bits), in constant time however many groups the wave
-// holds. Lanes with g < 0 take no part; their rank is meaningless.
-MOE_DEV int wave_match_rank(int g, int lane, int gbits, uint16_t* wave_cnt /* [E_loc] of this wave */) {
-    uint64_t same = __ballot(g >= 0);
-    for (int b = 0; b < gbits; ++b) {
-        const bool bit = (g >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        same &= bit ? m : ~m;
-    }
-    const int rank = __popcll(same & lanemask_lt(lane));
-    if (g >= 0 && rank == 0) wave_cnt[g] = (uint16_t)__popcll(same);
-    return rank;
-}
-
-// Bits of a group index in [0, E_loc).
-__host__ __device__ inline int group_bits(int E_loc) { return E_loc > 1 ? 32 - __builtin_clz((unsigned)(E_loc - 1)) : 0; }
-
-// Per-wave lane counts of one chunk -> per-wave exclusive prefix (in place),
-// and the chunk totals in tot (if non-null).
-template <int NW>
-MOE_DEV void scan_waves(uint16_t* cnt, int E_loc, int* tot) {
-    for (int g = threadIdx.x; g < E_loc; g += blockDim.x) {
-        int run = 0;
-        #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            int v = cnt[w * E_loc + g];
-            cnt[w * E_loc + g] = (uint16_t)run;
-            run += v;
-        }
-        if (tot) tot[g] = run;
-    }
-}
-
-MOE_DEV void write_row(int a, int g, int row, int k, int ks, float w,
-                       int32_t* row_src, float* row_w, int32_t* slot_row) {
-    int t = a / k, j = a - t * k;
-    if (g >= 0) {
-        row_src[row] = t;
-        row_w[row] = w;
-        slot_row[(size_t)t * ks + j] = row;
-    } else {
-        slot_row[(size_t)t * ks + j] = -1;
-    }
-}
-
-MOE_DEV void write_shared_rows(int t0, int t1, int T, int k, int ks, int base,
-                               int32_t* row_src, float* row_w, int32_t* slot_row) {
-    for (int t = t0 + (int)threadIdx.x; t < min(T, t1); t += blockDim.x) {
-        int r = base + t;
-        row_src[r] = t;
-        row_w[r] = 1.0f;
-        slot_row[(size_t)t * ks + k] = r;
-    }
-}
-
-// LDS ints needed by permute_in_block.
-constexpr size_t block_lds_ints(int NW, int G, int E_loc) {
-    return (size_t)3 * G + ((size_t)NW * E_loc * 2 + 3) / 4;
-}
-
-// The whole S2/S3 computation of up to 4096 assignments in one workgroup of
-// NW waves. idx_of(a) / w_of(a) read the routing of flattened assignment a.
-template <int NW, class IdxF, class WF>
-MOE_DEV void permute_in_block(IdxF idx_of, WF w_of, int T, int k, int e0, int E_loc, int s,
-                              int32_t* counts, int32_t* offsets, int32_t* offsets32,
-                              int32_t* row_src, float* row_w, int32_t* slot_row, int* lds) {
-    constexpr int NT = NW * 64;
-    const int G = E_loc + s;
-    int* hist = lds;                       // [G]   counts, then offsets
-    int* tmp = hist + G;                   // [G]   chunk totals
-    int* base = tmp + G;                   // [G]   running row of each group
-    uint16_t* cnt = (uint16_t*)(base + G);     // [NW][E_loc]
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int Tk = T * k, ks = k + s;
-    const int gbits = group_bits(E_loc);
-
-    for (int g = tid; g < G; g += NT) hist[g] = 0;
-    __syncthreads();
-    for (int a = tid; a < Tk; a += NT) {
-        int g = idx_of(a) - e0;
-        if (g >= 0 && g < E_loc) atomicAdd(&hist[g], 1);
-    }
-    __syncthreads();
-    if (s && tid == 0) hist[E_loc] = T;
-    __syncthreads();
-    write_offsets(hist, G, counts, offsets, offsets32);
-    for (int g = tid; g < G; g += NT) base[g] = hist[g];
-    __syncthreads();
-
-    for (int c0 = 0; c0 < Tk; c0 += NT) {
-        for (int i = tid; i < NW * E_loc; i += NT) cnt[i] = 0;
-        __syncthreads();
-        const int a = c0 + tid;
-        int g = -1;
-        if (a < Tk) {
-            int gg = idx_of(a) - e0;
-            if (gg >= 0 && gg < E_loc) g = gg;
-        }
-        const int rank = wave_match_rank(g, lane, gbits, cnt + w * E_loc);
-        __syncthreads();
-        scan_waves<NW>(cnt, E_loc, tmp);
-        __syncthreads();
-        if (a < Tk) {
-            int row = g >= 0 ? base[g] + cnt[w * E_loc + g] + rank : -1;
-            write_row(a, g, row, k, ks, g >= 0 ? w_of(a) : 0.f, row_src, row_w, slot_row);
-        }
-        __syncthreads();
-        for (int gg = tid; gg < E_loc; gg += NT) base[gg] += tmp[gg];
-        __syncthreads();
-    }
-    if (s) write_shared_rows(0, T, T, k, ks, hist[E_loc], row_src, row_w, slot_row);
-}
 
 // ---- single-workgroup path ---------------------------------------------
 __global__ __launch_bounds__(kFusedThreads)
@@ -206,28 +46,8 @@ void route_permute_kernel(const float* __restrict__ logits, int T, int E, int k,
     extern __shared__ int lds[];
     int* sidx = lds;                        // [T*k]
     float* sw = (float*)(lds + T * k);      // [T*k]
-    constexpr int TPW = 64 / LPT;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     constexpr int NW = kFusedThreads / 64;
-    const int t = TPW * w + lane / LPT;
-    if (TPW * w < T) {                      // waves past the tokens skip routing
-        float v[VPL];
-        if (t < T) load_logits<LPT, VPL>(logits + (size_t)t * E, E, lane, v);
-        else {
-            #pragma unroll
-            for (int i = 0; i < VPL; ++i) v[i] = -INFINITY;
-        }
-        int e = 0;
-        float wt = 0.f;
-        route_values<LPT, VPL>(v, t < T ? E : 0, k, renorm != 0, lane, e, wt);
-        const int j = lane & (LPT - 1);
-        if (t < T && j < k) {
-            sidx[t * k + j] = e;
-            sw[t * k + j] = wt;
-            topk_idx[(size_t)t * k + j] = e;
-            topk_w[(size_t)t * k + j] = wt;
-        }
-    }
+    route_block<NW, LPT, VPL>(logits, T, E, k, renorm != 0, sidx, sw, topk_idx, topk_w);
     __syncthreads();
     permute_in_block<NW>([&](int a) { return sidx[a]; }, [&](int a) { return sw[a]; },
                          T, k, e0, E_loc, s, counts, offsets, offsets32, row_src, row_w, slot_row,

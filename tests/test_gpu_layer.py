@@ -56,6 +56,11 @@ SMALL = [
     ("renorm-ceil", dict(T=24, E=16, k=4, n_local=16), moe.MOE_ROUTE_RENORM | moe.MOE_SCALE_RULE_CEIL),
     ("weight-at-combine", dict(T=20, E=8, k=3, n_local=8), moe.MOE_WEIGHT_AT_COMBINE),
     ("ragged-passes", dict(T=200, H=768, I=256, E=4, k=2, n_local=4, shared=True), 0),
+    # at most 8 tokens: the W1 launch routes and groups the tokens itself
+    ("self-route-renorm-ceil", dict(T=6, E=16, k=4, n_local=16), moe.MOE_ROUTE_RENORM | moe.MOE_SCALE_RULE_CEIL),
+    ("self-route-shared-wc", dict(T=5, H=1024, I=512, E=32, k=4, e0=8, n_local=12, shared=True),
+     moe.MOE_WEIGHT_AT_COMBINE),
+    ("self-route-one-token", dict(T=1, E=64, k=8, e0=16, n_local=24), 0),
     # about 275 rows per expert: the LDS-tiled GEMMs, with the transposed copy
     ("tiled-mxfp8-transpose", dict(T=1100, H=512, I=384, E=8, k=2, n_local=8, w_fmt="e4m3",
                                    transpose=True), moe.MOE_W1_WRITE_TRANSPOSE),
