@@ -232,7 +232,8 @@ void tiled_gemm_kernel(KParams p) {
         }
         const uint8_t* st = ring + (s & 1) * S::Bytes;
         // this wave's 4 weight tiles stay in registers for the K-tile; its
-        // 8 token tiles stream from LDS, each against all 4
+        // 8 token tiles stream from LDS, each against all 4, the next token
+        // tile's reads in flight while the current one is multiplied
         const int ash = 8 * (kt & 3);
         i32x8 A[kAT];
         int sa[kAT];
@@ -243,17 +244,37 @@ void tiled_gemm_kernel(KParams p) {
             const i32x4 alo = *(const i32x4*)ap;
             const i32x4 ahi = WFMT == MFMA_FMT_FP8 ? *(const i32x4*)(ap + 1024) : i32x4{0, 0, 0, 0};
             A[t] = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
-            sa[t] = ((const int*)(st + S::AS))[T * 64 + lane] >> ash;
+            sa[t] = ((const int*)(st + S::AS))[T * 64 + lane];
         }
-        #pragma unroll
-        for (int j = 0; j < kBT; ++j) {
+        auto load_b = [&](int j, i32x8& B, int& bs) {
             const i32x4 blo = *(const i32x4*)(st + boff_lo[j]);
             const i32x4 bhi = *(const i32x4*)(st + boff_hi[j]);
-            const i32x8 B = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
-            const int bs = ((const int*)(st + S::BS))[ti * 128 + 16 * j + r] >> (8 * q);
+            B = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+            bs = ((const int*)(st + S::BS))[ti * 128 + 16 * j + r];
+        };
+        i32x8 Bb[2];
+        int bsb[2];
+        load_b(0, Bb[0], bsb[0]);
+        #pragma unroll
+        for (int t = 0; t < kAT; ++t) sa[t] >>= ash;
+        #pragma unroll
+        for (int j = 0; j < kBT; ++j) {
+            if (j + 1 < kBT) load_b(j + 1, Bb[(j + 1) & 1], bsb[(j + 1) & 1]);
+            const int bs = bsb[j & 1] >> (8 * q);
             #pragma unroll
             for (int t = 0; t < kAT; ++t)
-                acc[j][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, 0, 0>(A[t], B, acc[j][t], sa[t], bs);
+                acc[j][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, 0, 0>(A[t], Bb[j & 1], acc[j][t], sa[t], bs);
+        }
+        // issue order: the weight tiles, their scales and the first two token
+        // tiles; then per token tile its 4 MFMAs followed by the reads of the
+        // token tile after next (the scheduler would otherwise reuse one
+        // register buffer for every token tile and wait for each read)
+        constexpr int kAR = WFMT == MFMA_FMT_FP8 ? 3 : 2;      // LDS reads per weight tile
+        __builtin_amdgcn_sched_group_barrier(0x100, kAR * kAT + 6, 0);
+        #pragma unroll
+        for (int j = 0; j < kBT; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kAT, 0);
+            if (j + 2 < kBT) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         }
         __builtin_amdgcn_s_waitcnt(0);       // the next step's operands have landed
         __syncthreads();
