@@ -22,9 +22,12 @@ the kernel sources differ from those the counters were taken with);
 "cpu_baseline" times the CPU oracle on
 a bounded sample (the T=8 call of one routing draw). "other_workloads"
 gives the layer latency, TB/s, TFLOP/s and roofline fraction of the tiny,
-full-expert, 16K-token prefill and shared-expert workloads (graph replay).
+full-expert, 16K-token prefill and shared-expert workloads (graph replay),
+each with the oracle timed on a token sample of the same workload
+("cpu_oracle").
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-other-workloads]
+    python bench.py --only prefill          # one workload's latency line only
 """
 from __future__ import annotations
 
@@ -90,6 +93,56 @@ def cpu_baseline(c8, moe_bytes_fn):
     return {"value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one layer call at T=8 (routing draw 0, {len(active)} active experts), "
                       f"{dt:.2f} s wall on the host CPU, fp64 NumPy"}, dt
+
+
+# token samples of the other workloads for the oracle's timing (about 1-5 s each)
+ORACLE_SAMPLE_TOKENS = {"tiny": 16, "full": 1, "prefill": 4, "shared": 1}
+
+
+def cpu_oracle_sample(name: str, ntok: int, threads: int):
+    """Time the oracle on the first ntok tokens of a workload's routing draw 0
+    (same shapes, experts and weights; the weights of the experts the sample
+    touches are quantised beforehand, untimed). Rates use the sample's own
+    algorithmic bytes and FLOPs."""
+    import numpy as np
+    from oracle import moe as omoe, mx
+    import synth
+    c = synth.config(name)
+    lg = np.ascontiguousarray(synth.logits(c, 0)[:ntok])
+    xq, xs = mx.quantize_mx(np.ascontiguousarray(synth.x(c, 0)[:ntok]), mx.FMT_E4M3)
+    idx, _ = omoe.route(lg, c.k)
+    local = [int(e) - c.e0 for e in idx.ravel() if 0 <= int(e) - c.e0 < c.n_local]
+    active = sorted(set(local))
+    w1q, w1s, w2q, w2s = [None] * c.n_local, [None] * c.n_local, [None] * c.n_local, [None] * c.n_local
+    for g in active:
+        w1q[g], w1s[g] = mx.quantize_mx(synth.w1(c, g), c.w_fmt)
+        w2q[g], w2s[g] = mx.quantize_mx(synth.w2(c, g), c.w_fmt)
+    shared = None
+    if c.shared:
+        a1, b1 = mx.quantize_mx(synth.shared_w1(c), c.w_fmt)
+        a2, b2 = mx.quantize_mx(synth.shared_w2(c), c.w_fmt)
+        shared = (a1, b1, a2, b2)
+    t0 = time.perf_counter()
+    omoe.moe_layer(lg, xq, xs, c.k, w1q, w1s, w2q, w2s, c.w_fmt, c.I, e0=c.e0, n_local=c.n_local,
+                   shared=shared, transpose=c.transpose)
+    dt = time.perf_counter() - t0
+    fp4 = c.w_fmt == "e2m1"
+    groups = len(active) + (1 if c.shared else 0)
+    rows = len(local) + (ntok if c.shared else 0)
+    nbytes = layer_bytes(ntok, c.E, c.H, c.I, groups, fp4)
+    flops = 6.0 * rows * c.H * c.I
+    return {"tokens": ntok, "wall_s": round(dt, 3), "TBps": nbytes / dt / 1e12,
+            "TFLOPs": flops / dt / 1e12, "cores": int(threads), "kind": "oracle",
+            "sample": f"the first {ntok} of {c.T} tokens (routing draw 0: {groups} groups, {rows} rows), "
+                      f"fp64 NumPy on the host CPU"}
+
+
+def oracle_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
 
 
 MFMA_FP8_PEAK_TFLOPS = 5000.0
@@ -204,6 +257,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the latency lines of the tiny, full-expert, prefill and shared-expert workloads")
+    ap.add_argument("--only", choices=["tiny", "full", "prefill", "shared"],
+                    help="time only this workload's layer (no decode bench, no oracle) and print its line; "
+                         "for profiling one workload")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -217,6 +273,9 @@ def main():
     from synth import device
 
     torch.cuda.set_device(0)
+    if args.only:
+        print(json.dumps(other_workloads(torch, moe, synth, device, [args.only])), flush=True)
+        return
     c = synth.config("decode", 128)
     fp4 = c.w_fmt == "e2m1"
     t_setup = time.perf_counter()
@@ -374,6 +433,12 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu, _ = cpu_baseline(cfg[8], lambda T, act: layer_bytes(T, c.E, c.H, c.I, act, fp4))
+        if others is not None:
+            import numpy  # noqa: F401  (loads BLAS so its thread count is visible)
+            threads = oracle_threads()
+            for name, ntok in ORACLE_SAMPLE_TOKENS.items():
+                others[name]["cpu_oracle"] = cpu_oracle_sample(name, ntok, threads)
+                log(f"{name} oracle: {others[name]['cpu_oracle']}")
 
     line = {
         "metric": "MoE layer latency µs + achieved HBM TB/s (decode), MFMA TFLOPS (prefill)",
