@@ -106,16 +106,19 @@ MOE_DEV Ctx decode(const KParams& p, const int* pass_off, int item, int wtiles, 
     c.wgrp = p.wbase[sel] + gi * p.gstride;
     // source rows of the item's grouped rows (branch-free: rows past the
     // item read as 0 through the bounded resource and are marked invalid)
+    // (all four requested before any is used: one memory latency, not four;
+    // without row_src the resource is empty and the row itself is the source)
     const rsrc_t rsrcs = make_rsrc(p.row_src + c.rbase, p.row_src ? (uint32_t)(c.nrows * 4) : 0u);
-    auto src_row = [&](int row) -> uint32_t {
-        return p.row_src ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrcs, (uint32_t)(row * 4), 0, 0)
-                         : (uint32_t)(c.rbase + row);
-    };
+    uint32_t xr[4];
+    #pragma unroll
+    for (int i = 0; i < 4; ++i)
+        xr[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rsrcs, (uint32_t)((32 * w + 8 * i + (lane >> 3)) * 4), 0, 0);
     #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 32 * w + 8 * i + (lane >> 3);
-        const uint32_t xr = src_row(row);
-        c.xoff[i] = row < c.nrows ? xr * (uint32_t)p.K : kInvalid;
+        const uint32_t src = p.row_src ? xr[i] : (uint32_t)(c.rbase + row);
+        c.xoff[i] = row < c.nrows ? src * (uint32_t)p.K : kInvalid;
     }
     return c;
 }
@@ -301,6 +304,18 @@ void tiled_gemm_kernel(KParams p) {
             const rsrc_t rhq = make_rsrc(p.hq + (size_t)cur.rbase * I, (uint32_t)(cur.nrows * I));
             const rsrc_t rhs = make_rsrc(p.hs + (size_t)cur.rbase * (I / 32), (uint32_t)(cur.nrows * (I / 32)));
             const rsrc_t rw_w = make_rsrc(p.row_w + cur.rbase, p.use_w ? (uint32_t)(cur.nrows * 4) : 0u);
+            // the routing weights of this lane's 8 token rows, all requested
+            // before the first is used (one memory latency per item, not 8);
+            // rows past the item read 0 and have zero sums anyway
+            // (without weights the resource is empty: the loads return 0 and
+            // are replaced by 1 without a branch)
+            float wrow[kBT];
+            #pragma unroll
+            for (int j = 0; j < kBT; ++j)
+                wrow[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rw_w, (uint32_t)((tok0 + 16 * j + r) * 4), 0, 0));
+            #pragma unroll
+            for (int j = 0; j < kBT; ++j) wrow[j] = p.use_w ? wrow[j] : 1.0f;
             #pragma unroll
             for (int jp = 0; jp < kBT / 2; ++jp) {
                 float h[2][2][4];                               // [j in pair][gate tile][v]
@@ -309,7 +324,7 @@ void tiled_gemm_kernel(KParams p) {
                     const int j = 2 * jp + jj;
                     const int tok = tok0 + 16 * j + r;
                     // rows past the item have zero token rows, so zero sums and h = 0
-                    const float wgt = p.use_w ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw_w, (uint32_t)(tok * 4), 0, 0)) : 1.0f;
+                    const float wgt = wrow[j];
                     float amf = 0.f;
                     #pragma unroll
                     for (int a = 0; a < 2; ++a)
