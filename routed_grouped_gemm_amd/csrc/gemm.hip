@@ -396,14 +396,25 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     const int rpp = 16 * ntt;
     // items never exceed units * (R_max / rpp + G): each group adds at most one partial pass
     const long max_items = (long)units * ((long)a.R_max / rpp + a.G);
-    // K-split waves per workgroup when few groups are active: enough waves
-    // for four per SIMD in W1 (the long K = H splits well), two in W2 (a
-    // shorter K, where wider splits cost more in the reduction than they gain)
+    // K-split waves per workgroup. W2 (the shorter K = I, where wider splits
+    // cost more in the reduction than they gain): enough waves for two per
+    // SIMD. W1 with one token tile: 16 waves per CU whatever the split, so a
+    // round of items covers cus * 16 / kw of them, each in about 1/kw of the
+    // time of a one-wave item; the split with the fewest kw-weighted rounds
+    // leaves the least of the last, partly idle round (ties: fewer waves).
     const long active = a.active_hint > 0 ? a.active_hint
                         : std::min<long>(a.G, std::max<long>(1, a.R_max / std::max(avg, 1)));
     const long items = active * units * std::max(1, (avg + rpp - 1) / rpp);
-    const long want = IS_W1 ? 4096 : 2048;
-    int kw = items * 4 >= want ? 4 : (items * 8 >= want ? 8 : 16);
+    int kw = items * 4 >= 2048 ? 4 : (items * 8 >= 2048 ? 8 : 16);
+    if (IS_W1 && ntt == 1) {
+        const long cus = device_cu_count();
+        double best = 1e30;
+        for (int c : {4, 8, 16}) {
+            const long slots = cus * (16 / c);
+            const double t = (double)((items + slots - 1) / slots) / c;
+            if (t < best - 1e-9) { best = t; kw = c; }
+        }
+    }
     kw = std::min(kw, std::max(4, p.kt));       // no more waves than K-tiles
     if (ntt > 1) kw = std::min(kw, 8);          // 1024-thread workgroups get 128 VGPRs: too few
     // weights stay in L2 (cached loads) when a typical group needs more than
