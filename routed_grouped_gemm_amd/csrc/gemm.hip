@@ -398,14 +398,15 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     const long max_items = (long)units * ((long)a.R_max / rpp + a.G);
     // K-split waves per workgroup. W2 (the shorter K = I, where wider splits
     // cost more in the reduction than they gain): enough waves for two per
-    // SIMD. W1 with one token tile: 16 waves per CU whatever the split, so a
-    // round of items covers cus * 16 / kw of them, each in about 1/kw of the
-    // time of a one-wave item; the split with the fewest kw-weighted rounds
-    // leaves the least of the last, partly idle round (ties: fewer waves).
+    // SIMD, but never 16 (slower even with a single token). W1 with one
+    // token tile: 16 waves per CU whatever the split, so a round of items
+    // covers cus * 16 / kw of them, each in about 1/kw of the time of a
+    // one-wave item; the split with the fewest kw-weighted rounds leaves the
+    // least of the last, partly idle round (ties: fewer waves).
     const long active = a.active_hint > 0 ? a.active_hint
                         : std::min<long>(a.G, std::max<long>(1, a.R_max / std::max(avg, 1)));
     const long items = active * units * std::max(1, (avg + rpp - 1) / rpp);
-    int kw = items * 4 >= 2048 ? 4 : (items * 8 >= 2048 ? 8 : 16);
+    int kw = items * 4 >= 2048 ? 4 : (items * 8 >= 2048 || !IS_W1 ? 8 : 16);
     if (IS_W1 && ntt == 1) {
         const long cus = device_cu_count();
         double best = 1e30;
