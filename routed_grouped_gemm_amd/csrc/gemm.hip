@@ -49,12 +49,13 @@ MOE_DEV i32x8 a_operand(const ATile<WFMT>& t) {
     return r;
 }
 
-// Operands of one batch of K-tiles for one wave.
-template <int WFMT, int NTT>
+// Operands of one batch of K-tiles for one wave: TPI of the unit's four
+// 16-row weight tiles (all four, or a half unit).
+template <int WFMT, int NTT, int TPI = 4>
 struct Batch {
     static constexpr int KB = batch_kt<WFMT, NTT>();
-    ATile<WFMT> A[KB][4];             // [kt][tile]
-    int sA[KB][4];                    // E8M0 of (tile row, kt) in the low byte after the shift
+    ATile<WFMT> A[KB][TPI];           // [kt][tile]
+    int sA[KB][TPI];                  // E8M0 of (tile row, kt) in the low byte after the shift
     i32x4 Blo[NTT][KB], Bhi[NTT][KB];
     int sB[NTT][KB];
 };
@@ -62,19 +63,19 @@ struct Batch {
 // CP: cache policy of the weight loads (kNonTemporal when no other pass of
 // the group reads the same weights, 0 when other passes do and can find them
 // in L2)
-template <int WFMT, int NTT, int CP>
-MOE_DEV void load_batch(Batch<WFMT, NTT>& b, int kt_first, int kt_end, int lane,
+template <int WFMT, int NTT, int CP, int TPI = 4>
+MOE_DEV void load_batch(Batch<WFMT, NTT, TPI>& b, int kt_first, int kt_end, int lane,
                         rsrc_t rw, rsrc_t rs, rsrc_t rx, rsrc_t rxs, const uint32_t (&xoff)[NTT],
-                        const uint32_t (&xsoff)[NTT]) {
+                        const uint32_t (&xsoff)[NTT], int t0 = 0) {
     constexpr int BPL = WFMT == MFMA_FMT_FP4 ? 16 : 32;
-    constexpr int KB = Batch<WFMT, NTT>::KB;
+    constexpr int KB = Batch<WFMT, NTT, TPI>::KB;
     const int grp = lane >> 4;
     // weight scales: batches never straddle a group of four K-tiles, so one
     // dword per tile covers the batch
-    int sword[4];
+    int sword[TPI];
     #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint32_t soff = kt_first < kt_end ? (uint32_t)((((kt_first >> 2) * 4 + t) * 64 + lane) * 4)
+    for (int t = 0; t < TPI; ++t) {
+        const uint32_t soff = kt_first < kt_end ? (uint32_t)((((kt_first >> 2) * 4 + t0 + t) * 64 + lane) * 4)
                                                 : kInvalid;
         sword[t] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, CP);
     }
@@ -83,9 +84,9 @@ MOE_DEV void load_batch(Batch<WFMT, NTT>& b, int kt_first, int kt_end, int lane,
         const int kt = kt_first + i;
         const bool ok = kt < kt_end;                       // uniform
         #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < TPI; ++t) {
             // FP4: lane's 16 B at lane*16; FP8: the two 16 B halves at lane*16 and 1024 + lane*16
-            const uint32_t off = ok ? (uint32_t)((kt * 4 + t) * 64 * BPL + lane * 16) : kInvalid;
+            const uint32_t off = ok ? (uint32_t)((kt * 4 + t0 + t) * 64 * BPL + lane * 16) : kInvalid;
             b.A[i][t].lo = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, CP);
             if (WFMT == MFMA_FMT_FP8)
                 b.A[i][t].hi = __builtin_amdgcn_raw_buffer_load_b128(rw, off + (ok ? 1024u : 0u), 0, CP);
@@ -103,9 +104,9 @@ MOE_DEV void load_batch(Batch<WFMT, NTT>& b, int kt_first, int kt_end, int lane,
     }
 }
 
-template <int WFMT, int NTT>
-MOE_DEV void mma_batch(const Batch<WFMT, NTT>& b, int ntt_active, f32x4 (&acc)[NTT][4]) {
-    constexpr int KB = Batch<WFMT, NTT>::KB;
+template <int WFMT, int NTT, int TPI = 4>
+MOE_DEV void mma_batch(const Batch<WFMT, NTT, TPI>& b, int ntt_active, f32x4 (&acc)[NTT][TPI]) {
+    constexpr int KB = Batch<WFMT, NTT, TPI>::KB;
     #pragma unroll
     for (int i = 0; i < KB; ++i) {
         #pragma unroll
@@ -115,7 +116,7 @@ MOE_DEV void mma_batch(const Batch<WFMT, NTT>& b, int ntt_active, f32x4 (&acc)[N
                 B[0] = b.Blo[tt][i][0]; B[1] = b.Blo[tt][i][1]; B[2] = b.Blo[tt][i][2]; B[3] = b.Blo[tt][i][3];
                 B[4] = b.Bhi[tt][i][0]; B[5] = b.Bhi[tt][i][1]; B[6] = b.Bhi[tt][i][2]; B[7] = b.Bhi[tt][i][3];
                 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < TPI; ++t)
                     acc[tt][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, 0, 0>(a_operand<WFMT>(b.A[i][t]), B,
                                                                         acc[tt][t], b.sA[i][t], b.sB[tt][i]);
             }
@@ -131,11 +132,16 @@ MOE_DEV void mma_batch(const Batch<WFMT, NTT>& b, int ntt_active, f32x4 (&acc)[N
 // its units and can find them in L2. RT (W1 at decode shapes): 0, or the
 // lanes per token with which every workgroup first routes and groups the
 // tokens itself in LDS (one launch fewer per layer); workgroup 0 also writes
-// the routing results to device memory for W2 and the combine.
-template <int WFMT, bool IS_W1, int NTT, int KW, int CP, int RT = 0>
+// the routing results to device memory for W2 and the combine. TPI (W2
+// only): 4, or 2 for items of half a unit (two of its four 16-row weight
+// tiles), twice as many items of half the work, which fill the last round of
+// items better when the items are few.
+template <int WFMT, bool IS_W1, int NTT, int KW, int CP, int RT = 0, int TPI = 4>
 __global__ __launch_bounds__(64 * KW, NTT == 1 ? 4 : 2)   // waves per SIMD: 4 (128 VGPRs) for one token tile
 void grouped_gemm_kernel(KParams p) {
+    static_assert(TPI == 4 || (TPI == 2 && !IS_W1), "W1 items pair gate and up tiles: whole units");
     constexpr int NT = 64 * KW;
+    constexpr int IPU = 4 / TPI;                        // items per unit
     const int rows_per_pass = 16 * NTT;
     const int G = p.G, units = p.N / 64;
 
@@ -187,18 +193,19 @@ void grouped_gemm_kernel(KParams p) {
     }
     if (w == 0) pass_prefix(cnt_tab, G, rows_per_pass, lane, pass_off);
     __syncthreads();
-    const int n_items = pass_off[G] * units;
+    const int n_items = pass_off[G] * units * IPU;
 
     const rsrc_t rx = make_rsrc(p.aq, p.aq_bytes);
     const rsrc_t rxs = make_rsrc(p.as, p.as_bytes);
     // this wave's contiguous run of K-tiles, in whole batches (batches of KB
     // K-tiles start at multiples of KB, and KB divides 4)
-    constexpr int KB = Batch<WFMT, NTT>::KB;
+    constexpr int KB = Batch<WFMT, NTT, TPI>::KB;
     const int nbt = (p.kt + KB - 1) / KB;
     const int kt0 = ((w * nbt) / KW) * KB, kt1 = min(p.kt, (((w + 1) * nbt) / KW) * KB);
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int pg = item / units, u = item - pg * units;
+        const int pg = item / (units * IPU), ui = item - pg * units * IPU;
+        const int u = ui / IPU, t0 = (ui - u * IPU) * TPI;     // unit, its first tile of this item
         int glo = 0, ghi = G;                           // largest g with pass_off[g] <= pg
         while (ghi - glo > 1) {
             const int mid = (glo + ghi) >> 1;
@@ -215,12 +222,12 @@ void grouped_gemm_kernel(KParams p) {
         const int nrows = min(rows_per_pass, n_g - pass * rows_per_pass);
         const int ntt_active = (nrows + 15) / 16;
 
-        f32x4 acc[NTT][4];
+        f32x4 acc[NTT][TPI];
         uint32_t xoff[NTT], xsoff[NTT];
         #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
             #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < TPI; ++t) acc[tt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int r = tt * 16 + (lane & 15);
             const long xr = r < nrows ? (rsrc_tab ? (long)rsrc_tab[rbase + r] : (long)(rbase + r)) : -1;
             xoff[tt] = xr >= 0 ? (uint32_t)(xr * p.K) : kInvalid;
@@ -228,16 +235,16 @@ void grouped_gemm_kernel(KParams p) {
         }
 
         for (int ktb = kt0; ktb < kt1; ktb += KB) {
-            Batch<WFMT, NTT> b;
-            load_batch<WFMT, NTT, CP>(b, ktb, kt1, lane, rw, rs, rx, rxs, xoff, xsoff);
-            mma_batch<WFMT, NTT>(b, ntt_active, acc);
+            Batch<WFMT, NTT, TPI> b;
+            load_batch<WFMT, NTT, CP, TPI>(b, ktb, kt1, lane, rw, rs, rx, rxs, xoff, xsoff, t0);
+            mma_batch<WFMT, NTT, TPI>(b, ntt_active, acc);
         }
 
         // Sum the KW waves' partials in a fixed tree order through KW/2 LDS
         // slots: in the round of half-width h, waves [h, 2h) store, waves
         // [0, h) add; the total ends up in wave 0 and is stored to slot 0.
         auto slot = [&](int s_, int tt, int t, int v) -> float& {
-            return red[(((s_ * NTT + tt) * 4 + t) * 4 + v) * 64 + lane];
+            return red[(((s_ * NTT + tt) * TPI + t) * 4 + v) * 64 + lane];
         };
         #pragma unroll
         for (int h = KW / 2; h >= 1; h >>= 1) {
@@ -245,7 +252,7 @@ void grouped_gemm_kernel(KParams p) {
                 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt)
                     #pragma unroll
-                    for (int t = 0; t < 4; ++t)
+                    for (int t = 0; t < TPI; ++t)
                         #pragma unroll
                         for (int v = 0; v < 4; ++v) slot(w - h, tt, t, v) = acc[tt][t][v];
             }
@@ -254,7 +261,7 @@ void grouped_gemm_kernel(KParams p) {
                 #pragma unroll
                 for (int tt = 0; tt < NTT; ++tt)
                     #pragma unroll
-                    for (int t = 0; t < 4; ++t)
+                    for (int t = 0; t < TPI; ++t)
                         #pragma unroll
                         for (int v = 0; v < 4; ++v) acc[tt][t][v] += slot(w, tt, t, v);
             }
@@ -264,7 +271,7 @@ void grouped_gemm_kernel(KParams p) {
             #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
                 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < TPI; ++t)
                     #pragma unroll
                     for (int v = 0; v < 4; ++v) slot(0, tt, t, v) = acc[tt][t][v];
         }
@@ -326,17 +333,17 @@ void grouped_gemm_kernel(KParams p) {
             }
         } else {
             const int H = p.N;
-            for (int e = tid; e < NTT * 256; e += NT) {
-                const int le = e & 63, t = (e >> 6) & 3, tt = e >> 8;
+            for (int e = tid; e < NTT * 64 * TPI; e += NT) {
+                const int le = e & 63, t = (e >> 6) % TPI, tt = e / (64 * TPI);
                 const int tok = tt * 16 + (le & 15);
                 if (tok >= nrows) continue;
                 float s[4];
                 #pragma unroll
-                for (int v = 0; v < 4; ++v) s[v] = red[((tt * 4 + t) * 4 + v) * 64 + le];
+                for (int v = 0; v < 4; ++v) s[v] = red[((tt * TPI + t) * 4 + v) * 64 + le];
                 uint2 o;
                 o.x = f32_to_bf16(s[0]) | (f32_to_bf16(s[1]) << 16);
                 o.y = f32_to_bf16(s[2]) | (f32_to_bf16(s[3]) << 16);
-                *(uint2*)(p.y + (size_t)(rbase + tok) * H + 64 * u + 16 * t + 4 * (le >> 4)) = o;
+                *(uint2*)(p.y + (size_t)(rbase + tok) * H + 64 * u + 16 * (t0 + t) + 4 * (le >> 4)) = o;
             }
         }
         __syncthreads();
@@ -350,27 +357,27 @@ inline size_t route_lds_ints(const KParams& p, int KW) {
            block_lds_ints(KW, p.G, p.E_loc);
 }
 
-template <int WFMT, bool IS_W1, int NTT, int KW, int CP, int RT = 0>
+template <int WFMT, bool IS_W1, int NTT, int KW, int CP, int RT = 0, int TPI = 4>
 int launch(const KParams& p, long max_items, hipStream_t stream) {
-    auto kern = grouped_gemm_kernel<WFMT, IS_W1, NTT, KW, CP, RT>;
+    auto kern = grouped_gemm_kernel<WFMT, IS_W1, NTT, KW, CP, RT, TPI>;
     const size_t lds = (size_t)((p.G + 4) & ~3) * 4 + (size_t)(KW / 2) * NTT * 1024 * 4 +
                        (IS_W1 ? (size_t)16 * NTT * 33 * 4 : 0) + (RT ? route_lds_ints(p, KW) * 4 : 0);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * KW, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
-    const long grid = std::max<long>(1, std::min<long>(max_items, (long)per_cu * device_cu_count()));
+    const long grid = std::max<long>(1, std::min<long>(max_items * (4 / TPI), (long)per_cu * device_cu_count()));
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * KW), lds, stream, p);
     return (int)hipGetLastError();
 }
 
 // 16 K-split waves only with one token tile: 1024-thread workgroups get 128
 // VGPRs, too few for more
-template <int WFMT, bool IS_W1, int NTT, int CP, int RT = 0>
+template <int WFMT, bool IS_W1, int NTT, int CP, int RT = 0, int TPI = 4>
 int launch_kw(const KParams& p, int kw, long max_items, hipStream_t stream) {
-    if constexpr (NTT == 1)
+    if constexpr (NTT == 1 && TPI == 4)
         if (kw >= 16) return launch<WFMT, IS_W1, NTT, 16, CP, RT>(p, max_items, stream);
-    if (kw >= 8) return launch<WFMT, IS_W1, NTT, 8, CP, RT>(p, max_items, stream);
-    return launch<WFMT, IS_W1, NTT, 4, CP, RT>(p, max_items, stream);
+    if (kw >= 8) return launch<WFMT, IS_W1, NTT, 8, CP, RT, TPI>(p, max_items, stream);
+    return launch<WFMT, IS_W1, NTT, 4, CP, RT, TPI>(p, max_items, stream);
 }
 
 constexpr int kTiledMinRows = 96;   // expected rows per group from which the tiled kernel runs
@@ -423,6 +430,18 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     // stream through non-temporally
     const bool reread = ntt > 1 || avg >= rpp;
     const bool fp4 = a.fmt == MOE_FMT_MXFP4;
+    // W2 streaming its weights once, with fewer items than one round of
+    // workgroups takes even at half a unit each: items of half a unit, each
+    // done in about half the time (one token: W2 7.3 -> 6.4 us). With more
+    // items, halves only thin out the weight bytes in flight per CU: at 20
+    // to 30 active experts, where the last round of whole units is partly
+    // idle, they were measured no faster (T = 32) or slower (T = 128).
+    if constexpr (!IS_W1) if (ntt == 1 && !reread) {
+        const long slots = (long)device_cu_count() * (16 / kw);
+        if (2 * items <= slots)
+            return fp4 ? launch_kw<MFMA_FMT_FP4, IS_W1, 1, kNonTemporal, 0, 2>(p, kw, max_items, stream)
+                       : launch_kw<MFMA_FMT_FP8, IS_W1, 1, kNonTemporal, 0, 2>(p, kw, max_items, stream);
+    }
     if constexpr (IS_W1) if (a.route) {
         // the layer skipped its routing launches: moe_w1_can_route held, so
         // ntt == 1 and the weights stream non-temporally
