@@ -116,14 +116,90 @@ constexpr size_t block_lds_ints(int NW, int G, int E_loc) {
     return (size_t)3 * G + ((size_t)NW * E_loc * 2 + 3) / 4;
 }
 
+// The whole S2/S3 computation for at most 64 assignments and 64 groups, in
+// one wave with neither LDS nor barriers: lane a holds assignment a, lane q
+// stands for group q. Each lane compares every lane's group with its own
+// target bit by bit, most significant first, through one ballot per bit:
+// with target q this counts group q's assignments and those of lower groups
+// (count and offset of group q); with target g(a) it finds the lower lanes of
+// the same group (the stable rank of assignment a).
+template <class IdxF, class WF>
+MOE_DEV void permute_in_wave(IdxF idx_of, WF w_of, int T, int k, int e0, int E_loc, int s,
+                             int32_t* counts, int32_t* offsets, int32_t* offsets32,
+                             int32_t* row_src, float* row_w, int32_t* slot_row, int lane) {
+    const int Tk = T * k, ks = k + s, G = E_loc + s;
+    const int gbits = group_bits(E_loc);
+    int g = -1;
+    if (lane < Tk) {
+        const int gg = idx_of(lane) - e0;
+        if (gg >= 0 && gg < E_loc) g = gg;
+    }
+    const uint64_t valid = __ballot(g >= 0);
+    const int q = lane;
+    uint64_t eq_q = valid, lt_q = 0, eq_a = valid;
+    for (int b = gbits - 1; b >= 0; --b) {
+        const uint64_t m = __ballot(g >= 0 && ((g >> b) & 1));
+        const bool qb = (q >> b) & 1;
+        lt_q = qb ? (lt_q | (eq_q & ~m)) : lt_q;
+        eq_q = qb ? (eq_q & m) : (eq_q & ~m);
+        eq_a = (g >= 0 && ((g >> b) & 1)) ? (eq_a & m) : (eq_a & ~m);
+    }
+    const int routed = __popcll(valid);
+    int cnt = 0, off = 0;
+    if (q < E_loc) {
+        cnt = __popcll(eq_q);
+        off = __popcll(lt_q);
+    } else if (q < G) {                     // the shared group: every token, after the routed rows
+        cnt = T;
+        off = routed;
+    }
+    // offsets32: exclusive scan over the groups of the 32-rounded counts
+    const int c32 = (cnt + 31) & ~31;
+    int inc = c32;
+    #pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += y;
+    }
+    if (q < G) {
+        counts[q] = cnt;
+        offsets[q] = off;
+        if (offsets32) offsets32[q] = inc - c32;
+    }
+    if (q == G - 1) {
+        offsets[G] = off + cnt;
+        if (offsets32) offsets32[G] = inc;
+    }
+    // rows of the routed assignments: the group's offset plus the stable rank
+    const int goff = __shfl(off, g >= 0 ? g : 0, 64);
+    if (lane < Tk) {
+        const int row = g >= 0 ? goff + __popcll(eq_a & lanemask_lt(lane)) : -1;
+        write_row(lane, g, row, k, ks, g >= 0 ? w_of(lane) : 0.f, row_src, row_w, slot_row);
+    }
+    if (s)
+        for (int t = lane; t < T; t += 64) {
+            const int r = routed + t;
+            row_src[r] = t;
+            row_w[r] = 1.0f;
+            slot_row[(size_t)t * ks + k] = r;
+        }
+}
+
 // The whole S2/S3 computation of up to 4096 assignments in one workgroup of
 // NW waves. idx_of(a) / w_of(a) read the routing of flattened assignment a.
+// At most 64 assignments and 64 groups: wave 0 alone (permute_in_wave).
 template <int NW, class IdxF, class WF>
 MOE_DEV void permute_in_block(IdxF idx_of, WF w_of, int T, int k, int e0, int E_loc, int s,
                               int32_t* counts, int32_t* offsets, int32_t* offsets32,
                               int32_t* row_src, float* row_w, int32_t* slot_row, int* lds) {
     constexpr int NT = NW * 64;
     const int G = E_loc + s;
+    if (T * k <= 64 && G <= 64) {
+        if (threadIdx.x < 64)
+            permute_in_wave(idx_of, w_of, T, k, e0, E_loc, s, counts, offsets, offsets32, row_src,
+                            row_w, slot_row, (int)threadIdx.x);
+        return;
+    }
     int* hist = lds;                       // [G]   counts, then offsets
     int* tmp = hist + G;                   // [G]   chunk totals
     int* base = tmp + G;                   // [G]   running row of each group
