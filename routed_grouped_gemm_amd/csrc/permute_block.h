@@ -116,42 +116,59 @@ constexpr size_t block_lds_ints(int NW, int G, int E_loc) {
     return (size_t)3 * G + ((size_t)NW * E_loc * 2 + 3) / 4;
 }
 
-// The whole S2/S3 computation for at most 64 assignments and 64 groups, in
-// one wave with neither LDS nor barriers: lane a holds assignment a, lane q
-// stands for group q. Each lane compares every lane's group with its own
-// target bit by bit, most significant first, through one ballot per bit:
-// with target q this counts group q's assignments and those of lower groups
-// (count and offset of group q); with target g(a) it finds the lower lanes of
-// the same group (the stable rank of assignment a).
-template <class IdxF, class WF>
+// The whole S2/S3 computation for at most 64 * APL assignments and 64 groups,
+// in one wave with neither LDS nor barriers: slot i of lane l holds
+// assignment a = 64 i + l, lane q stands for group q. Each lane compares the
+// groups of every lane's slot i with its own target bit by bit, most
+// significant first, through one ballot per slot and bit: with target q this
+// counts group q's assignments in each slot and those of lower groups (count
+// and offset of group q); with target g(a) it finds the lower lanes of the
+// same group in a's slot. An assignment's row is then its group's offset,
+// plus the group's assignments in earlier slots, plus its rank in its slot:
+// stable in a.
+template <int APL, class IdxF, class WF>
 MOE_DEV void permute_in_wave(IdxF idx_of, WF w_of, int T, int k, int e0, int E_loc, int s,
                              int32_t* counts, int32_t* offsets, int32_t* offsets32,
                              int32_t* row_src, float* row_w, int32_t* slot_row, int lane) {
     const int Tk = T * k, ks = k + s, G = E_loc + s;
     const int gbits = group_bits(E_loc);
-    int g = -1;
-    if (lane < Tk) {
-        const int gg = idx_of(lane) - e0;
-        if (gg >= 0 && gg < E_loc) g = gg;
-    }
-    const uint64_t valid = __ballot(g >= 0);
     const int q = lane;
-    uint64_t eq_q = valid, lt_q = 0, eq_a = valid;
-    for (int b = gbits - 1; b >= 0; --b) {
-        const uint64_t m = __ballot(g >= 0 && ((g >> b) & 1));
-        const bool qb = (q >> b) & 1;
-        lt_q = qb ? (lt_q | (eq_q & ~m)) : lt_q;
-        eq_q = qb ? (eq_q & m) : (eq_q & ~m);
-        eq_a = (g >= 0 && ((g >> b) & 1)) ? (eq_a & m) : (eq_a & ~m);
+    int g[APL];
+    uint64_t eq_q[APL], lt_q[APL], eq_a[APL];
+    #pragma unroll
+    for (int i = 0; i < APL; ++i) {
+        const int a = 64 * i + lane;
+        g[i] = -1;
+        if (a < Tk) {
+            const int gg = idx_of(a) - e0;
+            if (gg >= 0 && gg < E_loc) g[i] = gg;
+        }
+        eq_q[i] = eq_a[i] = __ballot(g[i] >= 0);
+        lt_q[i] = 0;
     }
-    const int routed = __popcll(valid);
-    int cnt = 0, off = 0;
-    if (q < E_loc) {
-        cnt = __popcll(eq_q);
-        off = __popcll(lt_q);
-    } else if (q < G) {                     // the shared group: every token, after the routed rows
-        cnt = T;
-        off = routed;
+    for (int b = gbits - 1; b >= 0; --b) {
+        const bool qb = (q >> b) & 1;
+        #pragma unroll
+        for (int i = 0; i < APL; ++i) {
+            const bool gb = g[i] >= 0 && ((g[i] >> b) & 1);
+            const uint64_t m = __ballot(gb);
+            lt_q[i] = qb ? (lt_q[i] | (eq_q[i] & ~m)) : lt_q[i];
+            eq_q[i] = qb ? (eq_q[i] & m) : (eq_q[i] & ~m);
+            eq_a[i] = gb ? (eq_a[i] & m) : (eq_a[i] & ~m);
+        }
+    }
+    int routed = 0, cnt = 0, off = 0;
+    int before[APL];                        // group q's assignments in slots < i
+    #pragma unroll
+    for (int i = 0; i < APL; ++i) {
+        before[i] = cnt;
+        routed += __popcll(__ballot(g[i] >= 0));
+        cnt += __popcll(eq_q[i]);
+        off += __popcll(lt_q[i]);
+    }
+    if (q >= E_loc) {                       // the shared group (every token, after the routed rows), or none
+        cnt = q < G ? T : 0;
+        off = q < G ? routed : 0;
     }
     // offsets32: exclusive scan over the groups of the 32-rounded counts
     const int c32 = (cnt + 31) & ~31;
@@ -170,11 +187,14 @@ MOE_DEV void permute_in_wave(IdxF idx_of, WF w_of, int T, int k, int e0, int E_l
         offsets[G] = off + cnt;
         if (offsets32) offsets32[G] = inc;
     }
-    // rows of the routed assignments: the group's offset plus the stable rank
-    const int goff = __shfl(off, g >= 0 ? g : 0, 64);
-    if (lane < Tk) {
-        const int row = g >= 0 ? goff + __popcll(eq_a & lanemask_lt(lane)) : -1;
-        write_row(lane, g, row, k, ks, g >= 0 ? w_of(lane) : 0.f, row_src, row_w, slot_row);
+    #pragma unroll
+    for (int i = 0; i < APL; ++i) {
+        const int base = __shfl(off + before[i], g[i] >= 0 ? g[i] : 0, 64);
+        const int a = 64 * i + lane;
+        if (a < Tk) {
+            const int row = g[i] >= 0 ? base + __popcll(eq_a[i] & lanemask_lt(lane)) : -1;
+            write_row(a, g[i], row, k, ks, g[i] >= 0 ? w_of(a) : 0.f, row_src, row_w, slot_row);
+        }
     }
     if (s)
         for (int t = lane; t < T; t += 64) {
@@ -187,17 +207,26 @@ MOE_DEV void permute_in_wave(IdxF idx_of, WF w_of, int T, int k, int e0, int E_l
 
 // The whole S2/S3 computation of up to 4096 assignments in one workgroup of
 // NW waves. idx_of(a) / w_of(a) read the routing of flattened assignment a.
-// At most 64 assignments and 64 groups: wave 0 alone (permute_in_wave).
+// At most 256 assignments and 64 groups: wave 0 alone (permute_in_wave).
 template <int NW, class IdxF, class WF>
 MOE_DEV void permute_in_block(IdxF idx_of, WF w_of, int T, int k, int e0, int E_loc, int s,
                               int32_t* counts, int32_t* offsets, int32_t* offsets32,
                               int32_t* row_src, float* row_w, int32_t* slot_row, int* lds) {
     constexpr int NT = NW * 64;
     const int G = E_loc + s;
-    if (T * k <= 64 && G <= 64) {
-        if (threadIdx.x < 64)
-            permute_in_wave(idx_of, w_of, T, k, e0, E_loc, s, counts, offsets, offsets32, row_src,
-                            row_w, slot_row, (int)threadIdx.x);
+    if (T * k <= 256 && G <= 64) {
+        if (threadIdx.x < 64) {
+            const int Tk = T * k, l = (int)threadIdx.x;
+            if (Tk <= 64)
+                permute_in_wave<1>(idx_of, w_of, T, k, e0, E_loc, s, counts, offsets, offsets32,
+                                   row_src, row_w, slot_row, l);
+            else if (Tk <= 128)
+                permute_in_wave<2>(idx_of, w_of, T, k, e0, E_loc, s, counts, offsets, offsets32,
+                                   row_src, row_w, slot_row, l);
+            else
+                permute_in_wave<4>(idx_of, w_of, T, k, e0, E_loc, s, counts, offsets, offsets32,
+                                   row_src, row_w, slot_row, l);
+        }
         return;
     }
     int* hist = lds;                       // [G]   counts, then offsets

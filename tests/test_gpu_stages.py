@@ -80,8 +80,11 @@ PERMUTE_CASES = [
     (16384, 64, 6, 0, 64, False, 256),      # chunked path (count / scan / scatter)
     (700, 2048, 8, 0, 2048, True, 256),     # many experts, chunked
     (4000, 16, 1, 3, 10, True, 512),        # k = 1, partial share, single workgroup at the edge
-    # at most 64 assignments and 64 groups: one wave does the whole grouping
-    (8, 256, 8, 0, 32, True, 512),          # 64 assignments, the limit, with a shared expert
+    # at most 256 assignments and 64 groups: one wave does the whole grouping
+    (8, 256, 8, 0, 32, True, 512),          # 64 assignments: one per lane, with a shared expert
+    (16, 64, 8, 0, 40, False, 256),         # 128 assignments: two per lane
+    (30, 32, 4, 5, 20, True, 256),          # 120 assignments, partial share
+    (31, 256, 8, 0, 64, False, 256),        # 248 assignments over 64 groups
     (3, 16, 4, 2, 13, True, 256),           # partial share
     (64, 4, 1, 0, 4, False, 256),           # k = 1, 64 tokens
     (5, 64, 8, 0, 63, True, 256),           # 64 groups, the limit
