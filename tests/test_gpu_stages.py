@@ -85,6 +85,10 @@ PERMUTE_CASES = [
     (16, 64, 8, 0, 40, False, 256),         # 128 assignments: two per lane
     (30, 32, 4, 5, 20, True, 256),          # 120 assignments, partial share
     (31, 256, 8, 0, 64, False, 256),        # 248 assignments over 64 groups
+    # past the one-wave limits: the workgroup path
+    (100, 64, 6, 0, 50, True, 256),         # 600 assignments, shared expert
+    (128, 128, 8, 0, 63, True, 256),        # 1024 assignments, 64 groups
+    (33, 16, 8, 3, 13, False, 256),         # 264 assignments: just past 256
     (3, 16, 4, 2, 13, True, 256),           # partial share
     (64, 4, 1, 0, 4, False, 256),           # k = 1, 64 tokens
     (5, 64, 8, 0, 63, True, 256),           # 64 groups, the limit
