@@ -29,7 +29,13 @@
 //    instead of 256 scattered 4-byte reads.
 //  - One barrier per K-tile. The loop runs over the workgroup's whole
 //    sequence of (item, K-tile) steps, so the next item's first K-tile is in
-//    flight while an item's epilogue runs.
+//    flight while an item's epilogue runs. Within a K-tile each wave keeps its
+//    4 weight tiles in registers and streams its 8 token tiles from LDS
+//    through two register buffers: the next token tile's reads are in flight
+//    while the current one's 4 MFMAs run.
+//  - Memory requests that an item waits for are issued together: the routing
+//    weights of the item's rows (W1 epilogue) and the source rows of the next
+//    item, one latency each per item.
 //  - Epilogues run on the accumulators. W1: gate and up of the same feature
 //    sit in the same lane (the prepacked units pair them), so
 //    h = SiLU(gate) * up * w is formed in place; the 32 features of a unit are
