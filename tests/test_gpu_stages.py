@@ -232,6 +232,8 @@ W2_CASES = [
     ([200], 768, 384, "e2m1"),
     ([0, 1, 255, 256, 257, 600, 33], 512, 256, "e4m3"),
     ([300, 17, 513], 1024, 512, "e2m1"),
+    # enough items (9 groups x 64 units) that the decode kernel keeps whole units
+    ([5, 1, 0, 20, 3, 7, 2, 16, 40], 4096, 256, "e4m3"),
 ]
 
 
