@@ -154,9 +154,25 @@ void permute_scan_lds_kernel(int32_t* __restrict__ chunk_hist, int nchunks, int 
     int* h = lds;                                  // [nchunks][ld]
     int* cnt = h + nchunks * ld;                   // [G]: counts, then offsets
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    for (int i = tid; i < nchunks * E_loc; i += kScanThreads) {
-        const int c = i / E_loc;
-        h[c * ld + (i - c * E_loc)] = chunk_hist[i];
+    // in batches of 16 values per thread, all requested before any is stored
+    // (one memory latency per batch, not per value)
+    constexpr int kB = 16;
+    const int n = nchunks * E_loc;
+    for (int i0 = 0; i0 < n; i0 += kB * kScanThreads) {
+        int v[kB];
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int i = i0 + u * kScanThreads + tid;
+            v[u] = i < n ? chunk_hist[i] : 0;
+        }
+        #pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int i = i0 + u * kScanThreads + tid;
+            if (i < n) {
+                const int c = i / E_loc;
+                h[c * ld + (i - c * E_loc)] = v[u];
+            }
+        }
     }
     __syncthreads();
     const int per = (nchunks + 63) / 64;
