@@ -378,16 +378,22 @@ def main():
                 call(T, v, copies[v % len(copies)])
         g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 4
-        e0.record(stream)
-        for _ in range(reps):
+        # 8 back-to-back replays, each between its own pair of events: the
+        # mean over all of them, and the min / median / max of the per-replay
+        # means (each over the 16 routing draws)
+        reps = 8
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
             g.replay()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * N_VARIANTS)
+        us = ev[0].elapsed_time(ev[reps]) * 1e3 / (reps * N_VARIANTS)
+        each = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / N_VARIANTS for i in range(reps))
         b = sum(layer_bytes(T, c.E, c.H, c.I, active[T, v], fp4) for v in range(N_VARIANTS)) / N_VARIANTS
         per_t[str(T)] = {"latency_us": round(us, 2), "TBps": round(b / us / 1e6, 3),
+                         "latency_us_min_median_max": [round(each[0], 2), round((each[3] + each[4]) / 2, 2),
+                                                       round(each[-1], 2)],
                          "active_experts": round(sum(active[T, v] for v in range(N_VARIANTS)) / N_VARIANTS, 2)}
     reps = max(16, args.steps)
 
