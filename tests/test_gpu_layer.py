@@ -122,6 +122,26 @@ def test_layer_small_every_element(name, kw, flags):
     assert_layer_close(bf16_bits(out), ref.out, "out")
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_layer_no_local_rows(T):
+    """No token picks a local expert: the GEMMs have no work item, and every
+    output element must still be written, as an exact zero, over a buffer
+    that held NaNs."""
+    c = replace(synth.config("tiny"), T=T, E=64, k=2, n_local=4)
+    lg = synth.logits(c)
+    picked = set(omoe.route(lg, c.k)[0].ravel().tolist())
+    e0 = next(e for e in range(0, c.E - c.n_local + 1) if not picked & set(range(e, e + c.n_local)))
+    c = replace(c, e0=e0)
+    banner(f"layer without local rows {c}")
+    _, xq, xs, w1, w2, _ = _oracle_inputs(c)
+    pw1, pw2 = _packed(w1, c.w_fmt, True), _packed(w2, c.w_fmt, False)
+    ws = moe.LayerWorkspace(c.T, c.E, c.k, c.n_local, c.H, c.I)
+    out = torch.full((c.T, c.H), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.uint16)   # BF16 NaN
+    moe.moe_layer(dev(lg), dev(xq), dev(xs), pw1, pw2, c.k, c.e0, c.n_local, out=out, ws=ws)
+    assert host(ws.view("counts")).sum() == 0
+    np.testing.assert_array_equal(host(out), np.zeros((c.T, c.H), np.uint16))
+
+
 def _transpose_tol(dh, ref, c):
     n = sum((int(ref.perm.counts[g]) + 31) // 32 * 32 for g in range(c.G))
     t = np.zeros((c.I, n))
