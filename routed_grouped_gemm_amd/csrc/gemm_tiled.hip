@@ -171,12 +171,14 @@ MOE_DEV void stage_all(const KParams& p, rsrc_t rx, rsrc_t rxs, const Ctx& c, in
 }
 
 // Quad transpose of bytes: lane k of each group of 4 lanes receives byte k of
-// the dword `x` of every lane of its quad, lane i's byte in byte i.
+// the dword `x` of every lane of its quad, lane i's byte in byte i. Every
+// lane is active and reads a lane of its own quad, so the broadcasts need no
+// fallback value (one DPP move each).
 MOE_DEV uint32_t quad_byte_transpose(uint32_t x, int lane) {
-    const uint32_t q0 = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x00, 0xF, 0xF, false);  // quad_perm(0,0,0,0)
-    const uint32_t q1 = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x55, 0xF, 0xF, false);  // (1,1,1,1)
-    const uint32_t q2 = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xAA, 0xF, 0xF, false);  // (2,2,2,2)
-    const uint32_t q3 = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xFF, 0xF, 0xF, false);  // (3,3,3,3)
+    const uint32_t q0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x00, 0xF, 0xF, true);  // quad_perm(0,0,0,0)
+    const uint32_t q1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x55, 0xF, 0xF, true);  // (1,1,1,1)
+    const uint32_t q2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xAA, 0xF, 0xF, true);  // (2,2,2,2)
+    const uint32_t q3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xFF, 0xF, 0xF, true);  // (3,3,3,3)
     const uint32_t k = (uint32_t)(lane & 3);
     // v_perm_b32(a, b, sel): selector byte values 0-3 pick bytes of b, 4-7 bytes of a
     const uint32_t sel01 = (k) | ((k + 4) << 8);                        // byte0 = b[k], byte1 = a[k]

@@ -69,17 +69,17 @@ MOE_DEV uint32_t f32_to_e2m1(float v) {
 // A zero or fp32-subnormal amax gives code 0.
 template <int EMAX, uint32_t MAXMANT>
 MOE_DEV uint32_t mx_scale_code(float amax, bool ceil_rule) {
-    uint32_t u = __float_as_uint(amax);
-    int e32 = (int)(u >> 23);                      // biased exponent; 0 for zero/subnormal
-    // e32 == 0 gives code <= 1 - EMAX <= 0, clamped to 0 below (no branch)
-    int code = e32 - EMAX;                         // (e32 - 127 - EMAX) + 127
-    if (ceil_rule) {
-        // amax <= max_finite * 2^(e-emax) iff its mantissa <= the max element's mantissa
-        // max_finite = (1 + MAXMANT/2^23) * 2^EMAX
-        code += ((u & 0x7FFFFFu) > MAXMANT) ? 1 : 0;
-    }
-    code = code < 0 ? 0 : (code > 254 ? 254 : code);
-    return (uint32_t)code;
+    // ceil rule: amax <= max_finite * 2^(e - emax) iff its mantissa is at most
+    // the largest element's, max_finite = (1 + MAXMANT / 2^23) * 2^EMAX; so the
+    // exponent goes up by one iff the mantissa exceeds MAXMANT, which is the
+    // carry out of the mantissa field when 2^23 - 1 - MAXMANT is added to the
+    // bits (at most one carry: both terms are below 2^23)
+    const uint32_t u = __float_as_uint(amax) + (ceil_rule ? 0x7FFFFFu - MAXMANT : 0u);
+    // biased exponent minus EMAX, i.e. (e32 - 127 - EMAX) + 127; a zero or
+    // subnormal amax (e32 = 0, or 1 after a carry) gives a negative code,
+    // clamped to 0
+    const int code = (int)(u >> 23) - EMAX;
+    return (uint32_t)(code < 0 ? 0 : (code > 254 ? 254 : code));
 }
 // E4M3: emax 8, max 448 = 1.75 * 2^8 (mantissa 0x600000); E2M1: emax 2, max 6 = 1.5 * 2^2.
 MOE_DEV uint32_t e4m3_scale_code(float amax, bool ceil_rule) { return mx_scale_code<8, 0x600000u>(amax, ceil_rule); }
@@ -122,12 +122,17 @@ MOE_DEV float silu(float g) { return g / (1.0f + __expf(-g)); }
 // nearest even.
 MOE_DEV float e4m3_clamp(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
 // codes of a, b in bytes 0, 1
+// (the converter writes one 16-bit half of its destination and keeps the
+// other: the first conversion's other half is don't-care, so it is given a
+// register that dies there instead of a zeroed one)
 MOE_DEV uint32_t e4m3x2(float a, float b) {
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false) & 0xFFFFu;
+    const float ca = e4m3_clamp(a);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, e4m3_clamp(b), __float_as_int(ca), false) & 0xFFFFu;
 }
 // codes of a, b, c, d in bytes 0..3
 MOE_DEV uint32_t e4m3x4(float a, float b, float c, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+    const float ca = e4m3_clamp(a);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ca, e4m3_clamp(b), __float_as_int(ca), false);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true);
 }
 typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
