@@ -265,9 +265,12 @@ size_t  moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_
                                  int32_t H, int32_t I, int32_t s, uint32_t flags);
 
 /*
- * Run route -> permute -> W1 -> W2 -> combine on `stream`: 4 launches when
- * T <= 64 (router and grouping share one workgroup), more otherwise. The
- * grouped token rows are not materialised: W1 reads them through row_src.
+ * Run route -> permute -> W1 -> W2 -> combine on `stream`. With at most 256
+ * experts, k <= 16 and at most 513 groups: 3 launches when T <= 8 and groups
+ * average under 16 rows without the transposed copy (every W1 workgroup
+ * routes and groups the tokens itself), 4 when T <= 64 (router and grouping
+ * share one workgroup), more otherwise. The grouped token rows are not
+ * materialised: W1 reads them through row_src.
  * Intermediates live in ws at offsets given by moe_layer_workspace_offsets.
  */
 int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
