@@ -19,7 +19,9 @@ for the dominant kernel (the grouped W1 GEMM), timed with HIP events around
 its launches on the launching stream, with "traffic" the HBM bytes per launch
 measured by hardware counters (profiles/decode_w1_hbm_traffic.txt; null once
 the kernel sources differ from those the counters were taken with);
-"cpu_baseline" times the CPU oracle on
+"hbm_read_measured" is the HBM read rate of a plain streaming read (the
+library's read probe over 2 GiB), with the step value and the W1 rate as
+fractions of it; "cpu_baseline" times the CPU oracle on
 a bounded sample (the T=8 call of one routing draw). "other_workloads"
 gives the layer latency, TB/s, TFLOP/s and roofline fraction of the tiny,
 full-expert, 16K-token prefill and shared-expert workloads (graph replay),
@@ -432,6 +434,27 @@ def main():
                 "kernel": "grouped_gemm_kernel (W1, MXFP4)",
                 "avg_launch_us": round(w1_ms * 1e3 / nlaunch, 2), "launches": nlaunch}
 
+    # the measured HBM read rate: the library's plain streaming read of 2 GiB
+    # (one pass per launch), 20 launches between HIP events on their stream
+    nb = 1 << 31
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(moe.MOE_HBM_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        moe.moe_hbm_read_probe(buf, sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(20):
+        moe.moe_hbm_read_probe(buf, sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    read_tbps = nb * 20 / (a.elapsed_time(b) * 1e-3) / 1e12
+    del buf, sink
+    hbm_read = {"kernel": "hbm_read_kernel: one streaming read of 2 GiB per launch",
+                "TBps": round(read_tbps, 3), "frac_of_peak": round(read_tbps * 1e3 / HBM_PEAK_GBS, 4),
+                "value_over_measured": round(value / read_tbps, 4),
+                "roofline_over_measured": round(w1_gbs / 1e3 / read_tbps, 4)}
+    log(f"measured HBM read rate: {hbm_read}")
+
     others = None
     if not args.no_other_workloads:
         others = other_workloads(torch, moe, synth, device, ["tiny", "full", "prefill", "shared"])
@@ -465,6 +488,7 @@ def main():
         "per_T": per_t,
         "eager_TBps": round(eager_tbps, 4),
         "roofline": roofline,
+        "hbm_read_measured": hbm_read,
         "cpu_baseline": cpu,
         "other_workloads": others,
     }

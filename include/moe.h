@@ -130,6 +130,18 @@ int32_t moe_prepack_weights(const uint8_t* q, const uint8_t* sc, int32_t G, int3
 int32_t moe_quantize_mx(const float* src, int32_t rows, int32_t K, int32_t fmt,
                         uint32_t flags, uint8_t* q, uint8_t* s, hipStream_t stream);
 
+/*
+ * HBM read-rate probe (a measurement utility, not a step of the layer): one
+ * plain streaming read of `bytes` of device memory at `src`, the practical
+ * read rate that the bandwidth-bound kernels are compared with. Every
+ * 16-byte chunk is read once; the chunks are folded with XOR into one word
+ * per wave, written to sink [MOE_HBM_PROBE_SINK_WORDS] (the XOR of all sink
+ * words is the XOR of all 4-byte words of the buffer). bytes % 16 == 0,
+ * bytes <= 2^31; 0 bytes enqueues nothing.
+ */
+#define MOE_HBM_PROBE_SINK_WORDS 8192
+int32_t moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* ---- S1: route -------------------------------------------------------- */
 /*
  * Top-k softmax router (k appears on the GC-MoE page only in the limit

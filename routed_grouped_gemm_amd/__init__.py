@@ -69,6 +69,22 @@ def moe_quantize_mx(src: torch.Tensor, fmt: int, flags: int = 0, q=None, s=None,
     return q, s
 
 
+MOE_HBM_PROBE_SINK_WORDS = 8192
+
+
+def moe_hbm_read_probe(src: torch.Tensor, sink=None, stream=None):
+    """One streaming read of the bytes of `src` (a measurement utility).
+    Returns sink (uint32 words, int32 dtype); their XOR is the XOR of the
+    buffer's 4-byte words."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise MoeError("src must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(MOE_HBM_PROBE_SINK_WORDS, dtype=torch.int32, device=src.device)
+    _check(lib.moe_hbm_read_probe(_p(src), nbytes, _p(sink), _stream(stream)), "moe_hbm_read_probe")
+    return sink
+
+
 class PackedWeights:
     """Prepacked expert weights (device buffer + its moe_weights descriptor)."""
 

@@ -40,6 +40,7 @@ SIGNATURES = {
     "moe_prepacked_size": (SZ, [I32, I32, I32, I32]),
     "moe_prepack_weights": (I32, [P, P, I32, I32, I32, I32, I32, P, SZ, P]),
     "moe_quantize_mx": (I32, [P, I32, I32, I32, U32, P, P, P]),
+    "moe_hbm_read_probe": (I32, [P, SZ, P, P]),
     "moe_route": (I32, [P, I32, I32, I32, U32, P, P, P]),
     "moe_permute_workspace_size": (SZ, [I32, I32, I32]),
     "moe_permute": (I32, [P, P, I32, I32, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]),

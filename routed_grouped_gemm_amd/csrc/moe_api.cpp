@@ -110,6 +110,14 @@ MOE_EXPORT int32_t moe_quantize_mx(const float* src, int32_t rows, int32_t K, in
     return hip_status(moe_launch_quantize(src, rows, K, fmt, flags, q, s, stream));
 }
 
+MOE_EXPORT int32_t moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
+                                      hipStream_t stream) {
+    if (bytes % 16 || bytes > ((size_t)1 << 31)) return MOE_ERR_SHAPE;
+    if (bytes == 0) return MOE_OK;
+    if (!src || !sink) return MOE_ERR_NULL;
+    return hip_status(moe_launch_hbm_read_probe(src, bytes, sink, stream));
+}
+
 // ------------------------------------------------------------------ route
 MOE_EXPORT int32_t moe_route(const float* logits, int32_t T, int32_t E_tot, int32_t k,
                              uint32_t flags, int32_t* topk_idx, float* topk_w,

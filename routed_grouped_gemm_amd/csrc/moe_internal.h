@@ -83,6 +83,7 @@ size_t moe_tiled_scale_bytes(int R_max, int G, int K);
 
 int moe_launch_combine(const uint16_t* y, const int32_t* slot_row, const float* row_w, int T,
                        int ks, int H, uint16_t* out, hipStream_t stream);
+int moe_launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 int moe_launch_quantize(const float* src, int rows, int K, int fmt, uint32_t flags,
                         uint8_t* q, uint8_t* s, hipStream_t stream);
 int moe_launch_prepack(const uint8_t* q, const uint8_t* sc, int G, int N, int K, int fmt,

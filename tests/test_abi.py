@@ -46,6 +46,14 @@ def test_route_validation():
     assert lib.moe_route(None, 0, 8, 2, 0, None, None, None) == _lib.MOE_OK              # T = 0
 
 
+def test_hbm_read_probe_validation():
+    lib = _lib.load()
+    assert lib.moe_hbm_read_probe(None, 24, None, None) == _lib.MOE_ERR_SHAPE             # not whole chunks
+    assert lib.moe_hbm_read_probe(None, (1 << 31) + 16, None, None) == _lib.MOE_ERR_SHAPE  # over 2 GiB
+    assert lib.moe_hbm_read_probe(None, 1 << 20, None, None) == _lib.MOE_ERR_NULL
+    assert lib.moe_hbm_read_probe(None, 0, None, None) == _lib.MOE_OK                      # nothing to read
+
+
 def test_permute_validation():
     lib = _lib.load()
     args = lambda T, k, e0, El, s, H: (None, None, T, k, e0, El, s, None, None, H,  # noqa: E731

@@ -275,3 +275,18 @@ def test_combine_bit_exact(with_weight):
     out = moe.moe_combine(dev(y.view(np.int16)).view(torch.uint16), dev(slot), H,
                           row_w=dev(row_w) if with_weight else None)
     np.testing.assert_array_equal(bf16_bits(out), ref)
+
+
+# ------------------------------------------------------- HBM read-rate probe
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (64 << 20) + 1024 * 16 * 3])
+def test_hbm_read_probe_reads_every_chunk(nbytes):
+    """The probe's XOR of all sink words equals the XOR of every 4-byte word
+    of the buffer, so every chunk was read once, including a ragged last
+    pass."""
+    banner(f"hbm read probe {nbytes} bytes")
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    src = dev(words.view(np.int32))
+    sink = moe.moe_hbm_read_probe(src)
+    got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
