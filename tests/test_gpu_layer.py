@@ -61,6 +61,10 @@ SMALL = [
     ("self-route-shared-wc", dict(T=5, H=1024, I=512, E=32, k=4, e0=8, n_local=12, shared=True),
      moe.MOE_WEIGHT_AT_COMBINE),
     ("self-route-one-token", dict(T=1, E=64, k=8, e0=16, n_local=24), 0),
+    # degenerate routing: one expert (every weight exactly 1), and k = E
+    # (every token picks every expert)
+    ("single-expert", dict(T=7, E=1, k=1, n_local=1), 0),
+    ("every-expert", dict(T=9, E=4, k=4, n_local=4), 0),
     # about 275 rows per expert: the LDS-tiled GEMMs, with the transposed copy
     ("tiled-mxfp8-transpose", dict(T=1100, H=512, I=384, E=8, k=2, n_local=8, w_fmt="e4m3",
                                    transpose=True), moe.MOE_W1_WRITE_TRANSPOSE),
@@ -120,6 +124,18 @@ def test_layer_small_every_element(name, kw, flags):
         assert_mx_within_1ulp(host(hTq)[:, :n], host(hTs)[:, :n // 32], q_ref, s_ref, "hT",
                               max_frac_diff=0.02, extra_tol=_transpose_tol(dh, ref, c))
     assert_layer_close(bf16_bits(out), ref.out, "out")
+
+
+def test_layer_no_tokens():
+    """T = 0: a valid call that enqueues nothing and returns an empty output."""
+    c = replace(synth.config("tiny"), T=1)
+    _, _, _, w1, w2, _ = _oracle_inputs(c)
+    pw1, pw2 = _packed(w1, c.w_fmt, True), _packed(w2, c.w_fmt, False)
+    lg = torch.empty((0, c.E), dtype=torch.float32, device="cuda")
+    xq = torch.empty((0, c.H), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((0, c.H // 32), dtype=torch.uint8, device="cuda")
+    out = moe.moe_layer(lg, xq, xs, pw1, pw2, c.k, c.e0, c.n_local)
+    assert tuple(out.shape) == (0, c.H)
 
 
 @pytest.mark.parametrize("T", [1, 3])
