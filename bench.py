@@ -372,18 +372,16 @@ def main():
     # per-T layer latency: a graph of 16 consecutive calls (one per routing
     # draw, rotating weight copies), timed with HIP events on the replay stream
     stream = torch.cuda.current_stream()
-    per_t = {}
-    for T in DECODE_T:
+
+    def graph_latency(T, weight_copies, reps):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for v in range(N_VARIANTS):
-                call(T, v, copies[v % len(copies)])
+                call(T, v, weight_copies[v % len(weight_copies)])
         g.replay()
         torch.cuda.synchronize()
-        # 8 back-to-back replays, each between its own pair of events: the
-        # mean over all of them, and the min / median / max of the per-replay
-        # means (each over the 16 routing draws)
-        reps = 8
+        # back-to-back replays, each between its own pair of events: the mean
+        # over all of them, and the per-replay means (each over the 16 draws)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         ev[0].record(stream)
         for i in range(reps):
@@ -392,10 +390,25 @@ def main():
         torch.cuda.synchronize()
         us = ev[0].elapsed_time(ev[reps]) * 1e3 / (reps * N_VARIANTS)
         each = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / N_VARIANTS for i in range(reps))
+        return us, each
+
+    def pct(xs, q):
+        return xs[min(len(xs) - 1, max(0, round(q * (len(xs) - 1))))]
+
+    per_t = {}
+    for T in DECODE_T:
+        # 20 replays: min / p10 / median / p90 / max of the per-replay means
+        us, each = graph_latency(T, copies, 20)
         b = sum(layer_bytes(T, c.E, c.H, c.I, active[T, v], fp4) for v in range(N_VARIANTS)) / N_VARIANTS
+        # warm cache, labelled as such: every call on the same weight copy, so
+        # the weights of the smaller T stay in the 256 MB MALL between calls
+        wus, _ = graph_latency(T, copies[:1], 4)
         per_t[str(T)] = {"latency_us": round(us, 2), "TBps": round(b / us / 1e6, 3),
-                         "latency_us_min_median_max": [round(each[0], 2), round((each[3] + each[4]) / 2, 2),
+                         "latency_us_min_median_max": [round(each[0], 2), round(pct(each, 0.5), 2),
                                                        round(each[-1], 2)],
+                         "latency_us_p10_median_p90": [round(pct(each, 0.1), 2), round(pct(each, 0.5), 2),
+                                                       round(pct(each, 0.9), 2)],
+                         "warm_cache_latency_us": round(wus, 2),
                          "active_experts": round(sum(active[T, v] for v in range(N_VARIANTS)) / N_VARIANTS, 2)}
     reps = max(16, args.steps)
 
