@@ -94,7 +94,31 @@ def cpu_baseline(c8, moe_bytes_fn):
     nbytes = moe_bytes_fn(c8.T, len(active))
     return {"value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one layer call at T=8 (routing draw 0, {len(active)} active experts), "
-                      f"{dt:.2f} s wall on the host CPU, fp64 NumPy"}, dt
+                      f"{dt:.2f} s wall on the host CPU, fp64 NumPy",
+            "host": host_description()}, dt
+
+
+def host_description():
+    """The host CPU's model name, the cores this process may run on, and the
+    BLAS library NumPy calls."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas = "; ".join(libs) or blas
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "numpy_blas": blas}
 
 
 # token samples of the other workloads for the oracle's timing (about 1-5 s each)
