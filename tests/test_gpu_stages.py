@@ -262,11 +262,13 @@ def test_grouped_w2_parity(counts, H, I, fmt, kernel):
 
 
 # ------------------------------------------------------------------- combine
+# T = 1025: two tokens per workgroup, the last workgroup with one
+@pytest.mark.parametrize("T", [37, 1025])
 @pytest.mark.parametrize("with_weight", [False, True])
-def test_combine_bit_exact(with_weight):
-    banner(f"combine with_weight={with_weight}")
+def test_combine_bit_exact(with_weight, T):
+    banner(f"combine with_weight={with_weight} T={T}")
     rng = np.random.default_rng(3)
-    T, ks, H, R = 37, 9, 1024, 200
+    ks, H, R = 9, 1024, 200
     y = mx.bf16_rne(rng.standard_normal((R, H)) * 10.0 ** rng.uniform(-3, 3, (R, 1)))
     slot = rng.integers(-1, R, (T, ks)).astype(np.int32)
     slot[0] = -1                                          # token with no local slot
