@@ -262,7 +262,6 @@ def test_grouped_w2_parity(counts, H, I, fmt, kernel):
 
 
 # ------------------------------------------------------------------- combine
-# T = 1025: two tokens per workgroup, the last workgroup with one
 @pytest.mark.parametrize("T", [37, 1025])
 @pytest.mark.parametrize("with_weight", [False, True])
 def test_combine_bit_exact(with_weight, T):
