@@ -10,13 +10,15 @@ are held in several identical copies and consecutive calls rotate through
 them, as consecutive MoE layers of a model would, so a call never finds the
 previous call's weights in the 256 MB last-level cache.
 
-Each step's launch sequence is captured once per routing draw into a HIP
-graph and replayed. Printed JSON line (stdout): value = algorithmic HBM bytes
-of the step's layer calls / wall time of the steps, in TB/s. Algorithmic bytes per call: router
+The launch sequences of exactly the warm-up steps and of exactly the timed
+steps are captured into one HIP graph each and replayed once. Printed JSON
+line (stdout): value = algorithmic HBM bytes of the timed steps' layer calls /
+wall time of the timed steps, in TB/s. Algorithmic bytes per call: router
 logits, x codes + scales, the W1 and W2 codes + scales of the experts that
 received at least one token, and the BF16 output. The "roofline" object is
-for the dominant kernel (the grouped W1 GEMM), timed with HIP events around
-its launches on the launching stream, with "traffic" the HBM bytes per launch
+for the dominant kernel (the grouped W1 GEMM): a graph of its launches on
+the step sequence's groupings, in step order, timed with HIP events on the
+replay stream, with "traffic" the HBM bytes per launch
 measured by hardware counters (profiles/decode_w1_hbm_traffic.txt; null once
 the kernel sources differ from those the counters were taken with);
 "hbm_read_measured" is the HBM read rate of a plain streaming read (the
@@ -335,44 +337,37 @@ def main():
         moe.moe_layer(lg, xq, xs, w.w1, w.w2, c.k, c.e0, c.n_local, None, 0, out=outs[T], ws=wss[T])
 
     def step(i):
+        # call j of step i takes weight copy (i + j) % copies: consecutive
+        # calls never share a copy, and every T cycles through all of them
         for j, T in enumerate(DECODE_T):
-            call(T, i % N_VARIANTS, copies[(i * len(DECODE_T) + j) % len(copies)])
+            call(T, i % N_VARIANTS, copies[(i + j) % len(copies)])
 
     def step_bytes(i):
         return sum(layer_bytes(T, c.E, c.H, c.I, active[T, i % N_VARIANTS], fp4) for T in DECODE_T)
 
-    # The launch sequence is captured once into HIP graphs and replayed: one
-    # graph per single step (routing draw i % 16) and one graph holding the 16
-    # steps of a full cycle of draws, so the host never paces the GPU.
-    torch.cuda.synchronize()
-    step_graphs = []
-    for v in range(N_VARIANTS):
+    # The launch sequence of exactly the warm-up steps and of exactly the
+    # timed steps is captured into one HIP graph each and replayed once, so
+    # the host never paces the GPU and the measured work is the same
+    # whatever --steps and --warmup are.
+    def capture(first, n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(v)
-        step_graphs.append(g)
-    cycle_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(cycle_graph):
-        for v in range(N_VARIANTS):
-            step(v)
+            for i in range(first, first + n):
+                step(i)
+        return g
+
     torch.cuda.synchronize()
-
-    def run_steps(first, n):
-        i = first
-        while i < first + n:
-            if i % N_VARIANTS == 0 and first + n - i >= N_VARIANTS:
-                cycle_graph.replay()
-                i += N_VARIANTS
-            else:
-                step_graphs[i % N_VARIANTS].replay()
-                i += 1
-
-    run_steps(0, args.warmup)
+    warm_graph = capture(0, args.warmup) if args.warmup > 0 else None
+    timed_graph = capture(args.warmup, args.steps)
+    torch.cuda.synchronize()
+    if warm_graph is not None:
+        warm_graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(args.warmup, args.steps)
+    timed_graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    del warm_graph, timed_graph
     total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + args.steps))
     value = total_bytes / wall / 1e12
     ms_per_step = wall / args.steps * 1e3
@@ -434,42 +429,58 @@ def main():
                                                        round(pct(each, 0.9), 2)],
                          "warm_cache_latency_us": round(wus, 2),
                          "active_experts": round(sum(active[T, v] for v in range(N_VARIANTS)) / N_VARIANTS, 2)}
-    reps = max(16, args.steps)
 
-    # dominant kernel: grouped W1. After a layer call has grouped the tokens,
-    # W1 is launched again through its own entry point with the arguments
-    # moe_layer gives it (on another weight copy, so it streams from HBM), with
-    # HIP events around the launch on the launching stream.
-    w1_ms, w1_b = 0.0, 0
-    nlaunch = 0
+    # dominant kernel: grouped W1, launched through its own entry point on
+    # the grouping each layer call of the step sequence produced (saved per
+    # routing draw and T), with R_max = that call's row count, so the library
+    # picks the configuration moe_layer picks. One graph holds the W1
+    # launches of 16 steps in step order (T = 1, 8, 32, 128 per draw, weight
+    # copies rotating as in the steps), so, as in the steps, each launch
+    # streams its weights from HBM; HIP events on the replay stream bracket
+    # the replays, and the average launch duration is their time over the
+    # launches (the short gaps between graph nodes included).
+    grouping = {}
     for T in DECODE_T:
+        for v in range(N_VARIANTS):
+            call(T, v, dw)
+            ws = wss[T]
+            grouping[T, v] = {n: ws.view(n).clone() for n in ("counts", "offsets", "offsets32", "row_src",
+                                                               "row_w")}
+    torch.cuda.synchronize()
+
+    def w1_launch(T, v, w):
+        gsv = grouping[T, v]
+        lg, xq, xs = inputs[T][v]
         ws = wss[T]
-        hint = moe.moe_layer_rows_hint(T, c.E, c.k)
-        ahint = moe.moe_layer_active_hint(T, c.E, c.k, c.n_local, 0)
-        for r in range(reps):
-            v = r % N_VARIANTS
-            lg, xq, xs = inputs[T][v]
-            # keep the GPU busy while the host enqueues the layer call and the
-            # W1 launch, so the events see the kernel and not the enqueue time
-            torch.cuda._sleep(300000)
-            call(T, v, copies[r % len(copies)])
-            w = copies[(r + 2) % len(copies)]
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            moe.moe_grouped_w1(w.w1, ws.view("counts"), ws.view("offsets"), ws.view("row_w"), xq, xs,
-                               c.I, 0, offsets32=ws.view("offsets32"), hq=ws.view("hq"),
-                               hs=ws.view("hs"), rows_hint=hint, row_src=ws.view("row_src"),
-                               R_max=T * c.k, active_hint=ahint)
-            b.record(stream)
-            torch.cuda.synchronize()
-            w1_ms += a.elapsed_time(b)
-            w1_b += w1_bytes(rows[T, v], c.H, c.I, active[T, v], fp4)
-            nlaunch += 1
+        moe.moe_grouped_w1(w.w1, gsv["counts"], gsv["offsets"], gsv["row_w"], xq, xs, c.I, 0,
+                           offsets32=gsv["offsets32"], hq=ws.view("hq"), hs=ws.view("hs"),
+                           row_src=gsv["row_src"], R_max=max(rows[T, v], 1))
+
+    w1_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(w1_graph):
+        for v in range(N_VARIANTS):
+            for j, T in enumerate(DECODE_T):
+                w1_launch(T, v, copies[(v + j) % len(copies)])
+    w1_graph.replay()
+    torch.cuda.synchronize()
+    w1_reps = 5
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(w1_reps):
+        w1_graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    w1_ms = a.elapsed_time(b)
+    nlaunch = w1_reps * N_VARIANTS * len(DECODE_T)
+    w1_b = w1_reps * sum(w1_bytes(rows[T, v], c.H, c.I, active[T, v], fp4)
+                         for v in range(N_VARIANTS) for T in DECODE_T)
+    del w1_graph
     w1_gbs = w1_b / (w1_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(w1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(w1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": "grouped_gemm_kernel (W1, MXFP4)",
-                "avg_launch_us": round(w1_ms * 1e3 / nlaunch, 2), "launches": nlaunch}
+                "avg_launch_us": round(w1_ms * 1e3 / nlaunch, 2), "launches": nlaunch,
+                "bytes_per_launch": round(w1_b / nlaunch)}
 
     # the measured HBM read rate: the library's plain streaming read of 2 GiB
     # (one pass per launch), 20 launches between HIP events on their stream

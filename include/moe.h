@@ -70,6 +70,15 @@ extern "C" {
                                             copy of h (blocks of 32 tokens)      */
 #define MOE_SCALE_RULE_CEIL    (1u << 3) /* requantisation scale 2^ceil(log2(amax/max))
                                             instead of the OCP floor rule        */
+/* Kernel family of the grouped GEMMs (moe_grouped_w1 / moe_grouped_w2). By
+ * default the library chooses from the expected rows per group, R_max / G:
+ * below 96 the weight-streaming kernel (weights read once, K split across
+ * waves), from 96 the LDS-tiled kernel (256 x 256 workgroup tiles). These
+ * flags override the choice; setting both is MOE_ERR_UNSUPPORTED. The two
+ * families sum the fp32 partial products in different orders, so their
+ * results may differ in the last bits of the accumulation. */
+#define MOE_GEMM_STREAMED      (1u << 8)
+#define MOE_GEMM_TILED         (1u << 9)
 
 #define MOE_MAX_EXPERTS 2048
 #define MOE_MAX_SLOTS   32      /* k + s */
@@ -208,9 +217,10 @@ int32_t moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t T, int
  * backward). ldT = moe_transposed_ld(R_max, G).
  * w1 holds the routed groups [0, E_loc); w1_shared (NULL when G == E_loc)
  * holds group E_loc. hq [R_max, I], hs [R_max, I/32]; rows >= R untouched.
- * rows_hint / active_hint: expected rows per group and expected number of
- * groups with rows, used only to choose the tiling (0: derived from R_max
- * and G); results do not depend on them.
+ * The launch configuration is chosen from R_max and G alone (expected rows
+ * per group R_max / G, see MOE_GEMM_STREAMED / MOE_GEMM_TILED), so a caller
+ * gets the best configuration by passing the tightest R_max it can
+ * guarantee. R_max * I < 2^31; with the transposed copy I * ldT < 2^31.
  * ws: moe_grouped_workspace_size(...) bytes.
  */
 int32_t moe_transposed_ld(int32_t R_max, int32_t G);
@@ -219,29 +229,23 @@ int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_shared,
                        const int32_t* counts, const int32_t* offsets, const int32_t* offsets32,
                        const float* row_w, const uint8_t* xq, const uint8_t* xs,
                        const int32_t* row_src, int32_t x_rows,
-                       int32_t R_max, int32_t H, int32_t I, int32_t G, int32_t rows_hint,
-                       int32_t active_hint, uint32_t flags, uint8_t* hq, uint8_t* hs,
-                       uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes, hipStream_t stream);
+                       int32_t R_max, int32_t H, int32_t I, int32_t G, uint32_t flags,
+                       uint8_t* hq, uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
 
 /* ---- S6: grouped W2 ----------------------------------------------------- */
 /*
  * y[r] = BF16_RNE(dec(hq[r]) . dec(W2_g)^T) for every row r of group g
  * (W2 produces BF16 fragments: GC-MoE page, "Approach"). hq [R_max, I],
- * hs [R_max, I/32], y bf16 [R_max, H]; rows >= R untouched. rows_hint and
- * active_hint as for moe_grouped_w1. R_max * I < 2^31.
+ * hs [R_max, I/32], y bf16 [R_max, H]; rows >= R untouched. flags: only
+ * MOE_GEMM_STREAMED / MOE_GEMM_TILED; the configuration is chosen as for
+ * moe_grouped_w1. R_max * I < 2^31.
  */
 int32_t moe_grouped_w2(const moe_weights* w2, const moe_weights* w2_shared,
                        const int32_t* counts, const int32_t* offsets,
                        const uint8_t* hq, const uint8_t* hs,
-                       int32_t R_max, int32_t H, int32_t I, int32_t G, int32_t rows_hint,
-                       int32_t active_hint, uint16_t* y, void* ws, size_t ws_bytes,
-                       hipStream_t stream);
-
-/* The hints moe_layer passes to the grouped GEMMs, from uniform routing: the
- * expected rows of a routed group, ceil(T * k / E_tot), and the expected
- * groups with rows, ceil(E_loc * (1 - (1 - k/E_tot)^T)) + s. */
-int32_t moe_layer_rows_hint(int32_t T, int32_t E_tot, int32_t k);
-int32_t moe_layer_active_hint(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc, int32_t s);
+                       int32_t R_max, int32_t H, int32_t I, int32_t G, uint32_t flags,
+                       uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- S7: combine ---------------------------------------------------------- */
 /*

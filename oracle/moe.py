@@ -272,11 +272,15 @@ def expert_output(x_row: np.ndarray, w1q, w1s, w2q, w2s, w_fmt: str, I: int, wei
 
 
 def token_output(logit_row, xq_row, xs_row, k: int, get_expert, w_fmt: str, I: int,
-                 e0: int = 0, n_local: int | None = None, shared=None, rule: str = "ocp"):
+                 e0: int = 0, n_local: int | None = None, shared=None, rule: str = "ocp",
+                 weight_at_combine: bool = False):
     """Brute-force output of one token: route it, run each local slot's expert
     MLP on it alone, sum in fp64, round to BF16. `get_expert(g)` returns the
     local expert's (w1q, w1s, w2q, w2s) codes, so weights can be produced on
-    demand; `shared` is the shared expert's codes or None. Returns bf16 bits [H]."""
+    demand; `shared` is the shared expert's codes or None. With
+    weight_at_combine the routing weight is not applied inside the expert
+    (h is quantised unweighted) but to the expert's BF16 output, in fp64,
+    when the slots are summed. Returns bf16 bits [H]."""
     logit_row = np.asarray(logit_row, dtype=np.float32)[None, :]
     E_tot = logit_row.shape[1]
     n_local = E_tot if n_local is None else n_local
@@ -286,19 +290,25 @@ def token_output(logit_row, xq_row, xs_row, k: int, get_expert, w_fmt: str, I: i
     for j in range(k):
         g = int(idx[0, j]) - e0
         if 0 <= g < n_local:
-            out += expert_output(x, *get_expert(g), w_fmt, I, float(w[0, j]), rule)
+            wj = float(w[0, j])
+            if weight_at_combine:
+                out += expert_output(x, *get_expert(g), w_fmt, I, 1.0, rule) * wj
+            else:
+                out += expert_output(x, *get_expert(g), w_fmt, I, wj, rule)
     if shared is not None:
         out += expert_output(x, *shared, w_fmt, I, 1.0, rule)
     return mx.bf16_rne(out)
 
 
 def dense_layer(logits, xq, xs, k: int, w1q, w1s, w2q, w2s, w_fmt: str, I: int,
-                e0: int = 0, n_local: int | None = None, shared=None, rule: str = "ocp"):
+                e0: int = 0, n_local: int | None = None, shared=None, rule: str = "ocp",
+                weight_at_combine: bool = False):
     """Brute-force evaluation with no grouping: every token on its own (see
     token_output). Returns bf16 bits [T, H]. Used to pin the grouped computation."""
     T = logits.shape[0]
     get = lambda g: (w1q[g], w1s[g], w2q[g], w2s[g])  # noqa: E731
-    rows = [token_output(logits[t], xq[t], xs[t], k, get, w_fmt, I, e0, n_local, shared, rule)
+    rows = [token_output(logits[t], xq[t], xs[t], k, get, w_fmt, I, e0, n_local, shared, rule,
+                         weight_at_combine)
             for t in range(T)]
     return np.stack(rows) if rows else np.zeros((0, xq.shape[1]), np.uint16)
 

@@ -8,13 +8,15 @@ library has not been built (python routed_grouped_gemm_amd/build.py).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 
 import torch
 
 from . import _lib
-from ._lib import (MOE_FMT_MXFP4, MOE_FMT_MXFP8, MOE_ROUTE_RENORM, MOE_SCALE_RULE_CEIL,  # noqa: F401
-                   MOE_W1_WRITE_TRANSPOSE, MOE_WEIGHT_AT_COMBINE, moe_layer_args, moe_weights)
+from ._lib import (MOE_FMT_MXFP4, MOE_FMT_MXFP8, MOE_GEMM_STREAMED, MOE_GEMM_TILED,  # noqa: F401
+                   MOE_ROUTE_RENORM, MOE_SCALE_RULE_CEIL, MOE_W1_WRITE_TRANSPOSE,
+                   MOE_WEIGHT_AT_COMBINE, moe_layer_args, moe_weights)
 
 lib = _lib.load()
 
@@ -32,9 +34,16 @@ def _p(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+def _on(stream):
+    """Context in which a wrapper allocates and launches: `stream` made the
+    current stream (so the caching allocator ties every temporary and output
+    to the stream whose kernels use it), or the current stream left as it is."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _stream():
+    """Handle of the current stream (inside `_on`, the caller's stream)."""
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
@@ -61,11 +70,14 @@ def moe_quantize_mx(src: torch.Tensor, fmt: int, flags: int = 0, q=None, s=None,
     [rows, K/2] packed E2M1."""
     _dev(src, torch.float32, "src")
     rows, K = src.shape
-    if q is None:
-        q = torch.empty((rows, K if fmt == MOE_FMT_MXFP8 else K // 2), dtype=torch.uint8, device=src.device)
-    if s is None:
-        s = torch.empty((rows, K // 32), dtype=torch.uint8, device=src.device)
-    _check(lib.moe_quantize_mx(_p(src), rows, K, fmt, flags, _p(q), _p(s), _stream(stream)), "moe_quantize_mx")
+    with _on(stream):
+        if q is None:
+            q = torch.empty((rows, K if fmt == MOE_FMT_MXFP8 else K // 2), dtype=torch.uint8,
+                            device=src.device)
+        if s is None:
+            s = torch.empty((rows, K // 32), dtype=torch.uint8, device=src.device)
+        _check(lib.moe_quantize_mx(_p(src), rows, K, fmt, flags, _p(q), _p(s), _stream()),
+               "moe_quantize_mx")
     return q, s
 
 
@@ -79,9 +91,10 @@ def moe_hbm_read_probe(src: torch.Tensor, sink=None, stream=None):
     if not src.is_cuda or not src.is_contiguous():
         raise MoeError("src must be a contiguous device tensor")
     nbytes = src.numel() * src.element_size()
-    if sink is None:
-        sink = torch.empty(MOE_HBM_PROBE_SINK_WORDS, dtype=torch.int32, device=src.device)
-    _check(lib.moe_hbm_read_probe(_p(src), nbytes, _p(sink), _stream(stream)), "moe_hbm_read_probe")
+    with _on(stream):
+        if sink is None:
+            sink = torch.empty(MOE_HBM_PROBE_SINK_WORDS, dtype=torch.int32, device=src.device)
+        _check(lib.moe_hbm_read_probe(_p(src), nbytes, _p(sink), _stream()), "moe_hbm_read_probe")
     return sink
 
 
@@ -96,9 +109,10 @@ class PackedWeights:
         nbytes = moe_prepacked_size(G, N, K, fmt)
         if nbytes == 0:
             raise MoeError(f"bad weight shape G={G} N={N} K={K}")
-        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-        _check(lib.moe_prepack_weights(_p(q), _p(s), G, N, K, fmt, int(is_w1), _p(self.buf), nbytes,
-                                       _stream(stream)), "moe_prepack_weights")
+        with _on(stream):
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+            _check(lib.moe_prepack_weights(_p(q), _p(s), G, N, K, fmt, int(is_w1), _p(self.buf),
+                                           nbytes, _stream()), "moe_prepack_weights")
         self.desc = moe_weights(fmt, G, N, K, int(is_w1), 0, _p(self.buf), nbytes)
         self.G, self.N, self.K, self.fmt, self.is_w1 = G, N, K, fmt, bool(is_w1)
 
@@ -123,8 +137,9 @@ class PackedWeights:
         _dev(s, torch.uint8, "s")
         st = self.group_stride
         dst = self.buf[g * st:(g + 1) * st]
-        _check(lib.moe_prepack_weights(_p(q), _p(s), 1, self.N, self.K, self.fmt, int(self.is_w1),
-                                       _p(dst), st, _stream(stream)), "moe_prepack_weights")
+        with _on(stream):
+            _check(lib.moe_prepack_weights(_p(q), _p(s), 1, self.N, self.K, self.fmt, int(self.is_w1),
+                                           _p(dst), st, _stream()), "moe_prepack_weights")
 
     def ref(self):
         return C.byref(self.desc)
@@ -138,11 +153,13 @@ def _wref(w):
 def moe_route(logits: torch.Tensor, k: int, flags: int = 0, topk_idx=None, topk_w=None, stream=None):
     _dev(logits, torch.float32, "logits")
     T, E = logits.shape
-    if topk_idx is None:
-        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
-    if topk_w is None:
-        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
-    _check(lib.moe_route(_p(logits), T, E, k, flags, _p(topk_idx), _p(topk_w), _stream(stream)), "moe_route")
+    with _on(stream):
+        if topk_idx is None:
+            topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        if topk_w is None:
+            topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+        _check(lib.moe_route(_p(logits), T, E, k, flags, _p(topk_idx), _p(topk_w), _stream()),
+               "moe_route")
     return topk_idx, topk_w
 
 
@@ -159,26 +176,27 @@ def moe_permute(topk_idx, topk_w, e0: int, n_local: int, shared: bool, xq=None, 
     R_max = T * k + s * T
     dev = topk_idx.device
     H = xq.shape[1] if xq is not None else 256
-    out = dict(
-        counts=torch.empty(G, dtype=torch.int32, device=dev),
-        offsets=torch.empty(G + 1, dtype=torch.int32, device=dev),
-        offsets32=torch.empty(G + 1, dtype=torch.int32, device=dev),
-        row_src=torch.empty(max(R_max, 1), dtype=torch.int32, device=dev),
-        row_w=torch.empty(max(R_max, 1), dtype=torch.float32, device=dev),
-        slot_row=torch.empty((T, k + s), dtype=torch.int32, device=dev),
-    )
-    if xq is not None:
-        _dev(xq, torch.uint8, "xq")
-        _dev(xs, torch.uint8, "xs")
-        out["xq_perm"] = torch.empty((max(R_max, 1), H), dtype=torch.uint8, device=dev)
-        out["xs_perm"] = torch.empty((max(R_max, 1), H // 32), dtype=torch.uint8, device=dev)
-    nws = int(lib.moe_permute_workspace_size(T, k, G))
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    _check(lib.moe_permute(_p(topk_idx), _p(topk_w), T, k, e0, n_local, s, _p(xq), _p(xs), H,
-                           _p(out["counts"]), _p(out["offsets"]), _p(out["offsets32"]),
-                           _p(out["row_src"]), _p(out["row_w"]), _p(out["slot_row"]),
-                           _p(out.get("xq_perm")), _p(out.get("xs_perm")), _p(ws), nws,
-                           _stream(stream)), "moe_permute")
+    with _on(stream):
+        out = dict(
+            counts=torch.empty(G, dtype=torch.int32, device=dev),
+            offsets=torch.empty(G + 1, dtype=torch.int32, device=dev),
+            offsets32=torch.empty(G + 1, dtype=torch.int32, device=dev),
+            row_src=torch.empty(max(R_max, 1), dtype=torch.int32, device=dev),
+            row_w=torch.empty(max(R_max, 1), dtype=torch.float32, device=dev),
+            slot_row=torch.empty((T, k + s), dtype=torch.int32, device=dev),
+        )
+        if xq is not None:
+            _dev(xq, torch.uint8, "xq")
+            _dev(xs, torch.uint8, "xs")
+            out["xq_perm"] = torch.empty((max(R_max, 1), H), dtype=torch.uint8, device=dev)
+            out["xs_perm"] = torch.empty((max(R_max, 1), H // 32), dtype=torch.uint8, device=dev)
+        nws = int(lib.moe_permute_workspace_size(T, k, G))
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        _check(lib.moe_permute(_p(topk_idx), _p(topk_w), T, k, e0, n_local, s, _p(xq), _p(xs), H,
+                               _p(out["counts"]), _p(out["offsets"]), _p(out["offsets32"]),
+                               _p(out["row_src"]), _p(out["row_w"]), _p(out["slot_row"]),
+                               _p(out.get("xq_perm")), _p(out.get("xs_perm")), _p(ws), nws,
+                               _stream()), "moe_permute")
     return out
 
 
@@ -187,64 +205,59 @@ def moe_transposed_ld(R_max: int, G: int) -> int:
     return int(lib.moe_transposed_ld(R_max, G))
 
 
-def moe_layer_rows_hint(T: int, E_tot: int, k: int) -> int:
-    return int(lib.moe_layer_rows_hint(T, E_tot, k))
-
-
-def moe_layer_active_hint(T: int, E_tot: int, k: int, E_loc: int, s: int = 0) -> int:
-    return int(lib.moe_layer_active_hint(T, E_tot, k, E_loc, s))
-
-
 def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq, xs, I: int,
                    flags: int = 0, w1_shared: PackedWeights | None = None, offsets32=None,
-                   hq=None, hs=None, hTq=None, hTs=None, rows_hint: int = 0, row_src=None,
-                   R_max: int | None = None, active_hint: int = 0, stream=None):
+                   hq=None, hs=None, hTq=None, hTs=None, row_src=None,
+                   R_max: int | None = None, stream=None):
     """xq/xs: the grouped rows [R_max, H] (row_src None) or the token rows
-    [T, H] read through row_src (then R_max must be given)."""
+    [T, H] read through row_src (then R_max must be given). The launch
+    configuration follows R_max / counts.shape[0] (see include/moe.h)."""
     H = xq.shape[1]
     if R_max is None:
         R_max = xq.shape[0]
     G = counts.shape[0]
     dev = xq.device
-    if hq is None:
-        hq = torch.empty((R_max, I), dtype=torch.uint8, device=dev)
-    if hs is None:
-        hs = torch.empty((R_max, I // 32), dtype=torch.uint8, device=dev)
-    if (flags & MOE_W1_WRITE_TRANSPOSE) and hTq is None:
-        ld = moe_transposed_ld(R_max, G)
-        hTq = torch.empty((I, ld), dtype=torch.uint8, device=dev)
-        hTs = torch.empty((I, ld // 32), dtype=torch.uint8, device=dev)
-    nws = int(lib.moe_grouped_workspace_size(R_max, G, 2 * I, H))
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    _check(lib.moe_grouped_w1(w1.ref(), _wref(w1_shared), _p(counts), _p(offsets), _p(offsets32),
-                              _p(row_w), _p(xq), _p(xs), _p(row_src), xq.shape[0], R_max, H, I, G,
-                              rows_hint, active_hint, flags, _p(hq),
-                              _p(hs), _p(hTq), _p(hTs), _p(ws), nws, _stream(stream)), "moe_grouped_w1")
+    with _on(stream):
+        if hq is None:
+            hq = torch.empty((R_max, I), dtype=torch.uint8, device=dev)
+        if hs is None:
+            hs = torch.empty((R_max, I // 32), dtype=torch.uint8, device=dev)
+        if (flags & MOE_W1_WRITE_TRANSPOSE) and hTq is None:
+            ld = moe_transposed_ld(R_max, G)
+            hTq = torch.empty((I, ld), dtype=torch.uint8, device=dev)
+            hTs = torch.empty((I, ld // 32), dtype=torch.uint8, device=dev)
+        nws = int(lib.moe_grouped_workspace_size(R_max, G, 2 * I, H))
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        _check(lib.moe_grouped_w1(w1.ref(), _wref(w1_shared), _p(counts), _p(offsets), _p(offsets32),
+                                  _p(row_w), _p(xq), _p(xs), _p(row_src), xq.shape[0], R_max, H, I, G,
+                                  flags, _p(hq), _p(hs), _p(hTq), _p(hTs), _p(ws), nws, _stream()),
+               "moe_grouped_w1")
     return hq, hs, hTq, hTs
 
 
 def moe_grouped_w2(w2: PackedWeights, counts, offsets, hq, hs, H: int,
-                   w2_shared: PackedWeights | None = None, y=None, rows_hint: int = 0,
-                   active_hint: int = 0, stream=None):
+                   w2_shared: PackedWeights | None = None, y=None, flags: int = 0, stream=None):
     R_max, I = hq.shape
     G = counts.shape[0]
-    if y is None:
-        y = torch.empty((R_max, H), dtype=torch.uint16, device=hq.device)
-    nws = int(lib.moe_grouped_workspace_size(R_max, G, H, I))
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=hq.device)
-    _check(lib.moe_grouped_w2(w2.ref(), _wref(w2_shared), _p(counts), _p(offsets), _p(hq), _p(hs),
-                              R_max, H, I, G, rows_hint, active_hint, _p(y), _p(ws), nws, _stream(stream)),
-           "moe_grouped_w2")
+    with _on(stream):
+        if y is None:
+            y = torch.empty((R_max, H), dtype=torch.uint16, device=hq.device)
+        nws = int(lib.moe_grouped_workspace_size(R_max, G, H, I))
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=hq.device)
+        _check(lib.moe_grouped_w2(w2.ref(), _wref(w2_shared), _p(counts), _p(offsets), _p(hq), _p(hs),
+                                  R_max, H, I, G, flags, _p(y), _p(ws), nws, _stream()),
+               "moe_grouped_w2")
     return y
 
 
 # ----------------------------------------------------------------- combine
 def moe_combine(y, slot_row, H: int, row_w=None, out=None, stream=None):
     T, ks = slot_row.shape
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.uint16, device=y.device)
-    _check(lib.moe_combine(_p(y), _p(slot_row), _p(row_w), T, ks, H, _p(out), _stream(stream)),
-           "moe_combine")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.uint16, device=y.device)
+        _check(lib.moe_combine(_p(y), _p(slot_row), _p(row_w), T, ks, H, _p(out), _stream()),
+               "moe_combine")
     return out
 
 
@@ -287,6 +300,22 @@ class LayerWorkspace:
         return self.buf[o:o + nbytes].view(dt).view(shp)
 
 
+def _layer_args(logits, xq, xs, w1, w2, k, e0, n_local, shared, flags, out, hTq, hTs):
+    T, E_tot = logits.shape
+    H = xq.shape[1]
+    args = moe_layer_args()
+    args.logits, args.T, args.E_tot, args.k = _p(logits), T, E_tot, k
+    args.e0, args.E_loc = e0, n_local
+    args.xq, args.xs, args.H, args.I = _p(xq), _p(xs), H, w1.N // 2
+    args.w1, args.w2 = C.pointer(w1.desc), C.pointer(w2.desc)
+    if shared is not None:
+        args.shared_w1, args.shared_w2 = C.pointer(shared[0].desc), C.pointer(shared[1].desc)
+    args.flags = flags
+    args.hTq, args.hTs = _p(hTq), _p(hTs)
+    args.out = _p(out)
+    return args
+
+
 def moe_layer(logits, xq, xs, w1: PackedWeights, w2: PackedWeights, k: int, e0: int = 0,
               n_local: int | None = None, shared=None, flags: int = 0, out=None, ws=None,
               hTq=None, hTs=None, stream=None):
@@ -300,19 +329,18 @@ def moe_layer(logits, xq, xs, w1: PackedWeights, w2: PackedWeights, k: int, e0: 
     I = w1.N // 2
     n_local = w1.G if n_local is None else n_local
     s = 1 if shared is not None else 0
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.uint16, device=xq.device)
-    if ws is None:
-        ws = LayerWorkspace(T, E_tot, k, n_local, H, I, bool(s), flags, device=xq.device)
-    args = moe_layer_args()
-    args.logits, args.T, args.E_tot, args.k = _p(logits), T, E_tot, k
-    args.e0, args.E_loc = e0, n_local
-    args.xq, args.xs, args.H, args.I = _p(xq), _p(xs), H, I
-    args.w1, args.w2 = C.pointer(w1.desc), C.pointer(w2.desc)
-    if shared is not None:
-        args.shared_w1, args.shared_w2 = C.pointer(shared[0].desc), C.pointer(shared[1].desc)
-    args.flags = flags
-    args.hTq, args.hTs = _p(hTq), _p(hTs)
-    args.out = _p(out)
-    _check(lib.moe_layer(C.byref(args), _p(ws.buf), ws.nbytes, _stream(stream)), "moe_layer")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.uint16, device=xq.device)
+        if ws is None:
+            ws = LayerWorkspace(T, E_tot, k, n_local, H, I, bool(s), flags, device=xq.device)
+        args = _layer_args(logits, xq, xs, w1, w2, k, e0, n_local, shared, flags, out, hTq, hTs)
+        _check(lib.moe_layer(C.byref(args), _p(ws.buf), ws.nbytes, _stream()), "moe_layer")
     return out
+
+
+def layer(xq, xs, logits, w1: PackedWeights, w2: PackedWeights, k: int, e0: int = 0,
+          n_local: int | None = None, shared=None, flags: int = 0, out=None, **kw):
+    """moe_layer with the argument order of the activation-first call form
+    (x codes, x scales, router logits, weights, top-k)."""
+    return moe_layer(logits, xq, xs, w1, w2, k, e0, n_local, shared, flags, out=out, **kw)

@@ -13,6 +13,8 @@ MOE_ROUTE_RENORM = 1 << 0
 MOE_WEIGHT_AT_COMBINE = 1 << 1
 MOE_W1_WRITE_TRANSPOSE = 1 << 2
 MOE_SCALE_RULE_CEIL = 1 << 3
+MOE_GEMM_STREAMED = 1 << 8
+MOE_GEMM_TILED = 1 << 9
 
 
 class moe_weights(C.Structure):
@@ -46,11 +48,9 @@ SIGNATURES = {
     "moe_permute": (I32, [P, P, I32, I32, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_transposed_ld": (I32, [I32, I32]),
     "moe_grouped_workspace_size": (SZ, [I32, I32, I32, I32]),
-    "moe_grouped_w1": (I32, [WP, WP, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, U32, P, P, P,
+    "moe_grouped_w1": (I32, [WP, WP, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, U32, P, P, P,
                              P, P, SZ, P]),
-    "moe_grouped_w2": (I32, [WP, WP, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, SZ, P]),
-    "moe_layer_rows_hint": (I32, [I32, I32, I32]),
-    "moe_layer_active_hint": (I32, [I32, I32, I32, I32, I32]),
+    "moe_grouped_w2": (I32, [WP, WP, P, P, P, P, I32, I32, I32, I32, U32, P, P, SZ, P]),
     "moe_combine": (I32, [P, P, P, I32, I32, I32, P, P]),
     "moe_layer_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, U32]),
     "moe_layer": (I32, [C.POINTER(moe_layer_args), P, SZ, P]),

@@ -394,8 +394,14 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     // token tiles per pass, from the expected rows per group
     const int avg = expected_rows(a.rows_hint, a.R_max, a.G);
     // many rows per group: the weights are reused across many token tiles and
-    // the MFMA, not HBM, is the bound -> the LDS-tiled kernel
-    if (avg >= kTiledMinRows) return IS_W1 ? moe_launch_tiled_w1(a, stream) : moe_launch_tiled_w2(a, stream);
+    // the MFMA, not HBM, is the bound -> the LDS-tiled kernel (unless the
+    // caller asked for one family)
+    const bool tiled = (a.flags & MOE_GEMM_TILED) ||
+                       (!(a.flags & MOE_GEMM_STREAMED) && avg >= kTiledMinRows);
+    if (tiled) {
+        if (IS_W1 && a.route) return (int)hipErrorInvalidValue;      // never routes: see moe_w1_can_route
+        return IS_W1 ? moe_launch_tiled_w1(a, stream) : moe_launch_tiled_w2(a, stream);
+    }
     KParams p = make_params(a, IS_W1);
     int ntt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
     if (p.transpose && ntt < 2) ntt = 2;       // 32-token blocks must not straddle passes
@@ -476,7 +482,7 @@ bool moe_w1_can_route(int T, int E_tot, int k, int E_loc, int s, int R_max, int 
     (void)H; (void)I;
     const int G = E_loc + s;
     if (T < 1 || T > kRouteMaxT || E_tot > 256 || k > 16 || G > 513 || G < 1) return false;
-    if (flags & MOE_W1_WRITE_TRANSPOSE) return false;
+    if (flags & (MOE_W1_WRITE_TRANSPOSE | MOE_GEMM_TILED)) return false;
     const int avg = expected_rows(rows_hint, R_max, G);
     return avg < 16;
 }

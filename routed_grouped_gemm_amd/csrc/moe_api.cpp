@@ -195,36 +195,54 @@ static int32_t check_hi(int H, int I) {
     return MOE_OK;
 }
 
-static int32_t grouped_w1_impl(const moe_weights* w1, const moe_weights* w1_shared,
-                               const int32_t* counts, const int32_t* offsets,
-                               const int32_t* offsets32, const float* row_w,
-                               const uint8_t* xq_perm, const uint8_t* xs_perm,
-                               const int32_t* row_src, int32_t x_rows, int32_t R_max,
-                               int32_t H, int32_t I, int32_t G, uint32_t flags, uint8_t* hq,
-                               uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes,
-                               int rows_hint, hipStream_t stream, int active_hint = 0,
-                               const RouteArgs* route = nullptr) {
+constexpr int64_t kI32Lim = 1ll << 31;
+
+// Size limits of the grouped GEMMs that depend on scalars only: every byte
+// offset the kernels form is a 32-bit value (buffer resources), so the arrays
+// they address must stay below 2 GiB.
+static int32_t check_grouped_sizes(int R_max, int G, int x_rows, int H, int I, bool transpose) {
+    if (R_max < 0 || G < 1 || G > MOE_MAX_EXPERTS + 1) return MOE_ERR_SHAPE;
+    if ((int64_t)x_rows * H >= kI32Lim) return MOE_ERR_SHAPE;               // W1 activations
+    if ((int64_t)R_max * I >= kI32Lim) return MOE_ERR_SHAPE;                // h, read by W2
+    if (transpose && (int64_t)I * moe_transposed_ld(R_max, G) >= kI32Lim) return MOE_ERR_SHAPE;
+    // scale tiles of the LDS-tiled kernels (W1 over K = H, W2 over K = I)
+    if (moe_grouped_workspace_size(R_max, G, 2 * I, H) >= (size_t)kI32Lim ||
+        moe_grouped_workspace_size(R_max, G, H, I) >= (size_t)kI32Lim) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+static int32_t check_gemm_flags(uint32_t flags) {
+    if ((flags & MOE_GEMM_STREAMED) && (flags & MOE_GEMM_TILED)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// Everything moe_grouped_w1 checks before it enqueues; a.* filled on success.
+static int32_t prepare_w1(GemmArgs& a, const moe_weights* w1, const moe_weights* w1_shared,
+                          const int32_t* counts, const int32_t* offsets, const int32_t* offsets32,
+                          const float* row_w, const uint8_t* xq_perm, const uint8_t* xs_perm,
+                          const int32_t* row_src, int32_t x_rows, int32_t R_max, int32_t H,
+                          int32_t I, int32_t G, uint32_t flags, uint8_t* hq, uint8_t* hs,
+                          uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes) {
     int32_t st = check_hi(H, I);
     if (st) return st;
-    if (R_max < 0 || G < 1 || G > MOE_MAX_EXPERTS + 1) return MOE_ERR_SHAPE;
-    GemmArgs a{};
+    if ((st = check_gemm_flags(flags))) return st;
+    const bool transpose = (flags & MOE_W1_WRITE_TRANSPOSE) != 0;
+    if (x_rows < 1) return MOE_ERR_SHAPE;
+    if ((st = check_grouped_sizes(R_max, G, x_rows, H, I, transpose))) return st;
     st = fill_gemm_args(a, w1, w1_shared, G, 2 * I, H, 1);
     if (st) return st;
-    if (!counts || !offsets || !xq_perm || !xs_perm || !hq || !hs) return MOE_ERR_NULL;
-    if (x_rows < 1 || (int64_t)x_rows * H >= (1ll << 31)) return MOE_ERR_SHAPE;
     if (!row_src && x_rows < R_max) return MOE_ERR_SHAPE;
-    const bool transpose = (flags & MOE_W1_WRITE_TRANSPOSE) != 0;
+    if (!counts || !offsets || !xq_perm || !xs_perm || !hq || !hs) return MOE_ERR_NULL;
     if (transpose && (!hTq || !hTs || !offsets32)) return MOE_ERR_NULL;
     if (!(flags & MOE_WEIGHT_AT_COMBINE) && !row_w) return MOE_ERR_NULL;
     const size_t need = moe_grouped_workspace_size(R_max, G, 2 * I, H);
     if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
     a.counts = counts; a.offsets = offsets; a.offsets32 = offsets32; a.row_w = row_w;
     a.aq = xq_perm; a.as = xs_perm; a.row_src = row_src; a.x_rows = x_rows;
-    a.R_max = R_max; a.rows_hint = rows_hint; a.active_hint = active_hint; a.flags = flags;
+    a.R_max = R_max; a.flags = flags;
     a.hq = hq; a.hs = hs; a.hTq = hTq; a.hTs = hTs; a.ldT = moe_transposed_ld(R_max, G);
     a.ws = ws; a.ws_bytes = ws_bytes;
-    a.route = route;
-    return hip_status(moe_launch_grouped_w1(a, stream));
+    return MOE_OK;
 }
 
 MOE_EXPORT int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_shared,
@@ -232,53 +250,58 @@ MOE_EXPORT int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_s
                                   const int32_t* offsets32, const float* row_w,
                                   const uint8_t* xq, const uint8_t* xs, const int32_t* row_src,
                                   int32_t x_rows, int32_t R_max, int32_t H, int32_t I, int32_t G,
-                                  int32_t rows_hint, int32_t active_hint, uint32_t flags,
-                                  uint8_t* hq, uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
-    if (rows_hint < 0 || active_hint < 0) return MOE_ERR_SHAPE;
-    return grouped_w1_impl(w1, w1_shared, counts, offsets, offsets32, row_w, xq, xs, row_src,
-                           x_rows, R_max, H, I, G, flags, hq, hs, hTq, hTs, ws, ws_bytes, rows_hint,
-                           stream, active_hint);
+                                  uint32_t flags, uint8_t* hq, uint8_t* hs, uint8_t* hTq,
+                                  uint8_t* hTs, void* ws, size_t ws_bytes, hipStream_t stream) {
+    GemmArgs a{};
+    const int32_t st = prepare_w1(a, w1, w1_shared, counts, offsets, offsets32, row_w, xq, xs,
+                                  row_src, x_rows, R_max, H, I, G, flags, hq, hs, hTq, hTs, ws,
+                                  ws_bytes);
+    if (st) return st;
+    return hip_status(moe_launch_grouped_w1(a, stream));
 }
 
-static int32_t grouped_w2_impl(const moe_weights* w2, const moe_weights* w2_shared,
-                               const int32_t* counts, const int32_t* offsets, const uint8_t* hq,
-                               const uint8_t* hs, int32_t R_max, int32_t H, int32_t I, int32_t G,
-                               uint16_t* y, void* ws, size_t ws_bytes, int rows_hint,
-                               hipStream_t stream, int active_hint = 0) {
+// Everything moe_grouped_w2 checks before it enqueues; a.* filled on success.
+static int32_t prepare_w2(GemmArgs& a, const moe_weights* w2, const moe_weights* w2_shared,
+                          const int32_t* counts, const int32_t* offsets, const uint8_t* hq,
+                          const uint8_t* hs, int32_t R_max, int32_t H, int32_t I, int32_t G,
+                          uint32_t flags, uint16_t* y, void* ws, size_t ws_bytes) {
     int32_t st = check_hi(H, I);
     if (st) return st;
-    if (R_max < 0 || G < 1 || G > MOE_MAX_EXPERTS + 1) return MOE_ERR_SHAPE;
-    GemmArgs a{};
+    if ((st = check_gemm_flags(flags))) return st;
+    if (flags & ~(MOE_GEMM_STREAMED | MOE_GEMM_TILED)) return MOE_ERR_UNSUPPORTED;
+    if ((st = check_grouped_sizes(R_max, G, 1, H, I, false))) return st;
     st = fill_gemm_args(a, w2, w2_shared, G, H, I, 0);
     if (st) return st;
     if (!counts || !offsets || !hq || !hs || !y) return MOE_ERR_NULL;
-    if ((int64_t)R_max * I >= (1ll << 31)) return MOE_ERR_SHAPE;
     const size_t need = moe_grouped_workspace_size(R_max, G, H, I);
     if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
     a.counts = counts; a.offsets = offsets; a.aq = hq; a.as = hs; a.x_rows = R_max; a.R_max = R_max;
-    a.rows_hint = rows_hint; a.active_hint = active_hint; a.y = y;
+    a.flags = flags; a.y = y;
     a.ws = ws; a.ws_bytes = ws_bytes;
-    return hip_status(moe_launch_grouped_w2(a, stream));
+    return MOE_OK;
 }
 
 MOE_EXPORT int32_t moe_grouped_w2(const moe_weights* w2, const moe_weights* w2_shared,
                                   const int32_t* counts, const int32_t* offsets, const uint8_t* hq,
                                   const uint8_t* hs, int32_t R_max, int32_t H, int32_t I,
-                                  int32_t G, int32_t rows_hint, int32_t active_hint, uint16_t* y,
-                                  void* ws, size_t ws_bytes, hipStream_t stream) {
-    if (rows_hint < 0 || active_hint < 0) return MOE_ERR_SHAPE;
-    return grouped_w2_impl(w2, w2_shared, counts, offsets, hq, hs, R_max, H, I, G, y, ws, ws_bytes,
-                           rows_hint, stream, active_hint);
+                                  int32_t G, uint32_t flags, uint16_t* y, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    GemmArgs a{};
+    const int32_t st = prepare_w2(a, w2, w2_shared, counts, offsets, hq, hs, R_max, H, I, G, flags,
+                                  y, ws, ws_bytes);
+    if (st) return st;
+    return hip_status(moe_launch_grouped_w2(a, stream));
 }
 
-MOE_EXPORT int32_t moe_layer_active_hint(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
-                                         int32_t s) {
+// The tiling hints moe_layer gives the grouped GEMMs, from uniform routing:
+// the expected rows of a routed group, ceil(T * k / E_tot), and the expected
+// groups with rows, ceil(E_loc * (1 - (1 - k/E_tot)^T)) + s.
+static int32_t layer_active_hint(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc, int32_t s) {
     if (T <= 0 || E_tot <= 0 || k <= 0 || E_loc <= 0) return 0;
     return (int32_t)ceil(E_loc * (1.0 - pow(1.0 - (double)k / E_tot, (double)T))) + (s ? 1 : 0);
 }
 
-MOE_EXPORT int32_t moe_layer_rows_hint(int32_t T, int32_t E_tot, int32_t k) {
+static int32_t layer_rows_hint(int32_t T, int32_t E_tot, int32_t k) {
     if (T <= 0 || E_tot <= 0 || k <= 0) return 0;
     return (int32_t)(((int64_t)T * k + E_tot - 1) / E_tot);
 }
@@ -320,8 +343,10 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     if ((a->shared_w1 == nullptr) != (a->shared_w2 == nullptr)) return MOE_ERR_NULL;
     if (T < 0 || E_tot < 1 || E_tot > MOE_MAX_EXPERTS || k < 1 || k > E_tot) return MOE_ERR_SHAPE;
     if (e0 < 0 || E_loc < 1 || e0 + E_loc > E_tot || k + s > MOE_MAX_SLOTS) return MOE_ERR_SHAPE;
+    if ((int64_t)T * (k + s) >= kI32Lim) return MOE_ERR_SHAPE;
     int32_t st = check_hi(H, I);
     if (st) return st;
+    if ((st = check_gemm_flags(a->flags))) return st;
     const int G = E_loc + s;
     st = check_weights(a->w1, E_loc, 2 * I, H, 1);
     if (st) return st;
@@ -337,6 +362,8 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     if (transpose && (!a->hTq || !a->hTs)) return MOE_ERR_NULL;
     if (T == 0) return MOE_OK;
     if (!a->logits || !a->xq || !a->xs || !a->out) return MOE_ERR_NULL;
+    const int R_max = T * k + s * T;
+    if ((st = check_grouped_sizes(R_max, G, T, H, I, transpose))) return st;
     const LayerLayout L = layer_layout(T, E_tot, k, E_loc, H, I, s);
     if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
 
@@ -354,16 +381,29 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     uint16_t* y = (uint16_t*)(base + L.off[10]);
     void* scratch = base + L.off[11];
     const size_t scratch_bytes = L.total - L.off[11];
-    const int R_max = T * k + s * T;
+
+    // Both GEMMs are validated before anything is enqueued, so a failing call
+    // leaves the stream untouched.
+    GemmArgs a1{}, a2{};
+    st = prepare_w1(a1, a->w1, a->shared_w1, counts, offsets, offsets32, row_w, a->xq, a->xs,
+                    row_src, T, R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch,
+                    scratch_bytes);
+    if (st) return st;
+    st = prepare_w2(a2, a->w2, a->shared_w2, counts, offsets, hq, hs, R_max, H, I, G,
+                    a->flags & (MOE_GEMM_STREAMED | MOE_GEMM_TILED), y, scratch, scratch_bytes);
+    if (st) return st;
 
     // expected rows of a routed group under uniform routing; the shared group
     // (T rows) gets more passes from the grid's pass dimension
-    const int hint = moe_layer_rows_hint(T, E_tot, k);
+    const int hint = layer_rows_hint(T, E_tot, k);
     // expected local experts with at least one token: E_loc (1 - (1 - k/E_tot)^T), plus the shared one
-    const int active = moe_layer_active_hint(T, E_tot, k, E_loc, s);
+    const int active = layer_active_hint(T, E_tot, k, E_loc, s);
+    a1.rows_hint = a2.rows_hint = hint;
+    a1.active_hint = a2.active_hint = active;
     // few tokens: the W1 launch routes and groups them itself
     const bool self_route = moe_w1_can_route(T, E_tot, k, E_loc, s, R_max, H, I, hint, a->flags);
     const RouteArgs ra{a->logits, T, E_tot, k, e0, a->flags, topk_idx, topk_w, slot_row};
+    if (self_route) a1.route = &ra;
 
     int e;
     if (self_route) {
@@ -381,13 +421,8 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
                                scratch, stream);
         if (e) return MOE_ERR_HIP;
     }
-    st = grouped_w1_impl(a->w1, a->shared_w1, counts, offsets, offsets32, row_w, a->xq, a->xs,
-                         row_src, T, R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch,
-                         scratch_bytes, hint, stream, active, self_route ? &ra : nullptr);
-    if (st) return st;
-    st = grouped_w2_impl(a->w2, a->shared_w2, counts, offsets, hq, hs, R_max, H, I, G, y, scratch,
-                         scratch_bytes, hint, stream, active);
-    if (st) return st;
+    if ((e = moe_launch_grouped_w1(a1, stream))) return MOE_ERR_HIP;
+    if ((e = moe_launch_grouped_w2(a2, stream))) return MOE_ERR_HIP;
     const bool wc = (a->flags & MOE_WEIGHT_AT_COMBINE) != 0;
     e = moe_launch_combine(y, slot_row, wc ? row_w : nullptr, T, k + s, H, a->out, stream);
     return hip_status(e);

@@ -116,3 +116,87 @@ def test_binding_requires_device_tensors():
     import routed_grouped_gemm_amd as moe
     with pytest.raises(moe.MoeError):
         moe.moe_route(torch.zeros((2, 8), dtype=torch.float32), 2)
+
+
+def _w(fmt, G, N, K, is_w1):
+    lib = _lib.load()
+    return _lib.moe_weights(fmt, G, N, K, is_w1, 0, 0x1000, lib.moe_prepacked_size(G, N, K, fmt))
+
+
+def test_grouped_w1_status_paths():
+    """Every status moe_grouped_w1 can return from its scalar checks (nothing
+    is launched: all of them fail before the first enqueue)."""
+    lib = _lib.load()
+    F = 0x1000                                      # stands for a device pointer; never dereferenced
+    I, H, G, R = 256, 512, 4, 64
+    w = _w(_lib.MOE_FMT_MXFP4, G, 2 * I, H, 1)
+
+    def call(w1=w, counts=F, offsets=F, off32=None, row_w=F, xq=F, xs=F, row_src=None, x_rows=R,
+             R_max=R, H=H, I=I, G=G, flags=0, hq=F, hs=F, hTq=None, hTs=None, ws=F, ws_bytes=1 << 30):
+        return lib.moe_grouped_w1(C.byref(w1), None, counts, offsets, off32, row_w, xq, xs, row_src,
+                                  x_rows, R_max, H, I, G, flags, hq, hs, hTq, hTs, ws, ws_bytes, None)
+
+    both = _lib.MOE_GEMM_STREAMED | _lib.MOE_GEMM_TILED
+    assert call(flags=both) == _lib.MOE_ERR_UNSUPPORTED
+    assert call(I=200) == _lib.MOE_ERR_SHAPE                                     # I % 128
+    assert call(H=500) == _lib.MOE_ERR_SHAPE                                     # H % 256
+    assert call(x_rows=0) == _lib.MOE_ERR_SHAPE
+    assert call(R_max=1 << 23, x_rows=1 << 23, I=256) == _lib.MOE_ERR_SHAPE      # R_max * I >= 2^31
+    assert call(x_rows=(1 << 31) // H, row_src=F) == _lib.MOE_ERR_SHAPE          # x_rows * H >= 2^31
+    # I * ldT >= 2^31 with the transposed copy (ldT ~ R_max)
+    assert call(R_max=600000, x_rows=600000, flags=_lib.MOE_W1_WRITE_TRANSPOSE, off32=F, hTq=F,
+                hTs=F, H=256) == _lib.MOE_ERR_SHAPE
+    assert call(x_rows=R // 2) == _lib.MOE_ERR_SHAPE                             # ungrouped rows need row_src
+    bad = _w(_lib.MOE_FMT_MXFP4, G + 1, 2 * I, H, 1)
+    assert call(w1=bad) == _lib.MOE_ERR_SHAPE                                    # weights for other groups
+    assert call(hq=None) == _lib.MOE_ERR_NULL
+    assert call(row_w=None) == _lib.MOE_ERR_NULL                                 # weight applied in W1
+    assert call(flags=_lib.MOE_W1_WRITE_TRANSPOSE) == _lib.MOE_ERR_NULL          # no hT buffers
+    assert call(ws=None, ws_bytes=0) == _lib.MOE_ERR_WORKSPACE
+
+
+def test_grouped_w2_status_paths():
+    lib = _lib.load()
+    F = 0x1000
+    I, H, G, R = 256, 512, 4, 64
+    w = _w(_lib.MOE_FMT_MXFP8, G, H, I, 0)
+
+    def call(w2=w, counts=F, R_max=R, H=H, I=I, G=G, flags=0, y=F, ws=F, ws_bytes=1 << 30):
+        return lib.moe_grouped_w2(C.byref(w2), None, counts, F, F, F, R_max, H, I, G, flags, y, ws,
+                                  ws_bytes, None)
+
+    assert call(flags=_lib.MOE_GEMM_STREAMED | _lib.MOE_GEMM_TILED) == _lib.MOE_ERR_UNSUPPORTED
+    assert call(flags=_lib.MOE_W1_WRITE_TRANSPOSE) == _lib.MOE_ERR_UNSUPPORTED   # no W1 flags here
+    assert call(I=4224) == _lib.MOE_ERR_SHAPE                                    # I > 4096
+    assert call(R_max=1 << 23) == _lib.MOE_ERR_SHAPE                             # R_max * I >= 2^31
+    assert call(G=0) == _lib.MOE_ERR_SHAPE
+    assert call(w2=_w(_lib.MOE_FMT_MXFP8, G, H, 2 * I, 0)) == _lib.MOE_ERR_SHAPE  # K != I
+    assert call(y=None) == _lib.MOE_ERR_NULL
+    assert call(counts=None) == _lib.MOE_ERR_NULL
+    assert call(ws=None, ws_bytes=0) == _lib.MOE_ERR_WORKSPACE
+
+
+def test_combine_validation():
+    lib = _lib.load()
+    assert lib.moe_combine(None, None, None, 4, 0, 512, None, None) == _lib.MOE_ERR_SHAPE    # no slots
+    assert lib.moe_combine(None, None, None, 4, 33, 512, None, None) == _lib.MOE_ERR_SHAPE   # > 32 slots
+    assert lib.moe_combine(None, None, None, 4, 8, 500, None, None) == _lib.MOE_ERR_SHAPE    # H % 8
+    assert lib.moe_combine(None, None, None, 4, 8, 512, None, None) == _lib.MOE_ERR_NULL
+    assert lib.moe_combine(None, None, None, 0, 8, 512, None, None) == _lib.MOE_OK           # T = 0
+
+
+def test_layer_rejects_oversized_prefill_before_enqueueing():
+    """A prefill whose h would pass 2^31 bytes (T = 131072, k = 8, I = 2048)
+    is refused from its scalars alone: the call passes a NULL stream and fake
+    pointers, so any enqueue would fault instead of returning a status."""
+    lib = _lib.load()
+    w1 = _w(_lib.MOE_FMT_MXFP8, 64, 4096, 2048, 1)
+    w2 = _w(_lib.MOE_FMT_MXFP8, 64, 2048, 2048, 0)
+    args = _lib.moe_layer_args()
+    args.logits = args.xq = args.xs = args.out = 0x1000
+    args.T, args.E_tot, args.k, args.e0, args.E_loc, args.H, args.I = 131072, 64, 8, 0, 64, 2048, 2048
+    args.w1, args.w2 = C.pointer(w1), C.pointer(w2)
+    assert lib.moe_layer(C.byref(args), 0x1000, 1 << 40, None) == _lib.MOE_ERR_SHAPE
+    args.flags = _lib.MOE_GEMM_STREAMED | _lib.MOE_GEMM_TILED
+    args.T = 16
+    assert lib.moe_layer(C.byref(args), 0x1000, 1 << 40, None) == _lib.MOE_ERR_UNSUPPORTED

@@ -19,8 +19,8 @@ import synth
 pytestmark = pytest.mark.gpu
 
 moe = pytest.importorskip("routed_grouped_gemm_amd")
-from gpu_util import (MFMA_REL, assert_layer_close, assert_mx_within_1ulp, banner, bf16_bits,  # noqa: E402
-                      dev, host)
+from gpu_util import (MFMA_REL, assert_bf16_close, assert_layer_close, assert_mx_within_1ulp,  # noqa: E402
+                      banner, bf16_bits, dev, host)
 
 FMT = {"e2m1": moe.MOE_FMT_MXFP4, "e4m3": moe.MOE_FMT_MXFP8}
 
@@ -171,6 +171,7 @@ def _transpose_tol(dh, ref, c):
 
 # ---------------------------------------------------------------- full size
 _WEIGHTS = {}
+_EXPERTS = {}           # (seed, fmt, H, I, g) -> oracle codes (w1q, w1s, w2q, w2s); g = -1: shared
 
 
 def _device_weights(c):
@@ -183,12 +184,118 @@ def _device_weights(c):
     return _WEIGHTS[key]
 
 
+def _experts(c, gs):
+    """The oracle's own quantisation of experts gs (-1: the shared expert),
+    drawn from the same float32 arrays the GPU weights were made from; the
+    library's quantisation of those arrays is checked byte-identical, so the
+    GPU computes on exactly the oracle's inputs. Prepared in parallel host
+    threads (NumPy releases the interpreter lock), cached per weight set."""
+    from concurrent.futures import ThreadPoolExecutor
+    base = (c.seed, c.w_fmt, c.H, c.I)
+    if any(k[:4] != base for k in _EXPERTS):
+        _EXPERTS.clear()
+    need = sorted({g for g in gs if base + (g,) not in _EXPERTS})
+
+    def draw(g):
+        a32 = synth.shared_w1(c) if g < 0 else synth.w1(c, g)
+        b32 = synth.shared_w2(c) if g < 0 else synth.w2(c, g)
+        return g, a32, b32, mx.quantize_mx(a32, c.w_fmt), mx.quantize_mx(b32, c.w_fmt)
+
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        for i in range(0, len(need), 16):
+            for g, a32, b32, (qa, sa), (qb, sb) in ex.map(draw, need[i:i + 16]):
+                gq, gsc = moe.moe_quantize_mx(dev(a32), FMT[c.w_fmt])
+                assert np.array_equal(host(gq), qa) and np.array_equal(host(gsc), sa), f"W1[{g}] quantisation"
+                gq, gsc = moe.moe_quantize_mx(dev(b32), FMT[c.w_fmt])
+                assert np.array_equal(host(gq), qb) and np.array_equal(host(gsc), sb), f"W2[{g}] quantisation"
+                _EXPERTS[base + (g,)] = (qa, sa, qb, sb)
+    return {g: _EXPERTS[base + (g,)] for g in gs}
+
+
+def _pick_tokens(c, perm, rng, n=16, budget=48):
+    """n tokens with a local slot, spread over the rows (and so the passes) of
+    the largest group, the rest drawn at random; a token is taken while the
+    distinct local experts of the picks stay within `budget` (the oracle
+    prepares every expert a pick uses)."""
+    k = c.k
+    gl = int(np.argmax(perm.counts[:c.n_local]))
+    lo, hi = int(perm.offsets[gl]), int(perm.offsets[gl + 1])
+    spread = [int(perm.row_src[r]) for r in np.linspace(lo, hi - 1, num=min(8, hi - lo)).astype(int)]
+    local = perm.slot_row[:, :k] >= 0
+    cand = list(dict.fromkeys(spread + list(rng.permutation(np.flatnonzero(local.any(1))))))
+    picks, experts = [], set()
+    for t in cand:
+        es = _local_groups(perm, t, k)
+        if len(experts | es) <= budget:
+            picks.append(int(t))
+            experts |= es
+        if len(picks) == n:
+            break
+    return picks
+
+
+def _local_groups(perm, t, k):
+    """Local groups of token t's routed slots (from the oracle's grouping)."""
+    rows = perm.slot_row[t, :k]
+    return {int(np.searchsorted(perm.offsets, r, side="right") - 1) for r in rows if r >= 0}
+
+
+def _check_group(c, g, w, ws, perm, x32, xq_d, xs_d, hT):
+    """Every element of group g's h (codes, scales), transposed copy and y
+    rows against the oracle, computed from the oracle's own quantisation of
+    the group's token rows and weights."""
+    lo, hi = int(perm.offsets[g]), int(perm.offsets[g + 1])
+    n = hi - lo
+    if n == 0:
+        return
+    print(f"  whole group {g}: {n} rows", flush=True)
+    src = perm.row_src[lo:hi]
+    xq_g, xs_g = mx.quantize_mx(x32[src], mx.FMT_E4M3)
+    np.testing.assert_array_equal(host(xq_d)[src], xq_g)
+    np.testing.assert_array_equal(host(xs_d)[src], xs_g)
+    w1q, w1s, w2q, w2s = w
+    loc = np.array([0, n], np.int32)
+    o1 = omoe.grouped_w1(xq_g, xs_g, loc, perm.row_w[lo:hi], [w1q], [w1s], c.w_fmt, c.I,
+                         transpose=c.transpose)
+    X = np.abs(mx.dequantize_mx(xq_g, xs_g, mx.FMT_E4M3))
+    mag = X @ np.abs(mx.dequantize_mx(w1q, w1s, c.w_fmt)).T
+    gate, up = o1.acc[:, :c.I], o1.acc[:, c.I:]
+    dg, du = MFMA_REL * mag[:, :c.I], MFMA_REL * mag[:, c.I:]
+    wts = np.abs(perm.row_w[lo:hi])[:, None]
+    dh = (1.1 * (np.abs(up) + du) * dg + np.abs(omoe.silu(gate)) * du) * wts + 2e-5 * np.abs(o1.h)
+    hq_g, hs_g = host(ws.view("hq"))[lo:hi], host(ws.view("hs"))[lo:hi]
+    assert_mx_within_1ulp(hq_g, hs_g, o1.hq, o1.hs, f"group {g} h", extra_tol=dh)
+    if c.transpose:
+        off32 = np.zeros(c.G + 1, np.int64)
+        off32[1:] = np.cumsum((perm.counts.astype(np.int64) + 31) // 32 * 32)
+        n32 = (n + 31) // 32 * 32
+        c0 = int(off32[g])
+        tq = host(hT[0])[:, c0:c0 + n32]
+        ts = host(hT[1])[:, c0 // 32:(c0 + n32) // 32]
+        dT = np.zeros((c.I, n32))
+        dT[:, :n] = dh.T
+        assert_mx_within_1ulp(tq, ts, o1.hTq[0], o1.hTs[0], f"group {g} hT", extra_tol=dT)
+    # y from the oracle's own h; the bound adds what the GPU's h deviates by
+    # (within one E4M3 step, checked above) through |W2|
+    y_ref = omoe.grouped_w2(o1.hq, o1.hs, loc, [w2q], [w2s], c.w_fmt, H=c.H)
+    W2 = np.abs(mx.dequantize_mx(w2q, w2s, c.w_fmt))
+    h_gpu = mx.dequantize_mx(hq_g, hs_g, mx.FMT_E4M3)
+    dy = np.abs(h_gpu - mx.dequantize_mx(o1.hq, o1.hs, mx.FMT_E4M3)) @ W2.T + MFMA_REL * (np.abs(h_gpu) @ W2.T)
+    assert_bf16_close(bf16_bits(ws.view("y"))[lo:hi], y_ref, f"group {g} y", max_ulp=1, abs_floor=dy)
+    assert_layer_close(bf16_bits(ws.view("y"))[lo:hi], y_ref, f"group {g} y")
+
+
 FULL = [("decode", 1), ("decode", 8), ("decode", 32), ("decode", 128), ("shared", None),
         ("full", None), ("prefill", None)]
 
 
 @pytest.mark.parametrize("name,T", FULL, ids=[f"{n}-{t}" for n, t in FULL])
 def test_layer_full_size_sampled(name, T):
+    """The workload at its full size, launched as the benchmark launches it:
+    routing and grouping of every token bit-exact; every element of whole
+    groups (the largest, and the smallest non-empty one; the shared group)
+    against the oracle; 16 sampled tokens' output rows, which the oracle
+    computes one by one."""
     from synth import device
     c = synth.config(name, T)
     banner(f"full-size layer {name} T={c.T} H={c.H} I={c.I} E={c.E} k={c.k}")
@@ -212,42 +319,42 @@ def test_layer_full_size_sampled(name, T):
     perm = omoe.permute(idx_ref, w_ref, c.e0, c.n_local, c.shared)
     np.testing.assert_array_equal(host(ws.view("counts")), perm.counts)
     np.testing.assert_array_equal(host(ws.view("offsets")), perm.offsets)
+    R = int(perm.offsets[-1])
+    np.testing.assert_array_equal(host(ws.view("row_src"))[:R], perm.row_src)
+    np.testing.assert_array_equal(host(ws.view("slot_row")), perm.slot_row)
+
+    # whole groups, every element
+    x32 = synth.x(c)
+    cnt = perm.counts[:c.n_local]
+    groups = [int(np.argmax(cnt))]
+    if name in ("prefill", "full"):
+        groups.append(int(np.flatnonzero(cnt == cnt[cnt > 0].min())[0]))
+    wgt = {g: e for g, e in _experts(c, groups).items()}
+    if c.shared:
+        groups.append(c.n_local)
+        wgt[c.n_local] = _experts(c, [-1])[-1]
+    for g in groups:
+        _check_group(c, g, wgt[g], ws, perm, x32, xq_d, xs_d, (hTq, hTs))
 
     # sampled tokens, computed one by one by the oracle
-    x32 = synth.x(c)
     rng = np.random.default_rng(c.T)
+    picks = _pick_tokens(c, perm, rng, n=16, budget=64 if name == "prefill" else 40)
     local = (perm.slot_row[:, :c.k] >= 0).sum(1)
-    cand = np.flatnonzero(local > 0)
-    picks = list(rng.choice(cand, size=min(2, len(cand)), replace=False)) if len(cand) else []
     none = np.flatnonzero(local == 0)
     if len(none) and not c.shared:
         picks.append(int(none[0]))                 # a token with no local slot: exact zeros
-    cache = {}
-
-    def get_expert(g):
-        if g not in cache:
-            a32, b32 = synth.w1(c, g), synth.w2(c, g)
-            qa, sa = mx.quantize_mx(a32, c.w_fmt)
-            qb, sb = mx.quantize_mx(b32, c.w_fmt)
-            # the library's quantisation of the same draws must be identical
-            gq, gs = moe.moe_quantize_mx(dev(a32), FMT[c.w_fmt])
-            assert np.array_equal(host(gq), qa) and np.array_equal(host(gs), sa), f"W1[{g}] quantisation"
-            gq, gs = moe.moe_quantize_mx(dev(b32), FMT[c.w_fmt])
-            assert np.array_equal(host(gq), qb) and np.array_equal(host(gs), sb), f"W2[{g}] quantisation"
-            cache[g] = (qa, sa, qb, sb)
-        return cache[g]
-
-    sh = None
-    if c.shared:
-        a, b = mx.quantize_mx(synth.shared_w1(c), c.w_fmt), mx.quantize_mx(synth.shared_w2(c), c.w_fmt)
-        sh = (a[0], a[1], b[0], b[1])
+    gs = sorted(set().union(*[_local_groups(perm, t, c.k) for t in picks]))
+    print(f"  {len(picks)} sampled tokens over {len(gs)} local experts", flush=True)
+    ex = _experts(c, gs)
+    sh = _experts(c, [-1])[-1] if c.shared else None
     xq_ref, xs_ref = mx.quantize_mx(x32[picks], mx.FMT_E4M3)
     np.testing.assert_array_equal(host(xq_d)[picks], xq_ref)
     np.testing.assert_array_equal(host(xs_d)[picks], xs_ref)
-    ref_rows = np.stack([omoe.token_output(lg[t], xq_ref[i], xs_ref[i], c.k, get_expert, c.w_fmt, c.I,
+    ref_rows = np.stack([omoe.token_output(lg[t], xq_ref[i], xs_ref[i], c.k, ex.__getitem__, c.w_fmt, c.I,
                                            c.e0, c.n_local, sh) for i, t in enumerate(picks)])
     for i, t in enumerate(picks):
         if local[t] == 0 and not c.shared:
             assert np.all(got[t] == 0), f"token {t} has no local slot but a nonzero row"
         else:
             assert_layer_close(got[t], ref_rows[i], f"token {t} ({local[t]} local slots)")
+    assert_layer_close(got[picks], ref_rows, f"{len(picks)} sampled tokens together")

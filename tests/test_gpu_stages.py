@@ -155,19 +155,24 @@ W1_CASES = [
     ([0, 1, 255, 256, 257, 600, 33], 512, 256, "e4m3", (1 << 31) | moe.MOE_W1_WRITE_TRANSPOSE),
     ([300, 17, 513], 1024, 512, "e2m1", 0),
     ([520, 0, 64], 512, 384, "e4m3", moe.MOE_SCALE_RULE_CEIL | moe.MOE_W1_WRITE_TRANSPOSE),
+    # 16 weight tiles (I = 2048) x about 50 row passes: about 800 work items,
+    # so each workgroup of the LDS-tiled kernel's persistent grid walks three
+    # or four of them (the cross-item prefetch, the stage reused as epilogue
+    # scratch); ragged tails and an empty group, with the transposed copy
+    ([5000, 257, 0, 3100, 2555, 1031], 512, 2048, "e4m3", (1 << 31) | moe.MOE_W1_WRITE_TRANSPOSE),
+    ([4100, 6000, 1, 1955], 256, 2048, "e2m1", moe.MOE_SCALE_RULE_CEIL),
 ]
 
-# rows_hint picks the kernel: few expected rows per group -> the decode-shaped
-# kernel (weights streamed once, K split across waves); many -> the LDS-tiled
-# kernel (256 x 256 workgroup tiles). Both must give the same answers.
-KERNELS = {"decode": 1, "tiled": 4096}
+# The kernel family: the weight-streaming kernel (weights streamed once, K
+# split across waves) or the LDS-tiled kernel (256 x 256 workgroup tiles),
+# forced by a flag. Both must give the same answers.
+KERNELS = {"decode": moe.MOE_GEMM_STREAMED, "tiled": moe.MOE_GEMM_TILED}
 
 
 @pytest.mark.parametrize("kernel", list(KERNELS))
 @pytest.mark.parametrize("counts,H,I,fmt,flags", W1_CASES)
 def test_grouped_w1_parity(counts, H, I, fmt, flags, kernel):
     banner(f"grouped_w1 {kernel} counts={counts} H={H} I={I} fmt={fmt} flags={flags}")
-    hint = KERNELS[kernel]
     gather = bool(flags & (1 << 31))
     flags &= ~(1 << 31)
     offsets, xq, xs, row_w, w1, _ = _grouped_problem(counts, H, I, fmt, 5 + H + I)
@@ -190,13 +195,13 @@ def test_grouped_w1_parity(counts, H, I, fmt, flags, kernel):
     counts_d = dev(np.array(counts, np.int32))
     off32 = np.zeros(G + 1, np.int32)
     off32[1:] = np.cumsum((np.array(counts) + 31) // 32 * 32)
+    kflags = flags | KERNELS[kernel]
     if gather:
         hq, hs, hTq, hTs = moe.moe_grouped_w1(pw, counts_d, dev(offsets), dev(row_w), dev(tq), dev(ts), I,
-                                              flags, offsets32=dev(off32), row_src=dev(row_src), R_max=R,
-                                              rows_hint=hint)
+                                              kflags, offsets32=dev(off32), row_src=dev(row_src), R_max=R)
     else:
         hq, hs, hTq, hTs = moe.moe_grouped_w1(pw, counts_d, dev(offsets), dev(row_w), dev(xq), dev(xs), I,
-                                              flags, offsets32=dev(off32), rows_hint=hint)
+                                              kflags, offsets32=dev(off32))
     dh = _h_error_bound(xq, xs, offsets, w1, fmt, I, ref, wts)
     assert_mx_within_1ulp(host(hq)[:R], host(hs)[:R], ref.hq, ref.hs, "h", extra_tol=dh)
     if transpose:
@@ -234,6 +239,10 @@ W2_CASES = [
     ([300, 17, 513], 1024, 512, "e2m1"),
     # enough items (9 groups x 64 units) that the decode kernel keeps whole units
     ([5, 1, 0, 20, 3, 7, 2, 16, 40], 4096, 256, "e4m3"),
+    # 16 weight tiles (H = 4096) x about 50 row passes: three or four work
+    # items per workgroup of the LDS-tiled kernel, ragged tails
+    ([5000, 257, 0, 3100, 2555, 1031], 4096, 256, "e4m3"),
+    ([4100, 6000, 1, 1955], 4096, 384, "e2m1"),
 ]
 
 
@@ -248,7 +257,7 @@ def test_grouped_w2_parity(counts, H, I, fmt, kernel):
     y_ref = omoe.grouped_w2(hq, hs, offsets, [a[0] for a in w2], [a[1] for a in w2], fmt)
     pw = _packed(w2, fmt, False)
     y = moe.moe_grouped_w2(pw, dev(np.array(counts, np.int32)), dev(offsets), dev(hq), dev(hs), H,
-                           rows_hint=KERNELS[kernel])
+                           flags=KERNELS[kernel])
     # tolerance: one BF16 step, plus the scaled-MFMA inner-sum bound for
     # outputs that cancel
     hd = mx.dequantize_mx(hq, hs, mx.FMT_E4M3)

@@ -188,6 +188,26 @@ def test_weight_at_combine_variant_close():
     assert np.linalg.norm(a - b) / np.linalg.norm(a) < 2.0 ** -3
 
 
+@pytest.mark.parametrize("kw", [dict(T=8, E=8, k=2), dict(T=7, E=16, k=3, e0=4, n_local=8, shared=True)])
+def test_weight_at_combine_equals_dense(kw):
+    """The weight-at-combine placement, grouped, equals the per-token brute
+    force that applies each routing weight to the expert's BF16 output: bit
+    for bit."""
+    c = _small(**kw)
+    lg, xq, xs, w1q, w1s, w2q, w2s, sh = _quantized_inputs(c, shared=c.shared)
+    lay = moe.moe_layer(lg, xq, xs, c.k, w1q, w1s, w2q, w2s, c.w_fmt, c.I, e0=c.e0,
+                        n_local=c.n_local, shared=sh, weight_at_combine=True)
+    ref = moe.dense_layer(lg, xq, xs, c.k, w1q, w1s, w2q, w2s, c.w_fmt, c.I, e0=c.e0,
+                          n_local=c.n_local, shared=sh, weight_at_combine=True)
+    np.testing.assert_array_equal(lay.out, ref)
+    # and the unweighted h: every routed row's h equals the shared-weight-1 MLP
+    r = int(lay.perm.offsets[1])
+    if r:
+        x0 = mx.dequantize_mx(xq[lay.perm.row_src[:1]], xs[lay.perm.row_src[:1]], mx.FMT_E4M3)
+        acc = x0 @ mx.dequantize_mx(w1q[0], w1s[0], c.w_fmt).T
+        np.testing.assert_array_equal(lay.w1.h[:1], moe.swiglu_rows(acc, c.I, np.ones(1)))
+
+
 def test_algorithmic_work_formulas():
     # decode share, T=1, one active expert: 4*256 logits + 7168*(1+1/32) x +
     # 3*2048*7168*(0.5 + 1/32) weights + 2*7168 out
