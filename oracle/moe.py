@@ -123,6 +123,158 @@ def swiglu_rows(acc: np.ndarray, I: int, w: np.ndarray) -> np.ndarray:
     return silu(gate) * up * np.asarray(w, dtype=np.float64)[:, None]
 
 
+# ------------------------------------------- epilogue variants and backward
+# The fusion blog's GLU section writes the gated unit as
+# SwiGLU(x, W, V, b, c, beta) = Swish_beta(xW + b) (x) (xV + c) and names GeGLU
+# and sReLU as the other supported activations, with clamping and bias
+# addition as fused options; its kernel list has a backward member,
+# "GroupGemm + dActivation + Quantize/Transpose", whose epilogue reads the
+# GEMM output, forms the activation's derivative and quantises it. Readings
+# (the page gives no further definition):
+#  * every variant keeps the two-chunk structure: rows [0, I) of W1 feed the
+#    activation (the gate), rows [I, 2I) multiply it (up);
+#  * GeGLU uses the exact GELU, z * Phi(z) with the normal CDF Phi;
+#  * sReLU is the squared ReLU max(z, 0)^2 applied to the gate chunk;
+#  * the bias (b for the gate, c for up) is added to the GEMM output, then
+#    the clamp limits both chunks to [-limit, limit] (limit 0: no clamp);
+#  * beta is Swish's slope (SwiGLU only; beta = 1 is SiLU).
+ACT_SWIGLU, ACT_GEGLU, ACT_SRELU = 0, 1, 2
+
+
+def _normal_cdf(z):
+    from math import erf
+    return 0.5 * (1.0 + np.vectorize(erf, otypes=[np.float64])(z / np.sqrt(2.0)))
+
+
+def _normal_pdf(z):
+    return np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi)
+
+
+def activation(z, act: int = ACT_SWIGLU, beta: float = 1.0):
+    """The gate activation a(z), fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    if act == ACT_SWIGLU:
+        with np.errstate(over="ignore"):
+            return z / (1.0 + np.exp(-beta * z))
+    if act == ACT_GEGLU:
+        return z * _normal_cdf(z)
+    if act == ACT_SRELU:
+        return np.maximum(z, 0.0) ** 2
+    raise ValueError(act)
+
+
+def activation_grad(z, act: int = ACT_SWIGLU, beta: float = 1.0):
+    """da/dz, fp64: Swish_beta: s + beta z s (1 - s) with s = sigmoid(beta z);
+    GELU: Phi(z) + z phi(z); squared ReLU: 2 max(z, 0)."""
+    z = np.asarray(z, dtype=np.float64)
+    if act == ACT_SWIGLU:
+        with np.errstate(over="ignore"):
+            sg = 1.0 / (1.0 + np.exp(-beta * z))
+        return sg + beta * z * sg * (1.0 - sg)
+    if act == ACT_GEGLU:
+        return _normal_cdf(z) + z * _normal_pdf(z)
+    if act == ACT_SRELU:
+        return 2.0 * np.maximum(z, 0.0)
+    raise ValueError(act)
+
+
+def preactivation(acc, I: int, bias=None, limit: float = 0.0):
+    """Gate and up chunks after the bias and the clamp: (g, u), each [n, I]."""
+    acc = np.asarray(acc, dtype=np.float64)
+    g, u = acc[:, :I], acc[:, I:2 * I]
+    if bias is not None:
+        b = np.asarray(bias, dtype=np.float64)
+        g, u = g + b[:I], u + b[I:2 * I]
+    if limit > 0:
+        g, u = np.clip(g, -limit, limit), np.clip(u, -limit, limit)
+    return g, u
+
+
+def glu_rows(acc, I: int, w, act: int = ACT_SWIGLU, beta: float = 1.0, bias=None,
+             limit: float = 0.0):
+    """h = a(g) * u * w for W1 output rows acc [n, 2I] (gate first), with the
+    bias, clamp and activation of the variant; SwiGLU with beta = 1 and no
+    bias or clamp is swiglu_rows."""
+    g, u = preactivation(acc, I, bias, limit)
+    return activation(g, act, beta) * u * np.asarray(w, dtype=np.float64)[:, None]
+
+
+def glu_backward_rows(pre, dh, I: int, w, act: int = ACT_SWIGLU, beta: float = 1.0,
+                      limit: float = 0.0):
+    """Backward of h = a(clamp(g)) * clamp(u) * w for rows of the saved
+    pre-activation pre = [g | u] ([n, 2I], bias included, before the clamp)
+    and the incoming gradient dh [n, I]:
+      dg = dh * w * clamp(u) * a'(clamp(g)) * [|g| <= limit]
+      du = dh * w * a(clamp(g)) * [|u| <= limit]
+      dw = sum_i dh * a(clamp(g)) * clamp(u)
+    (the clamp passes the gradient where |z| <= limit; without a clamp the
+    masks are 1). Returns (d_pre [n, 2I], dw [n])."""
+    pre = np.asarray(pre, dtype=np.float64)
+    dh = np.asarray(dh, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)[:, None]
+    g, u = pre[:, :I], pre[:, I:2 * I]
+    mg = np.ones_like(g) if limit <= 0 else (np.abs(g) <= limit).astype(np.float64)
+    mu = np.ones_like(u) if limit <= 0 else (np.abs(u) <= limit).astype(np.float64)
+    gc = g if limit <= 0 else np.clip(g, -limit, limit)
+    uc = u if limit <= 0 else np.clip(u, -limit, limit)
+    a = activation(gc, act, beta)
+    dg = dh * w * uc * activation_grad(gc, act, beta) * mg
+    du = dh * w * a * mu
+    dw = np.sum(dh * a * uc, axis=1)
+    return np.concatenate([dg, du], axis=1), dw
+
+
+@dataclass
+class BwdOut:
+    dq: np.ndarray                          # uint8 [R, 2I]   E4M3 codes of [dg | du]
+    ds: np.ndarray                          # uint8 [R, 2I/32]
+    d: np.ndarray                           # fp64  [R, 2I]   unrounded
+    dh: np.ndarray                          # fp64  [R, I]    the GEMM output
+    dw: np.ndarray                          # fp64  [R]
+    dTq: list = field(default_factory=list)   # per group uint8 [2I, roundup(n_g, 32)]
+    dTs: list = field(default_factory=list)
+
+
+def grouped_w1_backward(dq_tok, ds_tok, row_src, offsets, row_w, pre_bits, w2tq, w2ts,
+                        w_fmt: str, I: int, act: int = ACT_SWIGLU, beta: float = 1.0,
+                        limit: float = 0.0, transpose: bool = False, rule: str = "ocp",
+                        groups=None) -> BwdOut:
+    """The backward GEMM of the fused W1 epilogue, per group g:
+      dh = dec(dout rows) @ dec(W2T_g)^T      (fp64; W2T_g = W2_g^T [I, H],
+                                              MX-quantised along H)
+      [dg | du], dw = glu_backward_rows(bf16 pre-activation rows, dh, ...)
+    then [dg | du] requantised to MX-E4M3 along the 2I features and, with
+    `transpose`, per group in blocks of 32 rows (as the forward's transposed
+    copy). dq_tok/ds_tok: the gradient of the layer output, E4M3 codes
+    [T, H] and E8M0 scales [T, H/32]; grouped row r reads token row_src[r].
+    pre_bits: bf16 bits [R, 2I] of the saved pre-activation."""
+    R = int(offsets[-1])
+    G = len(offsets) - 1
+    dh = np.zeros((R, I))
+    d = np.zeros((R, 2 * I))
+    dw = np.zeros(R)
+    todo = range(G) if groups is None else groups
+    pre = mx.bf16_value(np.asarray(pre_bits))
+    for g in todo:
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi > lo:
+            src = np.asarray(row_src[lo:hi])
+            D = mx.dequantize_mx(np.asarray(dq_tok)[src], np.asarray(ds_tok)[src], mx.FMT_E4M3)
+            W = mx.dequantize_mx(np.asarray(w2tq[g]), np.asarray(w2ts[g]), w_fmt)
+            dh[lo:hi] = D @ W.T
+            d[lo:hi], dw[lo:hi] = glu_backward_rows(pre[lo:hi], dh[lo:hi], I, row_w[lo:hi], act,
+                                                     beta, limit)
+    q, sc = mx.quantize_mx(d, mx.FMT_E4M3, rule)
+    out = BwdOut(q, sc, d, dh, dw)
+    if transpose:
+        for g in range(G):
+            lo, hi = int(offsets[g]), int(offsets[g + 1])
+            tq, ts = quantize_transposed(d[lo:hi], rule)
+            out.dTq.append(tq)
+            out.dTs.append(ts)
+    return out
+
+
 def quantize_transposed(h: np.ndarray, rule: str = "ocp"):
     """Transposed MX-E4M3 copy of one expert's h [n, I]: hT [I, n32] with
     n32 = roundup(n, 32), quantised in blocks of 32 tokens counted from the
@@ -148,12 +300,15 @@ class W1Out:
 
 
 def grouped_w1(xq_perm, xs_perm, offsets, row_w, w1q, w1s, w1_fmt: str, I: int,
-               transpose: bool = False, rule: str = "ocp", groups=None) -> W1Out:
+               transpose: bool = False, rule: str = "ocp", groups=None, act: int = ACT_SWIGLU,
+               beta: float = 1.0, bias=None, limit: float = 0.0) -> W1Out:
     """Per group g: acc = X_g @ W1_g^T in fp64, then the fused epilogue.
 
     xq_perm/xs_perm: E4M3 codes [R, H] and E8M0 scales [R, H/32].
     w1q/w1s: per-group sequences of W1 codes [2I, H(*1/2 for FP4)] and scales [2I, H/32].
     `groups` optionally restricts the computation to a subset of group ids.
+    act/beta/bias/limit: the epilogue variant (see glu_rows); bias is per
+    group [G][2I] or None. The default is SwiGLU with beta = 1.
     """
     R = int(offsets[-1])
     G = len(offsets) - 1
@@ -167,7 +322,11 @@ def grouped_w1(xq_perm, xs_perm, offsets, row_w, w1q, w1s, w1_fmt: str, I: int,
             X = mx.dequantize_mx(xq_perm[lo:hi], xs_perm[lo:hi], mx.FMT_E4M3)
             W = mx.dequantize_mx(np.asarray(w1q[g]), np.asarray(w1s[g]), w1_fmt)
             acc[lo:hi] = X @ W.T
-            h[lo:hi] = swiglu_rows(acc[lo:hi], I, row_w[lo:hi])
+            if act == ACT_SWIGLU and beta == 1.0 and bias is None and limit <= 0:
+                h[lo:hi] = swiglu_rows(acc[lo:hi], I, row_w[lo:hi])
+            else:
+                h[lo:hi] = glu_rows(acc[lo:hi], I, row_w[lo:hi], act, beta,
+                                    None if bias is None else bias[g], limit)
     hq, hs = mx.quantize_mx(h, mx.FMT_E4M3, rule)
     if transpose:
         for g in range(G):
@@ -234,12 +393,14 @@ class LayerOut:
 def moe_layer(logits, xq, xs, k: int, w1q, w1s, w2q, w2s, w_fmt: str, I: int,
               e0: int = 0, n_local: int | None = None, shared=None,
               renorm: bool = False, transpose: bool = False,
-              weight_at_combine: bool = False, rule: str = "ocp") -> LayerOut:
+              weight_at_combine: bool = False, rule: str = "ocp", epi=None) -> LayerOut:
     """One GPU's share of the routed MoE layer, from quantised inputs to BF16.
 
     logits f32 [T, E_tot]; xq uint8 E4M3 [T, H]; xs uint8 E8M0 [T, H/32];
     w1q/w1s/w2q/w2s: per local expert codes and scales (see grouped_w1/w2);
     shared: None or (sw1q, sw1s, sw2q, sw2s) for an always-on shared expert.
+    epi: None (SwiGLU) or a dict of the epilogue variant: act, beta, limit and
+    bias (per group [G][2I], the shared expert's last, or None).
     """
     E_tot = logits.shape[1]
     n_local = E_tot if n_local is None else n_local
@@ -252,7 +413,7 @@ def moe_layer(logits, xq, xs, k: int, w1q, w1s, w2q, w2s, w_fmt: str, I: int,
         w2q_g.append(shared[2]); w2s_g.append(shared[3])
     row_w_h = np.ones_like(perm.row_w) if weight_at_combine else perm.row_w
     o1 = grouped_w1(xq_p, xs_p, perm.offsets, row_w_h, w1q_g, w1s_g, w_fmt, I,
-                    transpose=transpose, rule=rule)
+                    transpose=transpose, rule=rule, **(epi or {}))
     H = xq.shape[1]
     y = grouped_w2(o1.hq, o1.hs, perm.offsets, w2q_g, w2s_g, w_fmt, H=H)
     out = combine(y, perm.slot_row, H, perm.row_w if weight_at_combine else None)
@@ -260,11 +421,16 @@ def moe_layer(logits, xq, xs, k: int, w1q, w1s, w2q, w2s, w_fmt: str, I: int,
 
 
 def expert_output(x_row: np.ndarray, w1q, w1s, w2q, w2s, w_fmt: str, I: int, weight: float,
-                  rule: str = "ocp") -> np.ndarray:
+                  rule: str = "ocp", epi=None, bias=None) -> np.ndarray:
     """One expert's contribution for one token, from dequantised x [H]:
-    BF16 value of W2 . Q8(SiLU(gate) * up * weight), fp64 inside."""
+    BF16 value of W2 . Q8(SiLU(gate) * up * weight), fp64 inside (or the
+    epilogue variant `epi`, with this expert's `bias`)."""
     acc = x_row[None, :] @ mx.dequantize_mx(np.asarray(w1q), np.asarray(w1s), w_fmt).T
-    h = swiglu_rows(acc, I, np.array([weight]))
+    if epi is None:
+        h = swiglu_rows(acc, I, np.array([weight]))
+    else:
+        h = glu_rows(acc, I, np.array([weight]), epi.get("act", ACT_SWIGLU), epi.get("beta", 1.0),
+                     bias, epi.get("limit", 0.0))
     hq, hs = mx.quantize_mx(h, mx.FMT_E4M3, rule)
     yv = mx.dequantize_mx(hq, hs, mx.FMT_E4M3) @ \
         mx.dequantize_mx(np.asarray(w2q), np.asarray(w2s), w_fmt).T
@@ -273,7 +439,7 @@ def expert_output(x_row: np.ndarray, w1q, w1s, w2q, w2s, w_fmt: str, I: int, wei
 
 def token_output(logit_row, xq_row, xs_row, k: int, get_expert, w_fmt: str, I: int,
                  e0: int = 0, n_local: int | None = None, shared=None, rule: str = "ocp",
-                 weight_at_combine: bool = False):
+                 weight_at_combine: bool = False, epi=None):
     """Brute-force output of one token: route it, run each local slot's expert
     MLP on it alone, sum in fp64, round to BF16. `get_expert(g)` returns the
     local expert's (w1q, w1s, w2q, w2s) codes, so weights can be produced on
@@ -287,28 +453,30 @@ def token_output(logit_row, xq_row, xs_row, k: int, get_expert, w_fmt: str, I: i
     idx, w = route(logit_row, k)
     x = mx.dequantize_mx(np.asarray(xq_row)[None, :], np.asarray(xs_row)[None, :], mx.FMT_E4M3)[0]
     out = np.zeros(x.shape[0])
+    bias = (epi or {}).get("bias")
     for j in range(k):
         g = int(idx[0, j]) - e0
         if 0 <= g < n_local:
             wj = float(w[0, j])
+            b = None if bias is None else bias[g]
             if weight_at_combine:
-                out += expert_output(x, *get_expert(g), w_fmt, I, 1.0, rule) * wj
+                out += expert_output(x, *get_expert(g), w_fmt, I, 1.0, rule, epi, b) * wj
             else:
-                out += expert_output(x, *get_expert(g), w_fmt, I, wj, rule)
+                out += expert_output(x, *get_expert(g), w_fmt, I, wj, rule, epi, b)
     if shared is not None:
-        out += expert_output(x, *shared, w_fmt, I, 1.0, rule)
+        out += expert_output(x, *shared, w_fmt, I, 1.0, rule, epi, None if bias is None else bias[n_local])
     return mx.bf16_rne(out)
 
 
 def dense_layer(logits, xq, xs, k: int, w1q, w1s, w2q, w2s, w_fmt: str, I: int,
                 e0: int = 0, n_local: int | None = None, shared=None, rule: str = "ocp",
-                weight_at_combine: bool = False):
+                weight_at_combine: bool = False, epi=None):
     """Brute-force evaluation with no grouping: every token on its own (see
     token_output). Returns bf16 bits [T, H]. Used to pin the grouped computation."""
     T = logits.shape[0]
     get = lambda g: (w1q[g], w1s[g], w2q[g], w2s[g])  # noqa: E731
     rows = [token_output(logits[t], xq[t], xs[t], k, get, w_fmt, I, e0, n_local, shared, rule,
-                         weight_at_combine)
+                         weight_at_combine, epi)
             for t in range(T)]
     return np.stack(rows) if rows else np.zeros((0, xq.shape[1]), np.uint16)
 
