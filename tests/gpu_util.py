@@ -76,20 +76,37 @@ def assert_mx_within_1ulp(q_gpu, s_gpu, q_ref, s_ref, what: str, max_frac_diff: 
     assert frac_q <= max_frac_diff, f"{what}: {frac_q:.3f} of codes differ"
 
 
-def assert_bf16_close(got_bits, ref_bits, what: str, max_ulp: int = 1, abs_floor=None):
-    """|got - ref| <= max_ulp BF16 steps of |ref|, plus abs_floor (the
-    propagated error of the GPU's fp32 sum, where given)."""
+def _bf16_ulp(v):
+    return np.ldexp(1.0, np.frexp(np.maximum(np.abs(v), 2.0 ** -126))[1] - 8)
+
+
+def assert_bf16_close(got_bits, ref_bits, what: str, max_ulp: int = 1, abs_floor=None, mag=None):
+    """|got - ref| <= max_ulp * (half a BF16 step of |ref| + half a step of
+    |got|), i.e. one rounding on each side, each at its own binade, plus
+    abs_floor (the propagated error of the GPU's fp32 sum and of differing
+    inputs, where given). With `mag` (the sum of |terms| of each output),
+    reports the largest error beyond the roundings and abs_floor's non-MFMA
+    part as a fraction of mag: the observed accumulation error."""
     g = mx.bf16_value(got_bits)
     r = mx.bf16_value(ref_bits)
-    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(r), 2.0 ** -126))[1] - 8)
-    tol = max_ulp * ulp
-    if abs_floor is not None:
-        tol = tol + abs_floor
+    rnd = 0.5 * max_ulp * (_bf16_ulp(r) + _bf16_ulp(g))
+    tol = rnd if abs_floor is None else rnd + abs_floor
     diff = np.abs(g - r)
     bad = diff > tol
     worst = float(np.max(diff / np.maximum(tol, 1e-300))) if diff.size else 0.0
+    extra = ""
+    if mag is not None and diff.size:
+        acc_err = np.maximum(diff - rnd - (abs_floor - MFMA_REL * mag if abs_floor is not None else 0), 0)
+        extra = f", observed accumulation error / sum|terms| {float(np.max(acc_err / np.maximum(mag, 1e-300))):.2e}"
     print(f"  {what}: bits equal {float(np.mean(got_bits == ref_bits)):.4f}, beyond tol {int(bad.sum())}, "
-          f"largest |diff| / tolerance {worst:.3f}", flush=True)
+          f"largest |diff| / tolerance {worst:.3f}{extra}", flush=True)
+    if bad.any():
+        idx = np.argsort((diff / np.maximum(tol, 1e-300)).ravel())[-3:]
+        for i in idx:
+            print(f"    got {g.ravel()[i]:.6e} ref {r.ravel()[i]:.6e} diff {diff.ravel()[i]:.3e} "
+                  f"rounding {rnd.ravel()[i]:.3e} floor "
+                  f"{(abs_floor.ravel()[i] if abs_floor is not None else 0):.3e}"
+                  + (f" mag {mag.ravel()[i]:.3e}" if mag is not None else ""), flush=True)
     assert not bad.any(), f"{what}: {int(bad.sum())} values beyond tolerance"
 
 

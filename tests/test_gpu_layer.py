@@ -280,8 +280,10 @@ def _check_group(c, g, w, ws, perm, x32, xq_d, xs_d, hT):
     y_ref = omoe.grouped_w2(o1.hq, o1.hs, loc, [w2q], [w2s], c.w_fmt, H=c.H)
     W2 = np.abs(mx.dequantize_mx(w2q, w2s, c.w_fmt))
     h_gpu = mx.dequantize_mx(hq_g, hs_g, mx.FMT_E4M3)
-    dy = np.abs(h_gpu - mx.dequantize_mx(o1.hq, o1.hs, mx.FMT_E4M3)) @ W2.T + MFMA_REL * (np.abs(h_gpu) @ W2.T)
-    assert_bf16_close(bf16_bits(ws.view("y"))[lo:hi], y_ref, f"group {g} y", max_ulp=1, abs_floor=dy)
+    mag_y = np.abs(h_gpu) @ W2.T
+    dy = np.abs(h_gpu - mx.dequantize_mx(o1.hq, o1.hs, mx.FMT_E4M3)) @ W2.T + MFMA_REL * mag_y
+    assert_bf16_close(bf16_bits(ws.view("y"))[lo:hi], y_ref, f"group {g} y", max_ulp=1, abs_floor=dy,
+                      mag=mag_y)
     assert_layer_close(bf16_bits(ws.view("y"))[lo:hi], y_ref, f"group {g} y")
 
 

@@ -267,7 +267,7 @@ def test_grouped_w2_parity(counts, H, I, fmt, kernel):
         if hi > lo:
             W = mx.dequantize_mx(w2[g][0], w2[g][1], fmt)
             mag[lo:hi] = np.abs(hd[lo:hi]) @ np.abs(W).T
-    assert_bf16_close(bf16_bits(y)[:R], y_ref, "y", max_ulp=1, abs_floor=MFMA_REL * mag)
+    assert_bf16_close(bf16_bits(y)[:R], y_ref, "y", max_ulp=1, abs_floor=MFMA_REL * mag, mag=mag)
 
 
 # ------------------------------------------------------------------- combine
