@@ -291,6 +291,23 @@ size_t  moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_
  */
 int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * moe_layer without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same kernels as moe_layer, with the workspace
+ * in a fixed array of MOE_NOALLOC_SCRATCH_BYTES inside this library, one per
+ * GPU, held from its first use until the process ends. Nothing is allocated
+ * or freed. Calls whose moe_layer_workspace_size exceeds the array return
+ * MOE_ERR_WORKSPACE with nothing enqueued (64 MiB holds the layer at up to
+ * 256 tokens of the 7168 x 2048, 32-expert decode share, or of the 6144 x 1536,
+ * 128-expert set). All calls on one GPU share that GPU's array: calls that
+ * overlap in time on the same GPU (two streams, two threads) race and must
+ * be serialised by the caller. The intermediates of the last call stay in the
+ * array; nothing carries over into the next call.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int32_t moe_layer_noalloc(const moe_layer_args* a, hipStream_t stream);
+
 /* Byte offsets of the intermediates inside the moe_layer workspace, for
  * inspection by tests: [0] topk_idx [1] topk_w [2] counts [3] offsets
  * [4] offsets32 [5] row_src [6] row_w [7] slot_row [8] hq [9] hs [10] y

@@ -339,6 +339,25 @@ def moe_layer(logits, xq, xs, w1: PackedWeights, w2: PackedWeights, k: int, e0: 
     return out
 
 
+def moe_layer_noalloc(logits, xq, xs, w1: PackedWeights, w2: PackedWeights, k: int, e0: int = 0,
+                      n_local: int | None = None, shared=None, flags: int = 0, out=None,
+                      hTq=None, hTs=None, stream=None):
+    """moe_layer with the library's fixed per-GPU workspace (no workspace
+    argument, nothing allocated by the library). `out` must be given when the
+    call must not allocate either; calls overlapping on one GPU race."""
+    _dev(logits, torch.float32, "logits")
+    _dev(xq, torch.uint8, "xq")
+    _dev(xs, torch.uint8, "xs")
+    T = logits.shape[0]
+    n_local = w1.G if n_local is None else n_local
+    with _on(stream):
+        if out is None:
+            out = torch.empty((T, xq.shape[1]), dtype=torch.uint16, device=xq.device)
+        args = _layer_args(logits, xq, xs, w1, w2, k, e0, n_local, shared, flags, out, hTq, hTs)
+        _check(lib.moe_layer_noalloc(C.byref(args), _stream()), "moe_layer_noalloc")
+    return out
+
+
 def layer(xq, xs, logits, w1: PackedWeights, w2: PackedWeights, k: int, e0: int = 0,
           n_local: int | None = None, shared=None, flags: int = 0, out=None, **kw):
     """moe_layer with the argument order of the activation-first call form

@@ -15,6 +15,7 @@ MOE_W1_WRITE_TRANSPOSE = 1 << 2
 MOE_SCALE_RULE_CEIL = 1 << 3
 MOE_GEMM_STREAMED = 1 << 8
 MOE_GEMM_TILED = 1 << 9
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class moe_weights(C.Structure):
@@ -54,6 +55,7 @@ SIGNATURES = {
     "moe_combine": (I32, [P, P, P, I32, I32, I32, P, P]),
     "moe_layer_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, U32]),
     "moe_layer": (I32, [C.POINTER(moe_layer_args), P, SZ, P]),
+    "moe_layer_noalloc": (I32, [C.POINTER(moe_layer_args), P]),
     "moe_layer_workspace_offsets": (I32, [I32, I32, I32, I32, I32, I32, I32, U32, C.POINTER(SZ)]),
 }
 

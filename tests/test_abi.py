@@ -200,3 +200,23 @@ def test_layer_rejects_oversized_prefill_before_enqueueing():
     args.flags = _lib.MOE_GEMM_STREAMED | _lib.MOE_GEMM_TILED
     args.T = 16
     assert lib.moe_layer(C.byref(args), 0x1000, 1 << 40, None) == _lib.MOE_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_workspace_beyond_its_array():
+    """The fixed workspace holds MOE_NOALLOC_SCRATCH_BYTES; a layer needing more
+    (the 16K-token prefill) is refused from its scalars, before any HIP call."""
+    lib = _lib.load()
+    T, E, k, El, H, I = 16384, 64, 6, 64, 2048, 1408
+    assert lib.moe_layer_workspace_size(T, E, k, El, H, I, 0, 0) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    w1 = _w(_lib.MOE_FMT_MXFP8, El, 2 * I, H, 1)
+    w2 = _w(_lib.MOE_FMT_MXFP8, El, H, I, 0)
+    args = _lib.moe_layer_args()
+    args.logits = args.xq = args.xs = args.out = 0x1000
+    args.T, args.E_tot, args.k, args.e0, args.E_loc, args.H, args.I = T, E, k, 0, El, H, I
+    args.w1, args.w2 = C.pointer(w1), C.pointer(w2)
+    assert lib.moe_layer_noalloc(C.byref(args), None) == _lib.MOE_ERR_WORKSPACE
+    assert lib.moe_layer_noalloc(None, None) == _lib.MOE_ERR_NULL
+    args.T = 0                                     # nothing to enqueue: no workspace needed
+    assert lib.moe_layer_noalloc(C.byref(args), None) == _lib.MOE_OK
+    args.T, args.I = 16, 200                       # other argument errors come from moe_layer's checks
+    assert lib.moe_layer_noalloc(C.byref(args), None) == _lib.MOE_ERR_SHAPE
