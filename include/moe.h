@@ -79,6 +79,35 @@ extern "C" {
  * results may differ in the last bits of the accumulation. */
 #define MOE_GEMM_STREAMED      (1u << 8)
 #define MOE_GEMM_TILED         (1u << 9)
+/* moe_layer: run the separate kernels (router, grouping, W1, W2, combine)
+ * even where the single-launch decode path applies (see moe_layer). */
+#define MOE_LAYER_SEPARATE_KERNELS (1u << 10)
+
+/* ---- epilogue variants of the fused W1 epilogue ------------------------ */
+/*
+ * The fusion blog's GLU section: SwiGLU(x, W, V, b, c, beta) =
+ * Swish_beta(xW + b) (x) (xV + c), with GeGLU and sReLU as the other
+ * activations and clamping and bias addition as fused options. Every variant
+ * keeps the gate/up structure of W1 (rows [0, I) gate, [I, 2I) up):
+ *   g = acc_gate + b, u = acc_up + c          (bias, when given)
+ *   g, u clamped to [-limit, limit]           (when limit > 0)
+ *   h = a(g) * u * w,  a = Swish_beta (z * sigmoid(beta z)),
+ *                          exact GELU (z * Phi(z)), or squared ReLU (max(z,0)^2)
+ * save_pre, when non-NULL, receives BF16 [R_max, 2I] of the pre-activation
+ * (g | u after the bias, before the clamp): the input of the backward.
+ * A NULL moe_epilogue means SwiGLU with beta = 1, no bias, no clamp.
+ */
+#define MOE_ACT_SWIGLU 0
+#define MOE_ACT_GEGLU  1
+#define MOE_ACT_SRELU  2
+typedef struct moe_epilogue {
+    int32_t      act;        /* MOE_ACT_*                                        */
+    float        beta;       /* Swish slope (MOE_ACT_SWIGLU only), e.g. 1.0f     */
+    float        limit;      /* > 0: clamp both chunks to [-limit, limit]; 0: off */
+    int32_t      reserved;
+    const float* bias;       /* NULL, or device f32 [G][2I]: b then c per group  */
+    uint16_t*    save_pre;   /* NULL, or device bf16 [R_max, 2I] (written)       */
+} moe_epilogue;
 
 #define MOE_MAX_EXPERTS 2048
 #define MOE_MAX_SLOTS   32      /* k + s */
@@ -229,9 +258,42 @@ int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_shared,
                        const int32_t* counts, const int32_t* offsets, const int32_t* offsets32,
                        const float* row_w, const uint8_t* xq, const uint8_t* xs,
                        const int32_t* row_src, int32_t x_rows,
-                       int32_t R_max, int32_t H, int32_t I, int32_t G, uint32_t flags,
+                       int32_t R_max, int32_t H, int32_t I, int32_t G,
+                       const moe_epilogue* epi, uint32_t flags,
                        uint8_t* hq, uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws,
                        size_t ws_bytes, hipStream_t stream);
+
+/* ---- backward of the fused W1 epilogue ----------------------------------- */
+/*
+ * The fusion blog's "GroupGemm + dActivation + Quantize/Transpose" kernel
+ * (the backward epilogue reads the GEMM output, forms the activation's
+ * derivative and quantises it). For every group g and row r:
+ *   dh  = dec(dy_r) . dec(W2T_g)^T           (fp32 on MFMA; W2T_g = W2_g^T,
+ *                                              [I, H], MX-quantised along H)
+ *   with (g, u) the saved pre-activation row pre[r] (BF16, see moe_epilogue)
+ *   and w = row_w[r] (1 when row_w is NULL):
+ *   dg  = dh * w * clamp(u) * a'(clamp(g)) * [|g| <= limit]
+ *   du  = dh * w * a(clamp(g)) * [|u| <= limit]          ([...] = 1 without clamp)
+ *   dw[r] = sum_i dh * a(clamp(g)) * clamp(u)    (the routing weight's gradient)
+ *   dq[r], ds[r] = MX-E4M3 quantisation of [dg | du] in blocks of 32 along 2I
+ * and, with MOE_W1_WRITE_TRANSPOSE, the transposed copy dTq [2I, ldT],
+ * dTs [2I, ldT/32] in 32-row blocks per group, laid out as the forward's hT
+ * (ldT = moe_transposed_ld(R_max, G)). dy_r is row row_src[r] of dyq/dys
+ * ([x_rows, H] E4M3 + [x_rows, H/32] E8M0: the layer output's gradient, in
+ * token order). epi: act, beta and limit as in the forward (bias unused: it
+ * is part of pre). flags: MOE_W1_WRITE_TRANSPOSE, MOE_SCALE_RULE_CEIL. dw
+ * may be NULL; it needs row_w. Runs on the LDS-tiled GEMM kernel. Limits as
+ * moe_grouped_w1, and R_max * 2I < 2^31. ws: moe_backward_workspace_size.
+ */
+size_t  moe_backward_workspace_size(int32_t R_max, int32_t G, int32_t H, int32_t I);
+int32_t moe_grouped_w1_backward(const moe_weights* w2t, const moe_weights* w2t_shared,
+                                const int32_t* counts, const int32_t* offsets,
+                                const int32_t* offsets32, const float* row_w,
+                                const uint8_t* dyq, const uint8_t* dys, const int32_t* row_src,
+                                int32_t x_rows, const uint16_t* pre, int32_t R_max, int32_t H,
+                                int32_t I, int32_t G, const moe_epilogue* epi, uint32_t flags,
+                                uint8_t* dq, uint8_t* ds, uint8_t* dTq, uint8_t* dTs, float* dw,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- S6: grouped W2 ----------------------------------------------------- */
 /*
@@ -274,6 +336,7 @@ typedef struct moe_layer_args {
     uint8_t*       hTq;        /* with MOE_W1_WRITE_TRANSPOSE: [I, ldT]        */
     uint8_t*       hTs;        /*                               [I, ldT/32]    */
     uint16_t*      out;        /* [T, H] bf16                                  */
+    const moe_epilogue* epi;   /* NULL: SwiGLU, beta = 1 (see moe_epilogue)    */
 } moe_layer_args;
 
 /* Workspace of moe_layer: every intermediate sized for R_max, plus scratch. */
@@ -282,12 +345,19 @@ size_t  moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_
 
 /*
  * Run route -> permute -> W1 -> W2 -> combine on `stream`. With at most 256
- * experts, k <= 16 and at most 513 groups: 3 launches when T <= 8 and groups
- * average under 16 rows without the transposed copy (every W1 workgroup
- * routes and groups the tokens itself), 4 when T <= 64 (router and grouping
- * share one workgroup), more otherwise. The grouped token rows are not
- * materialised: W1 reads them through row_src.
- * Intermediates live in ws at offsets given by moe_layer_workspace_offsets.
+ * experts, k <= 16, at most 513 groups and T <= 8, without the transposed
+ * copy, MOE_GEMM_TILED or MOE_LAYER_SEPARATE_KERNELS: one persistent launch
+ * (the FlashDMoE page's single-kernel layer) in which every workgroup routes
+ * and groups the tokens, W2 work on a group starts when that group's W1 work
+ * is complete, and the last W2 work item of each 64-column block combines
+ * it. Otherwise 3 launches when T <= 8 and groups average under 16 rows
+ * (every W1 workgroup routes and groups the tokens itself), 4 when T <= 64
+ * (router and grouping share one workgroup), more otherwise. The grouped
+ * token rows are not materialised: W1 reads them through row_src.
+ * Intermediates live in ws at offsets given by moe_layer_workspace_offsets;
+ * the single-launch path keeps its counters in region [12] (a control block
+ * it initialises itself on first use and leaves ready after every call; its
+ * word 2 is nonzero if a wait between workgroups ever timed out).
  */
 int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -311,10 +381,10 @@ int32_t moe_layer_noalloc(const moe_layer_args* a, hipStream_t stream);
 /* Byte offsets of the intermediates inside the moe_layer workspace, for
  * inspection by tests: [0] topk_idx [1] topk_w [2] counts [3] offsets
  * [4] offsets32 [5] row_src [6] row_w [7] slot_row [8] hq [9] hs [10] y
- * [11] scratch. Returns the number written (12). */
+ * [11] scratch [12] control block. Returns the number written (13). */
 int32_t moe_layer_workspace_offsets(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
                                     int32_t H, int32_t I, int32_t s, uint32_t flags,
-                                    size_t* offsets12);
+                                    size_t* offsets13);
 
 #ifdef __cplusplus
 }

@@ -14,9 +14,11 @@ import ctypes as C
 import torch
 
 from . import _lib
-from ._lib import (MOE_FMT_MXFP4, MOE_FMT_MXFP8, MOE_GEMM_STREAMED, MOE_GEMM_TILED,  # noqa: F401
-                   MOE_ROUTE_RENORM, MOE_SCALE_RULE_CEIL, MOE_W1_WRITE_TRANSPOSE,
-                   MOE_WEIGHT_AT_COMBINE, moe_layer_args, moe_weights)
+from ._lib import (MOE_ACT_GEGLU, MOE_ACT_SRELU, MOE_ACT_SWIGLU, MOE_FMT_MXFP4,  # noqa: F401
+                   MOE_FMT_MXFP8, MOE_GEMM_STREAMED, MOE_GEMM_TILED, MOE_LAYER_SEPARATE_KERNELS,
+                   MOE_ROUTE_RENORM,
+                   MOE_SCALE_RULE_CEIL, MOE_W1_WRITE_TRANSPOSE, MOE_WEIGHT_AT_COMBINE,
+                   moe_epilogue, moe_layer_args, moe_weights)
 
 lib = _lib.load()
 
@@ -149,6 +151,29 @@ def _wref(w):
     return None if w is None else w.ref()
 
 
+class Epilogue:
+    """The W1 epilogue variant (moe_epilogue): activation (MOE_ACT_*), Swish
+    slope beta, clamp limit (0: none), optional per-group bias f32 [G, 2I] and
+    optional BF16 pre-activation output [R_max, 2I] (both device tensors,
+    referenced here so they outlive the call)."""
+
+    def __init__(self, act: int = MOE_ACT_SWIGLU, beta: float = 1.0, limit: float = 0.0, bias=None,
+                 save_pre=None):
+        if bias is not None:
+            _dev(bias, torch.float32, "bias")
+        if save_pre is not None:
+            _dev(save_pre, torch.uint16, "save_pre")
+        self.bias, self.save_pre = bias, save_pre
+        self.desc = moe_epilogue(act, beta, limit, 0, _p(bias), _p(save_pre))
+
+    def ref(self):
+        return C.byref(self.desc)
+
+
+def _eref(e):
+    return None if e is None else e.ref()
+
+
 # ------------------------------------------------------------------- route
 def moe_route(logits: torch.Tensor, k: int, flags: int = 0, topk_idx=None, topk_w=None, stream=None):
     _dev(logits, torch.float32, "logits")
@@ -208,7 +233,7 @@ def moe_transposed_ld(R_max: int, G: int) -> int:
 def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq, xs, I: int,
                    flags: int = 0, w1_shared: PackedWeights | None = None, offsets32=None,
                    hq=None, hs=None, hTq=None, hTs=None, row_src=None,
-                   R_max: int | None = None, stream=None):
+                   R_max: int | None = None, epi: Epilogue | None = None, stream=None):
     """xq/xs: the grouped rows [R_max, H] (row_src None) or the token rows
     [T, H] read through row_src (then R_max must be given). The launch
     configuration follows R_max / counts.shape[0] (see include/moe.h)."""
@@ -230,9 +255,42 @@ def moe_grouped_w1(w1: PackedWeights, counts, offsets, row_w, xq, xs, I: int,
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         _check(lib.moe_grouped_w1(w1.ref(), _wref(w1_shared), _p(counts), _p(offsets), _p(offsets32),
                                   _p(row_w), _p(xq), _p(xs), _p(row_src), xq.shape[0], R_max, H, I, G,
-                                  flags, _p(hq), _p(hs), _p(hTq), _p(hTs), _p(ws), nws, _stream()),
+                                  _eref(epi), flags, _p(hq), _p(hs), _p(hTq), _p(hTs), _p(ws), nws,
+                                  _stream()),
                "moe_grouped_w1")
     return hq, hs, hTq, hTs
+
+
+def moe_grouped_w1_backward(w2t: PackedWeights, counts, offsets, row_w, dyq, dys, row_src, pre, I: int,
+                            epi: Epilogue | None = None, flags: int = 0, offsets32=None,
+                            w2t_shared: PackedWeights | None = None, want_dw: bool = True, stream=None):
+    """The backward of the fused W1 epilogue: w2t holds W2^T per group (N = I,
+    K = H), dyq/dys the layer output's gradient in token order [T, H] (E4M3 +
+    E8M0), row_src the grouped rows' tokens, pre the saved BF16 pre-activation
+    [R_max, 2I]. Returns a dict: dq [R_max, 2I], ds [R_max, 2I/32], dTq/dTs
+    (with MOE_W1_WRITE_TRANSPOSE), dw [R_max] (with row_w and want_dw)."""
+    R_max = pre.shape[0]
+    H = dyq.shape[1]
+    G = counts.shape[0]
+    dev = dyq.device
+    with _on(stream):
+        out = dict(dq=torch.empty((R_max, 2 * I), dtype=torch.uint8, device=dev),
+                   ds=torch.empty((R_max, 2 * I // 32), dtype=torch.uint8, device=dev),
+                   dTq=None, dTs=None, dw=None)
+        if flags & MOE_W1_WRITE_TRANSPOSE:
+            ld = moe_transposed_ld(R_max, G)
+            out["dTq"] = torch.zeros((2 * I, ld), dtype=torch.uint8, device=dev)
+            out["dTs"] = torch.zeros((2 * I, ld // 32), dtype=torch.uint8, device=dev)
+        if want_dw and row_w is not None:
+            out["dw"] = torch.empty(R_max, dtype=torch.float32, device=dev)
+        nws = int(lib.moe_backward_workspace_size(R_max, G, H, I))
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        _check(lib.moe_grouped_w1_backward(
+            w2t.ref(), _wref(w2t_shared), _p(counts), _p(offsets), _p(offsets32), _p(row_w), _p(dyq),
+            _p(dys), _p(row_src), dyq.shape[0], _p(pre), R_max, H, I, G, _eref(epi), flags,
+            _p(out["dq"]), _p(out["ds"]), _p(out["dTq"]), _p(out["dTs"]), _p(out["dw"]), _p(ws), nws,
+            _stream()), "moe_grouped_w1_backward")
+    return out
 
 
 def moe_grouped_w2(w2: PackedWeights, counts, offsets, hq, hs, H: int,
@@ -263,7 +321,7 @@ def moe_combine(y, slot_row, H: int, row_w=None, out=None, stream=None):
 
 # ------------------------------------------------------------------- layer
 _NAMES = ["topk_idx", "topk_w", "counts", "offsets", "offsets32", "row_src", "row_w", "slot_row",
-          "hq", "hs", "y", "scratch"]
+          "hq", "hs", "y", "scratch", "ctrl"]
 
 
 class LayerWorkspace:
@@ -290,6 +348,7 @@ class LayerWorkspace:
             "row_w": ((R,), torch.float32), "slot_row": ((T, k + s), torch.int32),
             "hq": ((R, I), torch.uint8), "hs": ((R, I // 32), torch.uint8),
             "y": ((R, H), torch.uint16),
+            "ctrl": ((8 + G + H // 64,), torch.int32),
         }
         shp, dt = shapes[name]
         o = self.offsets[_NAMES.index(name)]
@@ -300,7 +359,7 @@ class LayerWorkspace:
         return self.buf[o:o + nbytes].view(dt).view(shp)
 
 
-def _layer_args(logits, xq, xs, w1, w2, k, e0, n_local, shared, flags, out, hTq, hTs):
+def _layer_args(logits, xq, xs, w1, w2, k, e0, n_local, shared, flags, out, hTq, hTs, epi=None):
     T, E_tot = logits.shape
     H = xq.shape[1]
     args = moe_layer_args()
@@ -313,12 +372,14 @@ def _layer_args(logits, xq, xs, w1, w2, k, e0, n_local, shared, flags, out, hTq,
     args.flags = flags
     args.hTq, args.hTs = _p(hTq), _p(hTs)
     args.out = _p(out)
+    if epi is not None:
+        args.epi = C.pointer(epi.desc)
     return args
 
 
 def moe_layer(logits, xq, xs, w1: PackedWeights, w2: PackedWeights, k: int, e0: int = 0,
               n_local: int | None = None, shared=None, flags: int = 0, out=None, ws=None,
-              hTq=None, hTs=None, stream=None):
+              hTq=None, hTs=None, epi: Epilogue | None = None, stream=None):
     """Whole layer. shared = (PackedWeights W1, PackedWeights W2) or None.
     Returns out (bf16 bits as uint16 [T, H])."""
     _dev(logits, torch.float32, "logits")
@@ -334,7 +395,7 @@ def moe_layer(logits, xq, xs, w1: PackedWeights, w2: PackedWeights, k: int, e0: 
             out = torch.empty((T, H), dtype=torch.uint16, device=xq.device)
         if ws is None:
             ws = LayerWorkspace(T, E_tot, k, n_local, H, I, bool(s), flags, device=xq.device)
-        args = _layer_args(logits, xq, xs, w1, w2, k, e0, n_local, shared, flags, out, hTq, hTs)
+        args = _layer_args(logits, xq, xs, w1, w2, k, e0, n_local, shared, flags, out, hTq, hTs, epi)
         _check(lib.moe_layer(C.byref(args), _p(ws.buf), ws.nbytes, _stream()), "moe_layer")
     return out
 

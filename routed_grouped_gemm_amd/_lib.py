@@ -15,6 +15,7 @@ MOE_W1_WRITE_TRANSPOSE = 1 << 2
 MOE_SCALE_RULE_CEIL = 1 << 3
 MOE_GEMM_STREAMED = 1 << 8
 MOE_GEMM_TILED = 1 << 9
+MOE_LAYER_SEPARATE_KERNELS = 1 << 10
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -24,17 +25,27 @@ class moe_weights(C.Structure):
                 ("bytes", C.c_size_t)]
 
 
+MOE_ACT_SWIGLU, MOE_ACT_GEGLU, MOE_ACT_SRELU = 0, 1, 2
+
+
+class moe_epilogue(C.Structure):
+    _fields_ = [("act", C.c_int32), ("beta", C.c_float), ("limit", C.c_float), ("reserved", C.c_int32),
+                ("bias", C.c_void_p), ("save_pre", C.c_void_p)]
+
+
 class moe_layer_args(C.Structure):
     _fields_ = [("logits", C.c_void_p), ("T", C.c_int32), ("E_tot", C.c_int32), ("k", C.c_int32),
                 ("e0", C.c_int32), ("E_loc", C.c_int32), ("xq", C.c_void_p), ("xs", C.c_void_p),
                 ("H", C.c_int32), ("I", C.c_int32), ("w1", C.POINTER(moe_weights)),
                 ("w2", C.POINTER(moe_weights)), ("shared_w1", C.POINTER(moe_weights)),
                 ("shared_w2", C.POINTER(moe_weights)), ("flags", C.c_uint32),
-                ("hTq", C.c_void_p), ("hTs", C.c_void_p), ("out", C.c_void_p)]
+                ("hTq", C.c_void_p), ("hTs", C.c_void_p), ("out", C.c_void_p),
+                ("epi", C.POINTER(moe_epilogue))]
 
 
 P, I32, U32, SZ = C.c_void_p, C.c_int32, C.c_uint32, C.c_size_t
 WP = C.POINTER(moe_weights)
+EP = C.POINTER(moe_epilogue)
 
 # name -> (restype, argtypes), in the order of include/moe.h
 SIGNATURES = {
@@ -49,8 +60,11 @@ SIGNATURES = {
     "moe_permute": (I32, [P, P, I32, I32, I32, I32, I32, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_transposed_ld": (I32, [I32, I32]),
     "moe_grouped_workspace_size": (SZ, [I32, I32, I32, I32]),
-    "moe_grouped_w1": (I32, [WP, WP, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, U32, P, P, P,
+    "moe_grouped_w1": (I32, [WP, WP, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, EP, U32, P, P, P,
                              P, P, SZ, P]),
+    "moe_backward_workspace_size": (SZ, [I32, I32, I32, I32]),
+    "moe_grouped_w1_backward": (I32, [WP, WP, P, P, P, P, P, P, P, I32, P, I32, I32, I32, I32, EP, U32,
+                                      P, P, P, P, P, P, SZ, P]),
     "moe_grouped_w2": (I32, [WP, WP, P, P, P, P, I32, I32, I32, I32, U32, P, P, SZ, P]),
     "moe_combine": (I32, [P, P, P, I32, I32, I32, P, P]),
     "moe_layer_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, U32]),

@@ -29,6 +29,18 @@ struct KParams {
     const uint32_t* bst;              // tiled kernels: activation scales per K-tile and pass
     uint32_t bst_bytes;
     int npass;                        // passes the scale tiles are laid out for
+    // W1 epilogue variant (act, beta, clamp limit, per-group bias [G][2I],
+    // optional BF16 copy of the pre-activation [R_max, 2I]); generic = 0 is
+    // SwiGLU with beta = 1 and none of the options
+    int generic, act;
+    float beta, limit;
+    const float* bias;
+    uint16_t* save_pre;
+    // backward (dActivation) epilogue: the saved pre-activation [R_max, 2I]
+    // (BF16), and the per-unit partial sums of the routing-weight gradient
+    // [R_max][N / 64]
+    const uint16_t* pre;
+    float* dw_part;
     // decode W1 that routes its own tokens (logits non-null): every workgroup
     // routes and groups the T tokens in LDS, workgroup 0 writes the results
     // to the routing outputs and to counts .. row_w above
@@ -80,6 +92,15 @@ inline KParams make_params(const GemmArgs& a, bool w1) {
     p.use_w = (w1 && a.row_w && !(a.flags & MOE_WEIGHT_AT_COMBINE)) ? 1 : 0;
     p.hq = a.hq; p.hs = a.hs; p.hTq = a.hTq; p.hTs = a.hTs; p.ldT = a.ldT;
     p.y = a.y;
+    if (a.epi && w1) {
+        p.act = a.epi->act; p.beta = a.epi->beta; p.limit = a.epi->limit;
+        p.bias = a.epi->bias; p.save_pre = a.epi->save_pre;
+        p.generic = (p.act != MOE_ACT_SWIGLU || p.beta != 1.0f || p.limit > 0.0f || p.bias ||
+                     p.save_pre) ? 1 : 0;
+    } else {
+        p.act = MOE_ACT_SWIGLU; p.beta = 1.0f;
+    }
+    p.pre = a.pre; p.dw_part = a.dw_part;
     if (a.route) {
         p.logits = a.route->logits;
         p.T = a.route->T; p.E_tot = a.route->E_tot; p.k_top = a.route->k; p.e0 = a.route->e0;

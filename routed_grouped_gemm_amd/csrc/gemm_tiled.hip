@@ -157,8 +157,11 @@ MOE_DEV void stage_all(const KParams& p, rsrc_t rx, rsrc_t rxs, const Ctx& c, in
     for (int i = 0; i < 2; ++i) {
         const int T = 2 * w + i;                // weight tile within the workgroup tile
         const int u = c.wt * kUnits + (T >> 2), t = T & 3;
-        const rsrc_t rw = make_rsrc(c.wgrp + (size_t)u * p.dpu, valid ? (uint32_t)p.dpu : 0u);
-        const rsrc_t rs = make_rsrc(c.wgrp + p.dpg + (size_t)u * p.spu, valid ? (uint32_t)p.spu : 0u);
+        // a partial last workgroup tile (N not a multiple of 256: the
+        // backward's N = I) stages zeros for the units past the last one
+        const bool uok = valid && u < p.N / 64;
+        const rsrc_t rw = make_rsrc(c.wgrp + (size_t)u * p.dpu, uok ? (uint32_t)p.dpu : 0u);
+        const rsrc_t rs = make_rsrc(c.wgrp + p.dpg + (size_t)u * p.spu, uok ? (uint32_t)p.spu : 0u);
         #pragma unroll
         for (int half = 0; half < S::kBPL / 16; ++half)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -187,12 +190,82 @@ MOE_DEV uint32_t quad_byte_transpose(uint32_t x, int lane) {
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                  // lo bytes 0,1 then hi bytes 0,1
 }
 
-template <int WFMT, bool IS_W1>
+// Sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the same lane of each
+// row of the wave), returned to all four, in a fixed order.
+MOE_DEV float rows4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Transposed copy, staging of one 32-token block jp of a wave (tokens
+// tok0 + 32 jp + [0, 32): token tiles 2 jp and 2 jp + 1) for 32 features
+// (two 16-feature tiles a, the lane's 4 features 16 a + 4 q + v): per feature
+// the amax over its 32 tokens (16 lanes x 2 tiles), the E8M0 code, and the
+// E4M3 codes, into the wave's LDS staging as [feature][token] bytes (tw) and
+// [block][feature] scale bytes (tsw, written by the lanes with r = 0).
+MOE_DEV void transpose_stage(const float (&h)[2][2][4], int jp, uint8_t* tw, uint8_t* tsw, int lane,
+                             bool ceil_rule) {
+    const int q = lane >> 4, r = lane & 15;
+    #pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        float sc[2][4];
+        uint32_t cw = 0;
+        #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint32_t am = row16_umax(__float_as_uint(fmaxf(fabsf(h[0][a][v]), fabsf(h[1][a][v]))));
+            const uint32_t code = e4m3_scale_code(__uint_as_float(am), ceil_rule);
+            const float inv = inv_scale(code);
+            sc[0][v] = h[0][a][v] * inv;
+            sc[1][v] = h[1][a][v] * inv;
+            cw |= code << (8 * v);
+        }
+        if (r == 0) *(uint32_t*)(tsw + jp * 32 + 16 * a + 4 * q) = cw;
+        // lane 4m + k: feature 16a + 4q + k, tokens 16 j + 4m .. +3
+        #pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const uint32_t pk = e4m3x4(sc[jj][0], sc[jj][1], sc[jj][2], sc[jj][3]);
+            const uint32_t tr = quad_byte_transpose(pk, lane);
+            const int fl = 16 * a + 4 * q + (lane & 3);
+            *(uint32_t*)(tw + fl * kTStride + 16 * (2 * jp + jj) + 4 * ((lane >> 2) & 3)) = tr;
+        }
+    }
+}
+
+// The staged 32 features x 128 tokens of a wave -> transposed rows
+// [fbase, fbase + 32) of a [rows, ldT] copy at columns col0 + [0, 128), as
+// 16-byte row stores, and their scales; only 32-token blocks that start
+// inside the item's rows (nrows counted from the wave's first token tok0).
+MOE_DEV void transpose_flush(const uint8_t* tw, const uint8_t* tsw, uint8_t* dq, uint8_t* ds, int rows,
+                             int ldT, int fbase, int col0, int tok0, int nrows, int lane) {
+    const rsrc_t rhT = make_rsrc(dq, (uint32_t)((size_t)rows * ldT));
+    const rsrc_t rhTs = make_rsrc(ds, (uint32_t)((size_t)rows * (ldT / 32)));
+    #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int fl = 8 * i + (lane >> 3), c = lane & 7;
+        const i32x4 d = *(const i32x4*)(tw + fl * kTStride + 16 * c);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            d, rhT, tok0 + 32 * (c >> 1) < nrows ? (uint32_t)((fbase + fl) * ldT + col0 + 16 * c) : kInvalid, 0, 0);
+    }
+    // scales: feature lane (< 32), 4 blocks -> bytes [col0/32, +4) of its scale row
+    const uint32_t so = (uint32_t)((fbase + (lane & 31)) * (ldT / 32) + (col0 >> 5));
+    #pragma unroll
+    for (int b = 0; b < 4; ++b)
+        __builtin_amdgcn_raw_buffer_store_b8(tsw[b * 32 + (lane & 31)], rhTs,
+                                             (lane < 32 && tok0 + 32 * b < nrows) ? so + b : kInvalid, 0, 0);
+}
+
+// Kernel modes: the epilogue that follows the shared K-loop.
+enum { kModeW2 = 0, kModeW1 = 1, kModeW1Gen = 2, kModeBwd = 3 };
+
+template <int WFMT, int MODE>
 __global__ __launch_bounds__(kThreads, 1)
 void tiled_gemm_kernel(KParams p) {
+    constexpr bool IS_W1 = MODE == kModeW1 || MODE == kModeW1Gen;
     using S = Stage<WFMT>;
     const int G = p.G, units = p.N / 64;
-    const int wtiles = units / kUnits;       // units is a multiple of 4 (N % 256 == 0)
+    const int wtiles = (units + kUnits - 1) / kUnits;   // a multiple of 4 units but for the backward
 
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* ring = smem;                                               // [2][S::Bytes]
@@ -301,7 +374,7 @@ void tiled_gemm_kernel(KParams p) {
         // ---------------------------------------------------- epilogue
         const int tok0 = ti * (kBT * 16);
         const int uu = cur.wt * kUnits + wi;                    // this wave's unit
-        if (IS_W1) {
+        if constexpr (IS_W1) {
             // the stage just consumed serves as scratch; the next step's
             // prefetch lands in it only after the barrier below
             uint8_t* scratch = ring + ((s - 1) & 1) * S::Bytes;
@@ -324,6 +397,24 @@ void tiled_gemm_kernel(KParams p) {
                     rw_w, (uint32_t)((tok0 + 16 * j + r) * 4), 0, 0));
             #pragma unroll
             for (int j = 0; j < kBT; ++j) wrow[j] = p.use_w ? wrow[j] : 1.0f;
+            // generic variant: this lane's 8 gate and 8 up biases (features
+            // 32 uu + 16 a + 4 q + v), zero without a bias; the BF16
+            // pre-activation copy goes to rows of 2I
+            float bg[2][4] = {}, bu[2][4] = {};
+            const bool spre = MODE == kModeW1Gen && p.save_pre;
+            const rsrc_t rpre = make_rsrc(spre ? p.save_pre + (size_t)cur.rbase * 2 * I : (uint16_t*)p.hq,
+                                          spre ? (uint32_t)(cur.nrows * 2 * I * 2) : 0u);
+            if constexpr (MODE == kModeW1Gen) {
+                const rsrc_t rb = make_rsrc(p.bias + (size_t)cur.g * 2 * I, p.bias ? (uint32_t)(2 * I * 4) : 0u);
+                #pragma unroll
+                for (int a = 0; a < 2; ++a)
+                    #pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const uint32_t f = (uint32_t)(32 * uu + 16 * a + 4 * q + v);
+                        bg[a][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * f, 0, 0));
+                        bu[a][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (f + I), 0, 0));
+                    }
+            }
             #pragma unroll
             for (int jp = 0; jp < kBT / 2; ++jp) {
                 float h[2][2][4];                               // [j in pair][gate tile][v]
@@ -335,13 +426,41 @@ void tiled_gemm_kernel(KParams p) {
                     const float wgt = wrow[j];
                     float amf = 0.f;
                     #pragma unroll
-                    for (int a = 0; a < 2; ++a)
-                        #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const float hv = silu_fast(acc[j][a][v]) * acc[j][a + 2][v] * wgt;
-                            h[jj][a][v] = hv;
-                            amf = fmaxf(amf, fabsf(hv));
+                    for (int a = 0; a < 2; ++a) {
+                        if constexpr (MODE == kModeW1Gen) {
+                            float gz[4], uz[4];
+                            #pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                gz[v] = acc[j][a][v] + bg[a][v];
+                                uz[v] = acc[j][a + 2][v] + bu[a][v];
+                            }
+                            // pre-activation rows (dropped past the item's rows)
+                            u32x2 pg, pu;
+                            pg.x = bf16x2(gz[0], gz[1]); pg.y = bf16x2(gz[2], gz[3]);
+                            pu.x = bf16x2(uz[0], uz[1]); pu.y = bf16x2(uz[2], uz[3]);
+                            const uint32_t po = (uint32_t)((tok * 2 * I + 32 * uu + 16 * a + 4 * q) * 2);
+                            __builtin_amdgcn_raw_buffer_store_b64(pg, rpre, po, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b64(pu, rpre, po + (uint32_t)(2 * I), 0, 0);
+                            #pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                float g = gz[v], u = uz[v];
+                                if (p.limit > 0.f) {
+                                    g = fminf(fmaxf(g, -p.limit), p.limit);
+                                    u = fminf(fmaxf(u, -p.limit), p.limit);
+                                }
+                                const float hv = act_value(g, p.act, p.beta) * u * wgt;
+                                h[jj][a][v] = hv;
+                                amf = fmaxf(amf, fabsf(hv));
+                            }
+                        } else {
+                            #pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const float hv = silu_fast(acc[j][a][v]) * acc[j][a + 2][v] * wgt;
+                                h[jj][a][v] = hv;
+                                amf = fmaxf(amf, fabsf(hv));
+                            }
                         }
+                    }
                     // the unit's 32 features of this token: 4 lanes (q) x 8 values
                     const uint32_t am = rows4_umax(__float_as_uint(amf));
                     const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
@@ -355,57 +474,121 @@ void tiled_gemm_kernel(KParams p) {
                     __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, rhs,
                                                          q == 0 ? (uint32_t)(tok * (I / 32) + uu) : kInvalid, 0, 0);
                 }
-                if (p.transpose) {
-                    // 32-token block jp of this wave (tokens tok0 + 32 jp + [0, 32)):
-                    // per feature, amax over its 16 lanes x 2 tiles; the codes go
-                    // to the wave's LDS staging as [block][feature] bytes, the 4
-                    // features of a lane in one dword (written by lane r = 0)
+                // 32-token block jp of this wave, staged in LDS for the transposed copy
+                if (p.transpose) transpose_stage(h, jp, tw, tsw, lane, p.ceil_rule);
+            }
+            if (p.transpose)
+                transpose_flush(tw, tsw, p.hTq, p.hTs, I, p.ldT, 32 * uu,
+                                p.offsets32[cur.g] + cur.pass * kRows + tok0, tok0, cur.nrows, lane);
+            __syncthreads();                 // scratch free before the next prefetch lands in it
+        } else if constexpr (MODE == kModeBwd) {
+            // dActivation epilogue. acc holds dh for this wave's 64 features
+            // (weight tile t: features 64 uu + 16 t + 4 q + v) of 128 token
+            // rows. Output rows are [dg | du], L = 2I bytes of E4M3 codes.
+            uint8_t* scratch = ring + ((s - 1) & 1) * S::Bytes;
+            uint8_t* tw = scratch + w * kTWave;
+            uint8_t* tsw = scratch + kWaves * kTWave + w * 128;
+            const int I = p.N, L = 2 * I;
+            if (uu < units) {                // a partial last tile: waves past the last unit idle
+                const rsrc_t rpre = make_rsrc(p.pre + (size_t)cur.rbase * L, (uint32_t)(cur.nrows * L * 2));
+                const rsrc_t rdq = make_rsrc(p.hq + (size_t)cur.rbase * L, (uint32_t)(cur.nrows * L));
+                const rsrc_t rds = make_rsrc(p.hs + (size_t)cur.rbase * (L / 32), (uint32_t)(cur.nrows * (L / 32)));
+                const rsrc_t rw_w = make_rsrc(p.row_w + cur.rbase, p.use_w ? (uint32_t)(cur.nrows * 4) : 0u);
+                const rsrc_t rdw = make_rsrc(p.dw_part + (size_t)cur.rbase * units,
+                                             p.dw_part ? (uint32_t)(cur.nrows * units * 4) : 0u);
+                float wrow[kBT];
+                #pragma unroll
+                for (int j = 0; j < kBT; ++j)
+                    wrow[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rw_w, (uint32_t)((tok0 + 16 * j + r) * 4), 0, 0));
+                #pragma unroll
+                for (int j = 0; j < kBT; ++j) wrow[j] = p.use_w ? wrow[j] : 1.0f;
+                const float lim = p.limit;
+                // dg (half 0) or du (half 1) of weight tiles t0, t0 + 1 for token
+                // tile j: x[tt][v]; returns those 8 features' part of dw
+                auto dact = [&](int j, int t0, int half, float (&x)[2][4]) __attribute__((always_inline)) -> float {
+                    const int tok = tok0 + 16 * j + r;
+                    float dwp = 0.f;
                     #pragma unroll
-                    for (int a = 0; a < 2; ++a) {
-                        float sc[2][4];
-                        uint32_t cw = 0;
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const uint32_t po = (uint32_t)((tok * L + 64 * uu + 16 * (t0 + tt) + 4 * q) * 2);
+                        const u32x2 pg = __builtin_amdgcn_raw_buffer_load_b64(rpre, po, 0, 0);
+                        const u32x2 pu = __builtin_amdgcn_raw_buffer_load_b64(rpre, po + (uint32_t)(2 * I), 0, 0);
+                        const float gv[4] = {bf16_to_f32(pg.x & 0xFFFFu), bf16_to_f32(pg.x >> 16),
+                                             bf16_to_f32(pg.y & 0xFFFFu), bf16_to_f32(pg.y >> 16)};
+                        const float uv[4] = {bf16_to_f32(pu.x & 0xFFFFu), bf16_to_f32(pu.x >> 16),
+                                             bf16_to_f32(pu.y & 0xFFFFu), bf16_to_f32(pu.y >> 16)};
                         #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            const uint32_t am = row16_umax(__float_as_uint(fmaxf(fabsf(h[0][a][v]), fabsf(h[1][a][v]))));
-                            const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
-                            const float inv = inv_scale(code);
-                            sc[0][v] = h[0][a][v] * inv;
-                            sc[1][v] = h[1][a][v] * inv;
-                            cw |= code << (8 * v);
-                        }
-                        if (r == 0) *(uint32_t*)(tsw + jp * 32 + 16 * a + 4 * q) = cw;
-                        // lane 4m + k: feature 16a + 4q + k, tokens 16 j + 4m .. +3
-                        #pragma unroll
-                        for (int jj = 0; jj < 2; ++jj) {
-                            const uint32_t pk = e4m3x4(sc[jj][0], sc[jj][1], sc[jj][2], sc[jj][3]);
-                            const uint32_t tr = quad_byte_transpose(pk, lane);
-                            const int fl = 16 * a + 4 * q + (lane & 3);
-                            *(uint32_t*)(tw + fl * kTStride + 16 * (2 * jp + jj) + 4 * ((lane >> 2) & 3)) = tr;
+                            float g = gv[v], u = uv[v], mg = 1.f, mu = 1.f;
+                            if (lim > 0.f) {
+                                mg = fabsf(g) <= lim ? 1.f : 0.f;
+                                mu = fabsf(u) <= lim ? 1.f : 0.f;
+                                g = fminf(fmaxf(g, -lim), lim);
+                                u = fminf(fmaxf(u, -lim), lim);
+                            }
+                            float a, da;
+                            act_and_grad(g, p.act, p.beta, a, da);
+                            const float dh = acc[j][t0 + tt][v];
+                            x[tt][v] = half == 0 ? dh * wrow[j] * u * da * mg : dh * wrow[j] * a * mu;
+                            dwp += dh * a * u;
                         }
                     }
-                }
-            }
-            if (p.transpose) {
-                // LDS -> hT rows: feature rows of 128 token bytes, 16 bytes per lane;
-                // only 32-token blocks that start inside the group's rows
-                const int col0 = p.offsets32[cur.g] + cur.pass * kRows + tok0;
-                const int fbase = 32 * uu;
-                const rsrc_t rhT = make_rsrc(p.hTq, (uint32_t)((size_t)I * p.ldT));
-                const rsrc_t rhTs = make_rsrc(p.hTs, (uint32_t)((size_t)I * (p.ldT / 32)));
-                #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int fl = 8 * i + (lane >> 3), c = lane & 7;
-                    const i32x4 d = *(const i32x4*)(tw + fl * kTStride + 16 * c);
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        d, rhT, tok0 + 32 * (c >> 1) < cur.nrows ? (uint32_t)((fbase + fl) * p.ldT + col0 + 16 * c) : kInvalid, 0, 0);
-                }
-                // scales: feature lane (< 32), 4 blocks -> bytes [col0/32, +4) of its hT scale row
-                {
-                    const uint32_t so = (uint32_t)((fbase + (lane & 31)) * (p.ldT / 32) + (col0 >> 5));
+                    return dwp;
+                };
+                static_for<kBT>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const int tok = tok0 + 16 * j + r;
+                    float dwp = 0.f;
                     #pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        __builtin_amdgcn_raw_buffer_store_b8(tsw[b * 32 + (lane & 31)], rhTs,
-                                                             (lane < 32 && tok0 + 32 * b < cur.nrows) ? so + b : kInvalid, 0, 0);
+                    for (int half = 0; half < 2; ++half)
+                        #pragma unroll
+                        for (int b = 0; b < 2; ++b) {
+                            float x[2][4];
+                            const float part = dact(j, 2 * b, half, x);
+                            if (half == 0) dwp += part;
+                            float amf = 0.f;
+                            #pragma unroll
+                            for (int tt = 0; tt < 2; ++tt)
+                                #pragma unroll
+                                for (int v = 0; v < 4; ++v) amf = fmaxf(amf, fabsf(x[tt][v]));
+                            const uint32_t am = rows4_umax(__float_as_uint(amf));
+                            const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
+                            const float inv = inv_scale(code);
+                            #pragma unroll
+                            for (int tt = 0; tt < 2; ++tt)
+                                __builtin_amdgcn_raw_buffer_store_b32(
+                                    e4m3x4(x[tt][0] * inv, x[tt][1] * inv, x[tt][2] * inv, x[tt][3] * inv), rdq,
+                                    (uint32_t)(tok * L + half * I + 64 * uu + 16 * (2 * b + tt) + 4 * q), 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b8(
+                                (unsigned char)code, rds,
+                                q == 0 ? (uint32_t)(tok * (L / 32) + half * (I / 32) + 2 * uu + b) : kInvalid, 0, 0);
+                        }
+                    // the routing weight's gradient: this unit's 64 features of the token
+                    const float dws = rows4_sum(dwp);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dws), rdw,
+                                                          q == 0 ? (uint32_t)((tok * units + uu) * 4) : kInvalid, 0, 0);
+                    // one token tile at a time: its loads are not hoisted above the
+                    // previous tile's work (that would hold all 8 tiles' inputs at once)
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                if (p.transpose) {
+                    // four 32-feature chunks (dg or du, tiles 2b and 2b + 1),
+                    // each staged and flushed like the forward's transposed copy
+                    const int col0 = p.offsets32[cur.g] + cur.pass * kRows + tok0;
+                    static_for<4>([&](auto cc) {
+                        constexpr int c = decltype(cc)::value, half = c >> 1, b = c & 1;
+                        static_for<kBT / 2>([&](auto jpc) {
+                            constexpr int jp = decltype(jpc)::value;
+                            float x2[2][2][4];
+                            (void)dact(2 * jp, 2 * b, half, x2[0]);
+                            (void)dact(2 * jp + 1, 2 * b, half, x2[1]);
+                            transpose_stage(x2, jp, tw, tsw, lane, p.ceil_rule);
+                            __builtin_amdgcn_sched_barrier(0);
+                        });
+                        transpose_flush(tw, tsw, p.hTq, p.hTs, L, p.ldT, half * I + 64 * uu + 32 * b, col0, tok0,
+                                        cur.nrows, lane);
+                    });
                 }
             }
             __syncthreads();                 // scratch free before the next prefetch lands in it
@@ -481,19 +664,31 @@ void scale_tiles_kernel(const int32_t* __restrict__ counts, const int32_t* __res
         if (kt0 + i < nkt) out[((size_t)(kt0 + i) * npass + b) * kRows + tid] = v[i];
 }
 
-template <int WFMT, bool IS_W1>
+template <int WFMT, int MODE>
 int launch_tiled(const KParams& p, int R_max, hipStream_t stream) {
-    auto kern = tiled_gemm_kernel<WFMT, IS_W1>;
+    auto kern = tiled_gemm_kernel<WFMT, MODE>;
     const size_t lds = 2 * (size_t)Stage<WFMT>::Bytes + (size_t)(p.G + 1) * 4;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
-    const long wtiles = p.N / 64 / kUnits;
+    const long wtiles = (p.N / 64 + kUnits - 1) / kUnits;
     // passes never exceed R_max / 256 + G: each group adds at most one partial pass
     const long max_items = wtiles * ((long)R_max / kRows + p.G);
     const long grid = std::max<long>(1, std::min<long>(max_items, (long)per_cu * device_cu_count()));
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
     return (int)hipGetLastError();
+}
+
+// dw[r] = sum over the units u of part[r][u], in unit order, for the rows of
+// the groups (r < offsets[G]); one thread per row.
+__global__ __launch_bounds__(256)
+void dw_reduce_kernel(const float* __restrict__ part, int units, const int32_t* __restrict__ offsets,
+                      int G, int R_max, float* __restrict__ dw) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= R_max || r >= offsets[G]) return;
+    float s = 0.f;
+    for (int u = 0; u < units; ++u) s += part[(size_t)r * units + u];
+    dw[r] = s;
 }
 
 // The activation scales as scale tiles in the workspace; fills p.bst.
@@ -522,14 +717,35 @@ int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream) {
     if (a.G == 0 || a.R_max == 0) return 0;
     KParams p = make_params(a, true);
     if (int e = launch_scale_tiles(a, p, stream)) return e;
-    return a.fmt == MOE_FMT_MXFP4 ? launch_tiled<MFMA_FMT_FP4, true>(p, a.R_max, stream)
-                                  : launch_tiled<MFMA_FMT_FP8, true>(p, a.R_max, stream);
+    const bool fp4 = a.fmt == MOE_FMT_MXFP4;
+    if (p.generic)
+        return fp4 ? launch_tiled<MFMA_FMT_FP4, kModeW1Gen>(p, a.R_max, stream)
+                   : launch_tiled<MFMA_FMT_FP8, kModeW1Gen>(p, a.R_max, stream);
+    return fp4 ? launch_tiled<MFMA_FMT_FP4, kModeW1>(p, a.R_max, stream)
+               : launch_tiled<MFMA_FMT_FP8, kModeW1>(p, a.R_max, stream);
 }
 
 int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream) {
     if (a.G == 0 || a.R_max == 0) return 0;
     KParams p = make_params(a, false);
     if (int e = launch_scale_tiles(a, p, stream)) return e;
-    return a.fmt == MOE_FMT_MXFP4 ? launch_tiled<MFMA_FMT_FP4, false>(p, a.R_max, stream)
-                                  : launch_tiled<MFMA_FMT_FP8, false>(p, a.R_max, stream);
+    return a.fmt == MOE_FMT_MXFP4 ? launch_tiled<MFMA_FMT_FP4, kModeW2>(p, a.R_max, stream)
+                                  : launch_tiled<MFMA_FMT_FP8, kModeW2>(p, a.R_max, stream);
+}
+
+int moe_launch_tiled_backward(const GemmArgs& a, float* dw, hipStream_t stream) {
+    if (a.G == 0 || a.R_max == 0) return 0;
+    KParams p = make_params(a, false);
+    // the backward's own parameters: the forward epilogue variant (act, beta,
+    // limit), the transposed copy, the routing weights whenever given
+    p.transpose = (a.flags & MOE_W1_WRITE_TRANSPOSE) ? 1 : 0;
+    p.use_w = a.row_w ? 1 : 0;
+    if (a.epi) { p.act = a.epi->act; p.beta = a.epi->beta; p.limit = a.epi->limit; }
+    if (int e = launch_scale_tiles(a, p, stream)) return e;
+    const int e = a.fmt == MOE_FMT_MXFP4 ? launch_tiled<MFMA_FMT_FP4, kModeBwd>(p, a.R_max, stream)
+                                         : launch_tiled<MFMA_FMT_FP8, kModeBwd>(p, a.R_max, stream);
+    if (e || !dw) return e;
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((a.R_max + 255) / 256)), dim3(256), 0, stream,
+                       a.dw_part, a.N / 64, a.offsets, a.G, a.R_max, dw);
+    return (int)hipGetLastError();
 }

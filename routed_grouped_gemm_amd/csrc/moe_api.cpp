@@ -28,7 +28,7 @@ int32_t check_weights(const moe_weights* w, int G, int N, int K, int is_w1) {
 }
 
 // Workspace layout of moe_layer (all regions 256-byte aligned).
-constexpr int kRegions = 12;
+constexpr int kRegions = 13;
 struct LayerLayout {
     size_t off[kRegions];
     size_t total;
@@ -51,12 +51,13 @@ LayerLayout layer_layout(int T, int E_tot, int k, int E_loc, int H, int I, int s
         R * (I / 32),                 // hs
         R * H * 2,                    // y
         0,                            // scratch
+        moe_fused_ctrl_words(G, H) * 4,   // control block of the single-launch path
     };
     size_t gws1 = moe_grouped_workspace_size((int)R, G, 2 * I, H);
     size_t gws2 = moe_grouped_workspace_size((int)R, G, H, I);
     size_t pws = moe_permute_workspace_size(T, k, G);
     size_t scr = pws > gws1 ? pws : gws1;
-    sz[kRegions - 1] = scr > gws2 ? scr : gws2;
+    sz[11] = scr > gws2 ? scr : gws2;
     LayerLayout L;
     size_t o = 0;
     for (int i = 0; i < kRegions; ++i) {
@@ -216,16 +217,30 @@ static int32_t check_gemm_flags(uint32_t flags) {
     return MOE_OK;
 }
 
+// The epilogue variant: a known activation, a finite positive Swish slope, a
+// finite non-negative clamp limit (NULL: SwiGLU with beta = 1).
+static int32_t check_epilogue(const moe_epilogue* e) {
+    if (!e) return MOE_OK;
+    if (e->act != MOE_ACT_SWIGLU && e->act != MOE_ACT_GEGLU && e->act != MOE_ACT_SRELU)
+        return MOE_ERR_UNSUPPORTED;
+    if (!(e->beta > 0.0f) || !isfinite(e->beta) || !(e->limit >= 0.0f) || !isfinite(e->limit))
+        return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
 // Everything moe_grouped_w1 checks before it enqueues; a.* filled on success.
 static int32_t prepare_w1(GemmArgs& a, const moe_weights* w1, const moe_weights* w1_shared,
                           const int32_t* counts, const int32_t* offsets, const int32_t* offsets32,
                           const float* row_w, const uint8_t* xq_perm, const uint8_t* xs_perm,
                           const int32_t* row_src, int32_t x_rows, int32_t R_max, int32_t H,
-                          int32_t I, int32_t G, uint32_t flags, uint8_t* hq, uint8_t* hs,
-                          uint8_t* hTq, uint8_t* hTs, void* ws, size_t ws_bytes) {
+                          int32_t I, int32_t G, const moe_epilogue* epi, uint32_t flags,
+                          uint8_t* hq, uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws,
+                          size_t ws_bytes) {
     int32_t st = check_hi(H, I);
     if (st) return st;
     if ((st = check_gemm_flags(flags))) return st;
+    if ((st = check_epilogue(epi))) return st;
+    if (epi && epi->save_pre && (int64_t)R_max * 4 * I >= kI32Lim) return MOE_ERR_SHAPE;
     const bool transpose = (flags & MOE_W1_WRITE_TRANSPOSE) != 0;
     if (x_rows < 1) return MOE_ERR_SHAPE;
     if ((st = check_grouped_sizes(R_max, G, x_rows, H, I, transpose))) return st;
@@ -242,6 +257,7 @@ static int32_t prepare_w1(GemmArgs& a, const moe_weights* w1, const moe_weights*
     a.R_max = R_max; a.flags = flags;
     a.hq = hq; a.hs = hs; a.hTq = hTq; a.hTs = hTs; a.ldT = moe_transposed_ld(R_max, G);
     a.ws = ws; a.ws_bytes = ws_bytes;
+    a.epi = epi;
     return MOE_OK;
 }
 
@@ -250,11 +266,12 @@ MOE_EXPORT int32_t moe_grouped_w1(const moe_weights* w1, const moe_weights* w1_s
                                   const int32_t* offsets32, const float* row_w,
                                   const uint8_t* xq, const uint8_t* xs, const int32_t* row_src,
                                   int32_t x_rows, int32_t R_max, int32_t H, int32_t I, int32_t G,
-                                  uint32_t flags, uint8_t* hq, uint8_t* hs, uint8_t* hTq,
-                                  uint8_t* hTs, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                  const moe_epilogue* epi, uint32_t flags, uint8_t* hq,
+                                  uint8_t* hs, uint8_t* hTq, uint8_t* hTs, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
     GemmArgs a{};
     const int32_t st = prepare_w1(a, w1, w1_shared, counts, offsets, offsets32, row_w, xq, xs,
-                                  row_src, x_rows, R_max, H, I, G, flags, hq, hs, hTq, hTs, ws,
+                                  row_src, x_rows, R_max, H, I, G, epi, flags, hq, hs, hTq, hTs, ws,
                                   ws_bytes);
     if (st) return st;
     return hip_status(moe_launch_grouped_w1(a, stream));
@@ -293,6 +310,53 @@ MOE_EXPORT int32_t moe_grouped_w2(const moe_weights* w2, const moe_weights* w2_s
     return hip_status(moe_launch_grouped_w2(a, stream));
 }
 
+// -------------------------------------------------------------- backward
+// Workspace of moe_grouped_w1_backward: the scale tiles of the dy rows (K = H),
+// then the routing-weight gradient's partials, one per row and 64-feature unit.
+static size_t backward_scale_bytes(int32_t R_max, int32_t G, int32_t H) {
+    return align_up(moe_tiled_scale_bytes(R_max, G, H));
+}
+
+MOE_EXPORT size_t moe_backward_workspace_size(int32_t R_max, int32_t G, int32_t H, int32_t I) {
+    if (R_max < 0 || G < 1 || H <= 0 || H % 128 || I <= 0 || I % 64) return 0;
+    return backward_scale_bytes(R_max, G, H) + (size_t)R_max * (I / 64) * 4;
+}
+
+MOE_EXPORT int32_t moe_grouped_w1_backward(
+        const moe_weights* w2t, const moe_weights* w2t_shared, const int32_t* counts,
+        const int32_t* offsets, const int32_t* offsets32, const float* row_w, const uint8_t* dyq,
+        const uint8_t* dys, const int32_t* row_src, int32_t x_rows, const uint16_t* pre,
+        int32_t R_max, int32_t H, int32_t I, int32_t G, const moe_epilogue* epi, uint32_t flags,
+        uint8_t* dq, uint8_t* ds, uint8_t* dTq, uint8_t* dTs, float* dw, void* ws,
+        size_t ws_bytes, hipStream_t stream) {
+    int32_t st = check_hi(H, I);
+    if (st) return st;
+    if (flags & ~(MOE_W1_WRITE_TRANSPOSE | MOE_SCALE_RULE_CEIL)) return MOE_ERR_UNSUPPORTED;
+    if ((st = check_epilogue(epi))) return st;
+    const bool transpose = (flags & MOE_W1_WRITE_TRANSPOSE) != 0;
+    if (x_rows < 1) return MOE_ERR_SHAPE;
+    if ((st = check_grouped_sizes(R_max, G, x_rows, H, I, false))) return st;
+    // outputs of 2I per row: the row copy and, with the transposed copy, 2I rows of ldT
+    if ((int64_t)R_max * 4 * I >= kI32Lim) return MOE_ERR_SHAPE;
+    if (transpose && (int64_t)2 * I * moe_transposed_ld(R_max, G) >= kI32Lim) return MOE_ERR_SHAPE;
+    GemmArgs a{};
+    if ((st = fill_gemm_args(a, w2t, w2t_shared, G, I, H, 0))) return st;
+    if (!row_src && x_rows < R_max) return MOE_ERR_SHAPE;
+    if (!counts || !offsets || !dyq || !dys || !pre || !dq || !ds) return MOE_ERR_NULL;
+    if (transpose && (!dTq || !dTs || !offsets32)) return MOE_ERR_NULL;
+    if (dw && !row_w) return MOE_ERR_NULL;
+    const size_t need = moe_backward_workspace_size(R_max, G, H, I);
+    if (ws_bytes < need || (need && !ws)) return MOE_ERR_WORKSPACE;
+    a.counts = counts; a.offsets = offsets; a.offsets32 = offsets32; a.row_w = row_w;
+    a.aq = dyq; a.as = dys; a.row_src = row_src; a.x_rows = x_rows;
+    a.R_max = R_max; a.flags = flags;
+    a.hq = dq; a.hs = ds; a.hTq = dTq; a.hTs = dTs; a.ldT = moe_transposed_ld(R_max, G);
+    a.ws = ws; a.ws_bytes = ws_bytes;
+    a.epi = epi; a.pre = pre;
+    a.dw_part = (float*)((char*)ws + backward_scale_bytes(R_max, G, H));
+    return hip_status(moe_launch_tiled_backward(a, dw, stream));
+}
+
 // The tiling hints moe_layer gives the grouped GEMMs, from uniform routing:
 // the expected rows of a routed group, ceil(T * k / E_tot), and the expected
 // groups with rows, ceil(E_loc * (1 - (1 - k/E_tot)^T)) + s.
@@ -326,11 +390,11 @@ MOE_EXPORT size_t moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, 
 
 MOE_EXPORT int32_t moe_layer_workspace_offsets(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
                                                int32_t H, int32_t I, int32_t s, uint32_t flags,
-                                               size_t* offsets12) {
+                                               size_t* offsets13) {
     (void)flags;
-    if (!offsets12) return 0;
+    if (!offsets13) return 0;
     LayerLayout L = layer_layout(T, E_tot, k, E_loc, H, I, s);
-    memcpy(offsets12, L.off, sizeof(L.off));
+    memcpy(offsets13, L.off, sizeof(L.off));
     return kRegions;
 }
 
@@ -380,13 +444,14 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     uint8_t* hs = (uint8_t*)(base + L.off[9]);
     uint16_t* y = (uint16_t*)(base + L.off[10]);
     void* scratch = base + L.off[11];
-    const size_t scratch_bytes = L.total - L.off[11];
+    const size_t scratch_bytes = L.off[12] - L.off[11];
+    uint32_t* ctrl = (uint32_t*)(base + L.off[12]);
 
     // Both GEMMs are validated before anything is enqueued, so a failing call
     // leaves the stream untouched.
     GemmArgs a1{}, a2{};
     st = prepare_w1(a1, a->w1, a->shared_w1, counts, offsets, offsets32, row_w, a->xq, a->xs,
-                    row_src, T, R_max, H, I, G, a->flags, hq, hs, a->hTq, a->hTs, scratch,
+                    row_src, T, R_max, H, I, G, a->epi, a->flags, hq, hs, a->hTq, a->hTs, scratch,
                     scratch_bytes);
     if (st) return st;
     st = prepare_w2(a2, a->w2, a->shared_w2, counts, offsets, hq, hs, R_max, H, I, G,
@@ -400,9 +465,15 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     const int active = layer_active_hint(T, E_tot, k, E_loc, s);
     a1.rows_hint = a2.rows_hint = hint;
     a1.active_hint = a2.active_hint = active;
+    const RouteArgs ra{a->logits, T, E_tot, k, e0, a->flags, topk_idx, topk_w, slot_row};
+    // a decode batch: the whole layer in one persistent launch
+    if (moe_fused_decode_ok(T, E_tot, k, E_loc, s, a->flags)) {
+        a1.route = &ra;
+        a2.y = y;
+        return hip_status(moe_launch_fused_decode(a1, a2, ctrl, a->out, stream));
+    }
     // few tokens: the W1 launch routes and groups them itself
     const bool self_route = moe_w1_can_route(T, E_tot, k, E_loc, s, R_max, H, I, hint, a->flags);
-    const RouteArgs ra{a->logits, T, E_tot, k, e0, a->flags, topk_idx, topk_w, slot_row};
     if (self_route) a1.route = &ra;
 
     int e;

@@ -3,6 +3,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
+#include "../../include/moe.h"
+
 typedef int   i32x4  __attribute__((ext_vector_type(4)));
 typedef int   i32x8  __attribute__((ext_vector_type(8)));
 typedef float f32x4  __attribute__((ext_vector_type(4)));
@@ -144,6 +148,43 @@ MOE_DEV uint32_t bf16x2(float a, float b) {
 }
 // SiLU with the hardware reciprocal (1 ulp) instead of a full division
 MOE_DEV float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+// Gate activations of the W1 epilogue variants (MOE_ACT_*): Swish with slope
+// beta, the exact GELU z * Phi(z), and the squared ReLU. act_and_grad also
+// gives da/dz for the backward.
+MOE_DEV float gelu_cdf(float z) { return 0.5f * (1.0f + erff(z * 0.70710678118654752f)); }
+MOE_DEV float act_value(float z, int act, float beta) {
+    if (act == MOE_ACT_GEGLU) return z * gelu_cdf(z);
+    if (act == MOE_ACT_SRELU) { const float r = fmaxf(z, 0.0f); return r * r; }
+    return z / (1.0f + __expf(-beta * z));
+}
+MOE_DEV void act_and_grad(float z, int act, float beta, float& a, float& da) {
+    if (act == MOE_ACT_GEGLU) {
+        const float cdf = gelu_cdf(z);
+        a = z * cdf;
+        da = cdf + z * (0.39894228040143268f * __expf(-0.5f * z * z));
+    } else if (act == MOE_ACT_SRELU) {
+        const float r = fmaxf(z, 0.0f);
+        a = r * r;
+        da = 2.0f * r;
+    } else {
+        const float s = 1.0f / (1.0f + __expf(-beta * z));
+        a = z * s;
+        da = s + beta * z * s * (1.0f - s);
+    }
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, each with a
+// compile-time index (register arrays indexed by it stay in registers, where
+// an unrolled loop whose body is too large to unroll would index them at
+// run time and move them to scratch memory).
+template <int N, typename F, int I = 0>
+MOE_DEV void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, F, I + 1>(static_cast<F&&>(f));
+    }
+}
 
 // Wave-wide helpers (wave64).
 MOE_DEV float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }

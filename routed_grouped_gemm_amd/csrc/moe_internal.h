@@ -64,6 +64,12 @@ struct GemmArgs {
     uint8_t* hTq; uint8_t* hTs; int ldT;
     uint16_t* y;                 // W2 output
     void* ws; size_t ws_bytes;   // workspace (moe_grouped_workspace_size bytes)
+    // W1 only, optional: the epilogue variant (null: SwiGLU, beta = 1)
+    const moe_epilogue* epi;
+    // backward only: the saved pre-activation and the routing-weight
+    // gradient's per-unit partials (workspace)
+    const uint16_t* pre;
+    float* dw_part;
     // W1 only, optional: route and group the tokens inside the W1 launch
     // (counts, offsets, offsets32, row_src and row_w are then written, not
     // read); only when moe_w1_can_route says so
@@ -77,9 +83,22 @@ int moe_launch_grouped_w2(const GemmArgs& a, hipStream_t stream);
 // LDS-tiled variants for groups with many rows (256 x 256 workgroup tiles)
 int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream);
 int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream);
+// The backward of the fused W1 epilogue on the LDS-tiled kernel: the W2^T
+// GEMM with the dActivation epilogue (outputs in a.hq/hs/hTq/hTs with rows
+// of 2 * a.N bytes, partials of the routing-weight gradient in a.dw_part),
+// then the sum of those partials into dw (when dw is non-null).
+int moe_launch_tiled_backward(const GemmArgs& a, float* dw, hipStream_t stream);
 // Workspace of the tiled kernels: the activation scales rearranged per K-tile
 // and 256-row pass (see gemm_tiled.hip).
 size_t moe_tiled_scale_bytes(int R_max, int G, int K);
+
+// The single-launch decode layer (fused_decode.hip): whether it applies, the
+// words of its control block, and the launch (a1/a2 as moe_layer prepares
+// them for W1, with its routing arguments, and W2).
+bool moe_fused_decode_ok(int T, int E_tot, int k, int E_loc, int s, uint32_t flags);
+size_t moe_fused_ctrl_words(int G, int H);
+int moe_launch_fused_decode(const GemmArgs& a1, const GemmArgs& a2, uint32_t* ctrl, uint16_t* out,
+                            hipStream_t stream);
 
 int moe_launch_combine(const uint16_t* y, const int32_t* slot_row, const float* row_w, int T,
                        int ks, int H, uint16_t* out, hipStream_t stream);

@@ -78,8 +78,8 @@ def test_sizes_are_pure_host_functions():
     R = T * k
     need = R * I + R * I // 32 + 2 * R * H
     assert lib.moe_layer_workspace_size(T, E, k, El, H, I, 0, 0) >= need
-    offs = (C.c_size_t * 12)()
-    assert lib.moe_layer_workspace_offsets(T, E, k, El, H, I, 0, 0, offs) == 12
+    offs = (C.c_size_t * 13)()
+    assert lib.moe_layer_workspace_offsets(T, E, k, El, H, I, 0, 0, offs) == 13
     assert all(o % 256 == 0 for o in offs) and list(offs) == sorted(offs)
 
 
@@ -134,7 +134,7 @@ def test_grouped_w1_status_paths():
     def call(w1=w, counts=F, offsets=F, off32=None, row_w=F, xq=F, xs=F, row_src=None, x_rows=R,
              R_max=R, H=H, I=I, G=G, flags=0, hq=F, hs=F, hTq=None, hTs=None, ws=F, ws_bytes=1 << 30):
         return lib.moe_grouped_w1(C.byref(w1), None, counts, offsets, off32, row_w, xq, xs, row_src,
-                                  x_rows, R_max, H, I, G, flags, hq, hs, hTq, hTs, ws, ws_bytes, None)
+                                  x_rows, R_max, H, I, G, None, flags, hq, hs, hTq, hTs, ws, ws_bytes, None)
 
     both = _lib.MOE_GEMM_STREAMED | _lib.MOE_GEMM_TILED
     assert call(flags=both) == _lib.MOE_ERR_UNSUPPORTED
@@ -220,3 +220,37 @@ def test_noalloc_rejects_workspace_beyond_its_array():
     assert lib.moe_layer_noalloc(C.byref(args), None) == _lib.MOE_OK
     args.T, args.I = 16, 200                       # other argument errors come from moe_layer's checks
     assert lib.moe_layer_noalloc(C.byref(args), None) == _lib.MOE_ERR_SHAPE
+
+
+def test_backward_and_epilogue_status_paths():
+    lib = _lib.load()
+    F = 0x1000
+    I, H, G, R = 256, 512, 4, 64
+    w2t = _w(_lib.MOE_FMT_MXFP8, G, I, H, 0)
+    ok_epi = _lib.moe_epilogue(_lib.MOE_ACT_GEGLU, 1.0, 0.0, 0, None, None)
+
+    def call(w=w2t, epi=None, flags=0, pre=F, dq=F, row_w=F, dw=F, I=I, R_max=R, ws_bytes=1 << 30,
+             dTq=None, off32=None):
+        return lib.moe_grouped_w1_backward(C.byref(w), None, F, F, off32, row_w, F, F, F, R, pre, R_max, H,
+                                           I, G, None if epi is None else C.byref(epi), flags, dq, F, dTq, F,
+                                           dw, F, ws_bytes, None)
+
+    assert lib.moe_backward_workspace_size(R, G, H, I) >= R * (I // 64) * 4
+    assert call(flags=_lib.MOE_ROUTE_RENORM) == _lib.MOE_ERR_UNSUPPORTED
+    assert call(epi=_lib.moe_epilogue(7, 1.0, 0.0, 0, None, None)) == _lib.MOE_ERR_UNSUPPORTED
+    assert call(epi=_lib.moe_epilogue(0, 0.0, 0.0, 0, None, None)) == _lib.MOE_ERR_SHAPE     # beta = 0
+    assert call(epi=_lib.moe_epilogue(0, 1.0, -1.0, 0, None, None)) == _lib.MOE_ERR_SHAPE    # limit < 0
+    assert call(epi=_lib.moe_epilogue(0, float("nan"), 0.0, 0, None, None)) == _lib.MOE_ERR_SHAPE
+    assert call(I=200) == _lib.MOE_ERR_SHAPE
+    assert call(R_max=1 << 21, I=256) == _lib.MOE_ERR_SHAPE                    # R_max * 2I bytes >= 2^31
+    assert call(w=_w(_lib.MOE_FMT_MXFP8, G, 2 * I, H, 0)) == _lib.MOE_ERR_SHAPE  # N must be I
+    assert call(pre=None, epi=ok_epi) == _lib.MOE_ERR_NULL
+    assert call(dq=None) == _lib.MOE_ERR_NULL
+    assert call(row_w=None) == _lib.MOE_ERR_NULL                               # dw needs the weights
+    assert call(flags=_lib.MOE_W1_WRITE_TRANSPOSE) == _lib.MOE_ERR_NULL        # no transposed buffers
+    assert call(ws_bytes=0) == _lib.MOE_ERR_WORKSPACE
+    # the forward's epilogue is validated the same way
+    w1 = _w(_lib.MOE_FMT_MXFP4, G, 2 * I, H, 1)
+    bad = _lib.moe_epilogue(3, 1.0, 0.0, 0, None, None)
+    assert lib.moe_grouped_w1(C.byref(w1), None, F, F, None, F, F, F, None, R, R, H, I, G, C.byref(bad), 0,
+                              F, F, None, None, F, 1 << 30, None) == _lib.MOE_ERR_UNSUPPORTED
