@@ -344,20 +344,16 @@ size_t  moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_
                                  int32_t H, int32_t I, int32_t s, uint32_t flags);
 
 /*
- * Run route -> permute -> W1 -> W2 -> combine on `stream`. With at most 256
- * experts, k <= 16, at most 513 groups and T <= 8, without the transposed
- * copy, MOE_GEMM_TILED or MOE_LAYER_SEPARATE_KERNELS: one persistent launch
- * (the FlashDMoE page's single-kernel layer) in which every workgroup routes
- * and groups the tokens, W2 work on a group starts when that group's W1 work
- * is complete, and the last W2 work item of each 64-column block combines
- * it. Otherwise 3 launches when T <= 8 and groups average under 16 rows
- * (every W1 workgroup routes and groups the tokens itself), 4 when T <= 64
- * (router and grouping share one workgroup), more otherwise. The grouped
- * token rows are not materialised: W1 reads them through row_src.
- * Intermediates live in ws at offsets given by moe_layer_workspace_offsets;
- * the single-launch path keeps its counters in region [12] (a control block
- * it initialises itself on first use and leaves ready after every call; its
- * word 2 is nonzero if a wait between workgroups ever timed out).
+ * Run route -> permute -> W1 -> W2 -> combine on `stream`: 3 launches when
+ * T <= 8 and groups average under 16 rows (every W1 workgroup routes and
+ * groups the tokens itself), 4 when T <= 64 (router and grouping share one
+ * workgroup), more otherwise. The grouped token rows are not materialised:
+ * W1 reads them through row_src. Intermediates live in ws at offsets given
+ * by moe_layer_workspace_offsets. Region [12] is the control block of a
+ * single-launch decode path (every workgroup routes, W2 work on a group
+ * waits for that group's W1 work, the last W2 item of a column block
+ * combines it), which is built but switched off in this version: every call
+ * takes the separate kernels (MOE_LAYER_SEPARATE_KERNELS changes nothing).
  */
 int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 

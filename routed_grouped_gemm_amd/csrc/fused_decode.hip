@@ -45,13 +45,16 @@ namespace {
 constexpr int kFW = 16;                      // waves per workgroup (K split)
 constexpr int kFT = 64 * kFW;
 constexpr int kCoherent = 16;                // sc1: agent-coherent loads and stores
-constexpr int kSpinMax = 1 << 24;            // polls of a wait before it gives up (about 1 s)
+constexpr int kWaitMs = 100;                 // a wait gives up after this long (wall clock)
 constexpr uint32_t kMagicLo = 0x4D6F4521u, kMagicHi = 0x7C3A9E55u;
-constexpr bool kFusedEnabled = false;        // the single-launch path is off until its GPU tests pass
+constexpr bool kFusedEnabled = false;
 
-// control block words: magic (2), error, ticket, exit count, then per group
-// the W1 units done, then per 64-column block the W2 arrivals
-enum { kCtlMagicLo = 0, kCtlMagicHi = 1, kCtlErr = 2, kCtlTick = 3, kCtlExit = 4, kCtlDone = 8 };
+// control block words: magic (2), error, ticket, exit count, the word a
+// timed-out wait watched and the value it last saw, then per group the W1
+// units done, then per 64-column block the W2 arrivals. Error codes: 1 = the
+// wait for the block's initialisation, 2 = a W2 item's wait for its group.
+enum { kCtlMagicLo = 0, kCtlMagicHi = 1, kCtlErr = 2, kCtlTick = 3, kCtlExit = 4, kCtlWhere = 5,
+       kCtlSeen = 6, kCtlDone = 8 };
 
 struct FusedArgs {
     KParams p1, p2;                          // the W1 and W2 parameter blocks (p2.aq/as: h)
@@ -59,6 +62,7 @@ struct FusedArgs {
     uint16_t* out;                           // [T, H] bf16
     int units2;                              // H / 64
     int weight_at_combine;
+    uint64_t wait_ticks;                     // kWaitMs in wall-clock ticks
 };
 
 MOE_DEV uint32_t ld_coherent(const uint32_t* p) {
@@ -68,13 +72,22 @@ MOE_DEV void st_coherent(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until ctrl[idx] >= target (thread 0 of the workgroup).
-MOE_DEV void wait_at_least(uint32_t* ctrl, int idx, uint32_t target) {
-    for (int i = 0; i < kSpinMax; ++i) {
-        if (ld_coherent(ctrl + idx) >= target || ld_coherent(ctrl + kCtlErr) != 0) return;
-        __builtin_amdgcn_s_sleep(2);
+// Wait until ctrl[idx] >= target (thread 0 of the workgroup), for at most
+// `ticks` of the constant-rate wall clock; on a timeout record the error
+// code, the word and its last value, and return (so the launch always ends).
+MOE_DEV void wait_at_least(uint32_t* ctrl, int idx, uint32_t target, uint64_t ticks, uint32_t code) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        const uint32_t v = ld_coherent(ctrl + idx);
+        if (v >= target || ld_coherent(ctrl + kCtlErr) != 0) return;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) {
+            st_coherent(ctrl + kCtlWhere, (uint32_t)idx);
+            st_coherent(ctrl + kCtlSeen, v);
+            st_coherent(ctrl + kCtlErr, code);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(8);
     }
-    st_coherent(ctrl + kCtlErr, 1);
 }
 
 // Sum of the KW waves' partials through KW/2 LDS slots in a fixed tree order;
@@ -204,12 +217,17 @@ void fused_decode_kernel(FusedArgs f) {
                 __builtin_amdgcn_s_waitcnt(0);
                 st_coherent(ctrl + kCtlMagicLo, kMagicLo);
             } else {
-                int i = 0;
-                for (; i < kSpinMax; ++i) {
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                for (;;) {
                     if (ld_coherent(ctrl + kCtlMagicLo) == kMagicLo && ld_coherent(ctrl + kCtlMagicHi) == magic_hi) break;
-                    __builtin_amdgcn_s_sleep(2);
+                    if (__builtin_amdgcn_s_memrealtime() - t0 > f.wait_ticks) {
+                        st_coherent(ctrl + kCtlWhere, kCtlMagicLo);
+                        st_coherent(ctrl + kCtlSeen, ld_coherent(ctrl + kCtlMagicLo));
+                        st_coherent(ctrl + kCtlErr, 1);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(8);
                 }
-                if (i == kSpinMax) st_coherent(ctrl + kCtlErr, 1);
             }
         }
     }
@@ -307,7 +325,7 @@ void fused_decode_kernel(FusedArgs f) {
             const int t2 = t - n1, ai = t2 / units2, c = t2 - ai * units2;
             const int g = act_l[ai];
             const int rbase = off_l[g], nrows = cnt_l[g];
-            if (tid == 0) wait_at_least(ctrl, kCtlDone + g, (uint32_t)units1);
+            if (tid == 0) wait_at_least(ctrl, kCtlDone + g, (uint32_t)units1, f.wait_ticks, 2);
             __syncthreads();
             const int sel = g < q.E_loc ? 0 : 1, gi = g < q.E_loc ? g : 0;
             const uint8_t* wgrp = q.wbase[sel] + gi * q.gstride;
@@ -388,6 +406,20 @@ void fused_decode_kernel(FusedArgs f) {
     }
 }
 
+// The device's constant wall-clock rate in kHz (cached per device; 100 MHz if
+// the attribute is unavailable).
+int wall_clock_khz() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 100000;
+    if (!cached[dev]) {
+        int r = 0;
+        if (hipDeviceGetAttribute(&r, hipDeviceAttributeWallClockRate, dev) != hipSuccess || r <= 0) r = 100000;
+        cached[dev] = r;
+    }
+    return cached[dev];
+}
+
 template <int WFMT, int RT>
 int launch_fused(const FusedArgs& f, hipStream_t stream) {
     auto kern = fused_decode_kernel<WFMT, RT>;
@@ -409,6 +441,11 @@ int launch_fused(const FusedArgs& f, hipStream_t stream) {
 size_t moe_fused_ctrl_words(int G, int H) { return (size_t)kCtlDone + G + H / 64; }
 
 bool moe_fused_decode_ok(int T, int E_tot, int k, int E_loc, int s, uint32_t flags) {
+    // Switched off: on the GPU the first launch of this kernel ran for minutes
+    // instead of microseconds (twice, the second time with every wait bounded
+    // in wall-clock time); the cause is not established (the hand-off's
+    // cross-XCD visibility and the wall clock are the candidates), so every
+    // layer takes the separate-kernel path.
     if (!kFusedEnabled) return false;
     const int G = E_loc + s;
     if (T < 1 || T > 8 || E_tot > 256 || k > 16 || G > 513 || G < 1) return false;
@@ -424,6 +461,7 @@ int moe_launch_fused_decode(const GemmArgs& a1, const GemmArgs& a2, uint32_t* ct
     f.out = out;
     f.units2 = a2.N / 64;
     f.weight_at_combine = (a1.flags & MOE_WEIGHT_AT_COMBINE) ? 1 : 0;
+    f.wait_ticks = (uint64_t)wall_clock_khz() * kWaitMs;
     const bool fp4 = a1.fmt == MOE_FMT_MXFP4;
     const bool wide = a1.route->T <= kFW;   // one token per wave per round
     if (fp4) return wide ? launch_fused<MFMA_FMT_FP4, 64>(f, stream) : launch_fused<MFMA_FMT_FP4, 16>(f, stream);
