@@ -165,6 +165,51 @@ def cpu_oracle_sample(name: str, ntok: int, threads: int):
                       f"fp64 NumPy on the host CPU"}
 
 
+def cpu_oracle_full(names, threads: int, reps: int = 3):
+    """The oracle on whole workloads (every token of routing draw 0): the
+    median wall time of `reps` runs (one run for the 16K-token prefill), with
+    the workload's algorithmic bytes and FLOPs. Minutes of CPU work, so only
+    with --cpu-full."""
+    import numpy as np
+    from oracle import moe as omoe, mx
+    import synth
+    res = {}
+    for name, T in names:
+        c = synth.config(name, T)
+        lg = synth.logits(c, 0)
+        xq, xs = mx.quantize_mx(synth.x(c, 0), mx.FMT_E4M3)
+        idx, _ = omoe.route(lg, c.k)
+        local = [int(e) - c.e0 for e in idx.ravel() if 0 <= int(e) - c.e0 < c.n_local]
+        active = sorted(set(local))
+        w1q, w1s, w2q, w2s = [None] * c.n_local, [None] * c.n_local, [None] * c.n_local, [None] * c.n_local
+        for g in active:
+            w1q[g], w1s[g] = mx.quantize_mx(synth.w1(c, g), c.w_fmt)
+            w2q[g], w2s[g] = mx.quantize_mx(synth.w2(c, g), c.w_fmt)
+        shared = None
+        if c.shared:
+            a1, b1 = mx.quantize_mx(synth.shared_w1(c), c.w_fmt)
+            a2, b2 = mx.quantize_mx(synth.shared_w2(c), c.w_fmt)
+            shared = (a1, b1, a2, b2)
+        n = 1 if name == "prefill" else reps
+        walls = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            omoe.moe_layer(lg, xq, xs, c.k, w1q, w1s, w2q, w2s, c.w_fmt, c.I, e0=c.e0, n_local=c.n_local,
+                           shared=shared, transpose=c.transpose)
+            walls.append(time.perf_counter() - t0)
+            log(f"oracle {name} T={c.T}: {walls[-1]:.1f} s")
+        dt = sorted(walls)[len(walls) // 2]
+        fp4 = c.w_fmt == "e2m1"
+        groups = len(active) + (1 if c.shared else 0)
+        rows = len(local) + (c.T if c.shared else 0)
+        nbytes = layer_bytes(c.T, c.E, c.H, c.I, groups, fp4)
+        res[f"{name}-{c.T}"] = {"wall_s_median": round(dt, 2), "runs": n, "TBps": nbytes / dt / 1e12,
+                                "TFLOPs": 6.0 * rows * c.H * c.I / dt / 1e12, "cores": int(threads),
+                                "kind": "oracle", "sample": f"the whole workload (routing draw 0: {groups} groups, "
+                                                            f"{rows} rows), fp64 NumPy on the host CPU"}
+    return res
+
+
 def oracle_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -210,8 +255,11 @@ def other_workloads(torch, moe, synth, device, names, reps=4):
     the bandwidth-bound shapes, dense FP8 MFMA for prefill."""
     out = {}
     for name in names:
-        c = synth.config(name)
+        ring = name == "prefill_token_ring"          # the prefill with the token ring
+        c = synth.config("prefill" if ring else name)
         flags = moe.MOE_W1_WRITE_TRANSPOSE if c.transpose else 0
+        if ring:
+            flags |= moe.MOE_LAYER_TOKEN_RING
         dw = device.build_weights(c)
         copies = [dw]
         w1 = moe.PackedWeights.empty(c.n_local, 2 * c.I, c.H, dw.w1.fmt, True)
@@ -263,7 +311,7 @@ def other_workloads(torch, moe, synth, device, names, reps=4):
             flops += 6.0 * R * c.H * c.I / 2
         tbps = nbytes / us / 1e6
         tflops = flops / us / 1e6
-        bound = "mfma" if name == "prefill" else "hbm"
+        bound = "mfma" if c.name == "prefill" else "hbm"
         frac = tflops / MFMA_FP8_PEAK_TFLOPS if bound == "mfma" else tbps * 1e3 / HBM_PEAK_GBS
         out[name] = {"T": c.T, "H": c.H, "I": c.I, "E": c.E, "k": c.k, "local": c.n_local,
                      "shared": bool(c.shared), "weights": "MXFP4" if fp4 else "MXFP8",
@@ -276,6 +324,60 @@ def other_workloads(torch, moe, synth, device, names, reps=4):
     return out
 
 
+def backward_workload(torch, moe, synth, device, reps=4):
+    """The backward of the fused W1 epilogue at the 16K-token prefill shape:
+    the forward layer runs once with the BF16 pre-activation saved, then the
+    backward (dh = dy . W2^T on MFMA, the SwiGLU derivative with the routing
+    weight, MX-E4M3 rows and 32-row transposed blocks of [dg | du], dw) on
+    that grouping, with W2^T quantised along H and prepacked, and dy a seeded
+    N(0, 1) gradient quantised to MXFP8. Timed with HIP events around `reps`
+    back-to-back calls after one untimed call; FLOPs 2 R H I."""
+    import numpy as np
+    c = synth.config("prefill")
+    fmt = moe.MOE_FMT_MXFP8
+    dw = device.build_weights(c)
+    w2t = moe.PackedWeights.empty(c.n_local, c.I, c.H, fmt, False)
+    for g in range(c.n_local):
+        q, sc = moe.moe_quantize_mx(torch.from_numpy(np.ascontiguousarray(synth.w2(c, g).T)).cuda(), fmt)
+        w2t.fill_group(g, q, sc)
+    logits, xq, xs = device.build_inputs(c)
+    flags = moe.MOE_W1_WRITE_TRANSPOSE
+    ws = moe.LayerWorkspace(c.T, c.E, c.k, c.n_local, c.H, c.I, False, flags)
+    ld = moe.moe_transposed_ld(c.R_max, c.G)
+    hT = (torch.empty((c.I, ld), dtype=torch.uint8, device="cuda"),
+          torch.empty((c.I, ld // 32), dtype=torch.uint8, device="cuda"))
+    pre = torch.empty((c.R_max, 2 * c.I), dtype=torch.uint16, device="cuda")
+    moe.moe_layer(logits, xq, xs, dw.w1, dw.w2, c.k, c.e0, c.n_local, None, flags, ws=ws, hTq=hT[0], hTs=hT[1],
+                  epi=moe.Epilogue(save_pre=pre))
+    g32 = torch.Generator(device="cpu").manual_seed(c.seed + 77)
+    dyq, dys = moe.moe_quantize_mx(torch.randn((c.T, c.H), generator=g32).cuda(), fmt)
+    R = int(ws.view("counts").sum().item())
+
+    def call():
+        return moe.moe_grouped_w1_backward(w2t, ws.view("counts"), ws.view("offsets"), ws.view("row_w"), dyq, dys,
+                                           ws.view("row_src"), pre, c.I, flags=moe.MOE_W1_WRITE_TRANSPOSE,
+                                           offsets32=ws.view("offsets32"))
+    call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    keep = [call() for _ in range(reps)]
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del keep
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    flops = 2.0 * R * c.H * c.I
+    res = {"T": c.T, "H": c.H, "I": c.I, "E": c.E, "k": c.k, "rows": R, "weights": "MXFP8 (W2 transposed)",
+           "latency_us": round(us, 2), "TFLOPs": round(flops / us / 1e6, 1), "bound": "mfma",
+           "roofline_frac": round(flops / us / 1e6 / MFMA_FP8_PEAK_TFLOPS, 4),
+           "work": "dh = dy . W2^T, SwiGLU derivative, MX-E4M3 rows + 32-row transposed blocks, dw"}
+    log(f"prefill_backward: {res}")
+    del dw, w2t, ws, hT, pre
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,9 +385,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated between calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the oracle on every whole workload (median of 3; minutes of CPU work)")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the latency lines of the tiny, full-expert, prefill and shared-expert workloads")
-    ap.add_argument("--only", choices=["tiny", "full", "prefill", "shared"],
+    ap.add_argument("--only", choices=["tiny", "full", "prefill", "shared", "prefill_token_ring",
+                                       "prefill_backward"],
                     help="time only this workload's layer (no decode bench, no oracle) and print its line; "
                          "for profiling one workload")
     args = ap.parse_args()
@@ -302,7 +407,10 @@ def main():
 
     torch.cuda.set_device(0)
     if args.only:
-        print(json.dumps(other_workloads(torch, moe, synth, device, [args.only])), flush=True)
+        if args.only == "prefill_backward":
+            print(json.dumps({"prefill_backward": backward_workload(torch, moe, synth, device)}), flush=True)
+        else:
+            print(json.dumps(other_workloads(torch, moe, synth, device, [args.only])), flush=True)
         return
     c = synth.config("decode", 128)
     fp4 = c.w_fmt == "e2m1"
@@ -505,7 +613,9 @@ def main():
 
     others = None
     if not args.no_other_workloads:
-        others = other_workloads(torch, moe, synth, device, ["tiny", "full", "prefill", "shared"])
+        others = other_workloads(torch, moe, synth, device, ["tiny", "full", "prefill", "shared",
+                                                            "prefill_token_ring"])
+        others["prefill_backward"] = backward_workload(torch, moe, synth, device)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -516,6 +626,13 @@ def main():
             for name, ntok in ORACLE_SAMPLE_TOKENS.items():
                 others[name]["cpu_oracle"] = cpu_oracle_sample(name, ntok, threads)
                 log(f"{name} oracle: {others[name]['cpu_oracle']}")
+
+    cpu_full = None
+    if args.cpu_full:
+        import numpy  # noqa: F401
+        cpu_full = cpu_oracle_full([("tiny", None), ("decode", 1), ("decode", 8), ("decode", 32),
+                                    ("decode", 128), ("shared", None), ("full", None), ("prefill", None)],
+                                   oracle_threads())
 
     line = {
         "metric": "MoE layer latency µs + achieved HBM TB/s (decode), MFMA TFLOPS (prefill)",
@@ -540,6 +657,8 @@ def main():
         "cpu_baseline": cpu,
         "other_workloads": others,
     }
+    if cpu_full is not None:
+        line["cpu_oracle_full"] = cpu_full
     print(json.dumps(line), flush=True)
 
 

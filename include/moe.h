@@ -82,6 +82,20 @@ extern "C" {
 /* moe_layer: run the separate kernels (router, grouping, W1, W2, combine)
  * even where the single-launch decode path applies (see moe_layer). */
 #define MOE_LAYER_SEPARATE_KERNELS (1u << 10)
+/* moe_layer, when W1 runs on the LDS-tiled kernel (many rows per group): the
+ * token dispatch as a producer on a second stream. The GC-MoE page's role1
+ * fills a token ring in blocks of BM rows and publishes each filled block;
+ * role2 runs W1 on filled blocks. Here a producer kernel copies the grouped
+ * token rows of 64 256-row blocks at a time into one of two ring slots in the
+ * workspace (and writes their scale tiles), on a library stream restricted
+ * to 16 compute units where the runtime can create one; W1 runs on each
+ * chunk once its "filled" event has fired, on the caller's stream, leaving
+ * those 16 units to the producer; the producer refills a slot after the
+ * chunk using it has been consumed ("consumed" event). No workgroup waits on
+ * another. Results are identical to the unflagged call; the flag is ignored
+ * when W1 takes the weight-streaming kernel. Not for calls on the same GPU
+ * from several threads at once (the library's stream and events are shared). */
+#define MOE_LAYER_TOKEN_RING (1u << 11)
 
 /* ---- epilogue variants of the fused W1 epilogue ------------------------ */
 /*

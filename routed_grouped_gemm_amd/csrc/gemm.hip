@@ -399,6 +399,12 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
 
 int moe_launch_grouped_w1(const GemmArgs& a, hipStream_t stream) { return launch_grouped<true>(a, stream); }
 
+// Whether launch_grouped runs these arguments on the LDS-tiled kernel.
+bool moe_grouped_uses_tiled(const GemmArgs& a) {
+    const int avg = expected_rows(a.rows_hint, a.R_max, a.G);
+    return (a.flags & MOE_GEMM_TILED) || (!(a.flags & MOE_GEMM_STREAMED) && avg >= kTiledMinRows);
+}
+
 // The conditions under which launch_grouped<true> takes the one-token-tile,
 // non-temporal path, plus the limits of the in-workgroup routing (at most
 // 256 experts, k <= 16, T <= 8 tokens, at most 513 groups).

@@ -29,6 +29,10 @@ struct KParams {
     const uint32_t* bst;              // tiled kernels: activation scales per K-tile and pass
     uint32_t bst_bytes;
     int npass;                        // passes the scale tiles are laid out for
+    // tiled kernels: the work items [item_lo, item_hi) only; with ring_pass0
+    // >= 0 the token rows come from a ring slot (aq) holding the grouped rows
+    // from the first row of pass ring_pass0 on, one after another
+    int item_lo, item_hi, ring_pass0;
     // W1 epilogue variant (act, beta, clamp limit, per-group bias [G][2I],
     // optional BF16 copy of the pre-activation [R_max, 2I]); generic = 0 is
     // SwiGLU with beta = 1 and none of the options
@@ -108,6 +112,9 @@ inline KParams make_params(const GemmArgs& a, bool w1) {
         p.topk_idx = a.route->topk_idx; p.topk_w = a.route->topk_w; p.slot_row = a.route->slot_row;
     }
     p.R_max = a.R_max;
+    p.item_lo = 0;
+    p.item_hi = 0x7FFFFFFF;
+    p.ring_pass0 = -1;
     return p;
 }
 

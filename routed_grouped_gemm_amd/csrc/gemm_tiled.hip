@@ -63,6 +63,8 @@ constexpr int kAT = 4;                      // 16-row weight tiles per wave (one
 constexpr int kTStride = 136;               // bytes per feature row of the transposed staging
 constexpr int kTWave = 32 * kTStride;       // per-wave staging of the transposed copy
 constexpr int kYStride = 144;               // bytes per token row of the BF16 output staging (conflict-free)
+constexpr int kRingPasses = 64;             // token ring: 256-row passes per chunk (one slot)
+constexpr int kRingCUs = 16;                // compute units the W1 consumer leaves to the ring's producer
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -92,7 +94,7 @@ struct Ctx {
     int pidx;                               // pass index over all groups (scale tile column)
 };
 
-MOE_DEV Ctx decode(const KParams& p, const int* pass_off, int item, int wtiles, int w, int lane) {
+MOE_DEV Ctx decode(const KParams& p, const int* pass_off, int item, int wtiles, int w, int lane, int r0) {
     Ctx c;
     const int pg = item / wtiles;
     c.wt = item - pg * wtiles;
@@ -123,7 +125,7 @@ MOE_DEV Ctx decode(const KParams& p, const int* pass_off, int item, int wtiles, 
     #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 32 * w + 8 * i + (lane >> 3);
-        const uint32_t src = p.row_src ? xr[i] : (uint32_t)(c.rbase + row);
+        const uint32_t src = p.row_src ? xr[i] : (uint32_t)(c.rbase + row - r0);
         c.xoff[i] = row < c.nrows ? src * (uint32_t)p.K : kInvalid;
     }
     return c;
@@ -277,10 +279,22 @@ void tiled_gemm_kernel(KParams p) {
     const int wi = w & 3, ti = w >> 2;       // weight unit, token half
     if (w == 0) pass_prefix(p.counts, G, kRows, lane, pass_off);
     __syncthreads();
-    const int n_items = pass_off[G] * wtiles;
+    // the items of this launch: [item_lo, item_hi) of all (pass, weight tile) items
+    const int i_lo = p.item_lo, i_hi = min(p.item_hi, pass_off[G] * wtiles);
+    const int n_items = max(0, i_hi - i_lo);
     const int grid = gridDim.x;
     const int slot = (grid % 8 == 0) ? (blockIdx.x % 8) * (grid / 8) + blockIdx.x / 8 : blockIdx.x;
     if (slot >= n_items) return;
+    // token rows from a ring slot: the slot's first row is the first row of pass ring_pass0
+    int r0 = 0;
+    if (p.ring_pass0 >= 0) {
+        int glo = 0, ghi = G;                   // largest g with pass_off[g] <= ring_pass0
+        while (ghi - glo > 1) {
+            const int mid = (glo + ghi) >> 1;
+            if (pass_off[mid] <= p.ring_pass0) glo = mid; else ghi = mid;
+        }
+        r0 = p.offsets[glo] + (p.ring_pass0 - pass_off[glo]) * kRows;
+    }
     const int n_my = (n_items - slot + grid - 1) / grid;                 // this workgroup's items
     const int nkt = p.kt;
     const int total = n_my * nkt;
@@ -288,8 +302,8 @@ void tiled_gemm_kernel(KParams p) {
     const rsrc_t rx = make_rsrc(p.aq, p.aq_bytes);
     const rsrc_t rxs = make_rsrc(p.bst, p.bst_bytes);
 
-    Ctx cur = decode(p, pass_off, slot, wtiles, w, lane);
-    Ctx nxt = n_my > 1 ? decode(p, pass_off, slot + grid, wtiles, w, lane) : cur;
+    Ctx cur = decode(p, pass_off, i_lo + slot, wtiles, w, lane, r0);
+    Ctx nxt = n_my > 1 ? decode(p, pass_off, i_lo + slot + grid, wtiles, w, lane, r0) : cur;
 
     stage_all<WFMT>(p, rx, rxs, cur, 0, true, ring, w, lane);
     __builtin_amdgcn_s_waitcnt(0);
@@ -624,7 +638,7 @@ void tiled_gemm_kernel(KParams p) {
             __syncthreads();                 // scratch free before the next prefetch lands in it
         }
         cur = nxt;
-        if (it + 2 < n_my) nxt = decode(p, pass_off, slot + (it + 2) * grid, wtiles, w, lane);
+        if (it + 2 < n_my) nxt = decode(p, pass_off, i_lo + slot + (it + 2) * grid, wtiles, w, lane, r0);
     }
 }
 
@@ -636,12 +650,12 @@ void tiled_gemm_kernel(KParams p) {
 __global__ __launch_bounds__(kRows)
 void scale_tiles_kernel(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int G,
                         const int32_t* __restrict__ row_src, const uint8_t* as, uint32_t as_bytes,
-                        int K, int npass, uint32_t* __restrict__ out) {
+                        int K, int npass, uint32_t* __restrict__ out, int pass_lo = 0) {
     extern __shared__ int pass_off[];                                   // [G + 1]
     const int tid = threadIdx.x;
     if (tid < 64) pass_prefix(counts, G, kRows, tid, pass_off);
     __syncthreads();
-    const int b = blockIdx.x;
+    const int b = pass_lo + (int)blockIdx.x;
     if (b >= pass_off[G]) return;
     int glo = 0, ghi = G;                   // largest g with pass_off[g] <= b
     while (ghi - glo > 1) {
@@ -664,8 +678,80 @@ void scale_tiles_kernel(const int32_t* __restrict__ counts, const int32_t* __res
         if (kt0 + i < nkt) out[((size_t)(kt0 + i) * npass + b) * kRows + tid] = v[i];
 }
 
+// Token ring fill: the grouped token rows of passes [pass0, pass0 + gridDim.x)
+// copied one after another into a ring slot (the slot's first row is the
+// first row of pass pass0), and their scale tiles written as
+// scale_tiles_kernel writes them. Workgroup (x, y) serves rows
+// [32y, 32y + 32) of pass pass0 + x: 16-byte pieces with kFillBatch loads in
+// flight per thread before their stores; passes past the total are skipped.
+constexpr int kFillRows = 32;               // rows per fill workgroup
+constexpr int kFillBatch = 8;               // 16-byte loads in flight per thread
+
+__global__ __launch_bounds__(kRows)
+void ring_fill_kernel(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int G,
+                      const int32_t* __restrict__ row_src, const uint8_t* __restrict__ xq, uint32_t x_bytes,
+                      const uint8_t* as, uint32_t as_bytes, int K, int npass, uint32_t* __restrict__ tiles,
+                      int pass0, uint8_t* __restrict__ ring, uint32_t ring_bytes) {
+    extern __shared__ int pass_off[];                                   // [G + 1], then kFillRows sources
+    int* src_row = pass_off + G + 1;
+    const int tid = threadIdx.x;
+    if (tid < 64) pass_prefix(counts, G, kRows, tid, pass_off);
+    __syncthreads();
+    const int b = pass0 + (int)blockIdx.x;
+    if (b >= pass_off[G] || pass0 >= pass_off[G]) return;
+    auto row_of = [&](int pass) {           // group and first grouped row of a pass
+        int glo = 0, ghi = G;
+        while (ghi - glo > 1) {
+            const int mid = (glo + ghi) >> 1;
+            if (pass_off[mid] <= pass) glo = mid; else ghi = mid;
+        }
+        return std::pair<int, int>(glo, offsets[glo] + (pass - pass_off[glo]) * kRows);
+    };
+    const auto [g, pstart] = row_of(b);
+    const int r0 = row_of(pass0).second;
+    const int rin0 = kFillRows * (int)blockIdx.y;                       // first row within the pass
+    const int rstart = pstart + rin0;
+    const int nrows = max(0, min(kFillRows, offsets[g] + counts[g] - rstart));
+    if (tid < kFillRows) src_row[tid] = tid < nrows ? row_src[rstart + tid] : -1;
+    __syncthreads();
+
+    // scale tiles of these rows (0 past the group's end)
+    const rsrc_t rs = make_rsrc(as, as_bytes);
+    const int nkt = K / 128;
+    for (int t = tid; t < kFillRows * nkt; t += kRows) {
+        const int i = t % kFillRows, kt = t / kFillRows;
+        const int src = src_row[i];
+        const uint32_t v = src >= 0 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                                          rs, (uint32_t)src * (uint32_t)(K / 32) + 4u * kt, 0, 0)
+                                    : 0u;
+        tiles[((size_t)kt * npass + b) * kRows + rin0 + i] = v;
+    }
+
+    // token rows
+    const rsrc_t rx = make_rsrc(xq, x_bytes);
+    const rsrc_t rr = make_rsrc(ring, ring_bytes);
+    const int chunks = K / 16;                                          // 16-byte pieces per row
+    const int n = nrows * chunks;
+    for (int e0 = 0; e0 < n; e0 += kRows * kFillBatch) {
+        i32x4 v[kFillBatch];
+        uint32_t dst[kFillBatch];
+        #pragma unroll
+        for (int j = 0; j < kFillBatch; ++j) {
+            const int e = e0 + j * kRows + tid;
+            const int i = e / chunks, c = e - i * chunks;
+            const bool ok = e < n;
+            const uint32_t src = ok ? (uint32_t)src_row[i] : 0u;
+            v[j] = ok ? __builtin_amdgcn_raw_buffer_load_b128(rx, src * (uint32_t)K + 16 * c, 0, 0) : i32x4{0, 0, 0, 0};
+            dst[j] = ok ? (uint32_t)(rstart + i - r0) * K + 16 * c : 0xFFFFFFFFu;
+        }
+        #pragma unroll
+        for (int j = 0; j < kFillBatch; ++j)
+            if (dst[j] != 0xFFFFFFFFu) __builtin_amdgcn_raw_buffer_store_b128(v[j], rr, dst[j], 0, 0);
+    }
+}
+
 template <int WFMT, int MODE>
-int launch_tiled(const KParams& p, int R_max, hipStream_t stream) {
+int launch_tiled(const KParams& p, int R_max, hipStream_t stream, int max_grid = 0) {
     auto kern = tiled_gemm_kernel<WFMT, MODE>;
     const size_t lds = 2 * (size_t)Stage<WFMT>::Bytes + (size_t)(p.G + 1) * 4;
     int per_cu = 0;
@@ -674,7 +760,8 @@ int launch_tiled(const KParams& p, int R_max, hipStream_t stream) {
     const long wtiles = (p.N / 64 + kUnits - 1) / kUnits;
     // passes never exceed R_max / 256 + G: each group adds at most one partial pass
     const long max_items = wtiles * ((long)R_max / kRows + p.G);
-    const long grid = std::max<long>(1, std::min<long>(max_items, (long)per_cu * device_cu_count()));
+    long grid = std::max<long>(1, std::min<long>(max_items, (long)per_cu * device_cu_count()));
+    if (max_grid > 0) grid = std::min<long>(grid, max_grid);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
     return (int)hipGetLastError();
 }
@@ -707,6 +794,9 @@ int launch_scale_tiles(const GemmArgs& a, KParams& p, hipStream_t stream) {
 
 }  // namespace
 
+// bytes of one token-ring slot: kRingPasses passes of 256 rows of K bytes
+size_t moe_ring_slot_bytes(int K) { return (size_t)kRingPasses * kRows * K; }
+
 // passes never exceed R_max / 256 + G (each group adds at most one partial
 // pass); one 4-byte word per row, pass and K-tile
 size_t moe_tiled_scale_bytes(int R_max, int G, int K) {
@@ -723,6 +813,58 @@ int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream) {
                    : launch_tiled<MFMA_FMT_FP8, kModeW1Gen>(p, a.R_max, stream);
     return fp4 ? launch_tiled<MFMA_FMT_FP4, kModeW1>(p, a.R_max, stream)
                : launch_tiled<MFMA_FMT_FP8, kModeW1>(p, a.R_max, stream);
+}
+
+// W1 fed through a token ring (see moe_layer, MOE_LAYER_TOKEN_RING): chunks of
+// kRingPasses passes; for chunk c, on `side`: wait until the slot's previous
+// chunk is consumed (event), fill the slot with the chunk's rows and write
+// their scale tiles (one kernel), record "ready"; on `stream`: wait for "ready", run W1 on the chunk's
+// items (grid capped so that kRingCUs compute units stay free for the
+// producer), record "consumed". ev: [0] fork, [1 + s] ready of slot s,
+// [1 + slots + s] consumed of slot s.
+int moe_launch_tiled_w1_ring(const GemmArgs& a, uint8_t* ring, size_t slot_bytes, int slots,
+                             hipStream_t stream, hipStream_t side, hipEvent_t* ev) {
+    if (a.G == 0 || a.R_max == 0) return 0;
+    KParams p = make_params(a, true);
+    const int npass = a.R_max / kRows + a.G;                 // every pass the layout allows
+    const size_t need = moe_tiled_scale_bytes(a.R_max, a.G, a.K);
+    if (!a.ws || a.ws_bytes < need || need > 0x7FFFFFFFu) return (int)hipErrorInvalidValue;
+    p.bst = (const uint32_t*)a.ws;
+    p.bst_bytes = (uint32_t)need;
+    p.npass = npass;
+    const int wtiles = (a.N / 64 + kUnits - 1) / kUnits;     // as the kernel counts them
+    const int chunks = (npass + kRingPasses - 1) / kRingPasses;
+    const int max_grid = std::max(1, device_cu_count() - kRingCUs);
+    const bool fp4 = a.fmt == MOE_FMT_MXFP4;
+    int e;
+    if ((e = (int)hipEventRecord(ev[0], stream))) return e;
+    if ((e = (int)hipStreamWaitEvent(side, ev[0], 0))) return e;
+    for (int c = 0; c < chunks; ++c) {
+        const int sl = c % slots;
+        uint8_t* slot = ring + (size_t)sl * slot_bytes;
+        if (c >= slots && (e = (int)hipStreamWaitEvent(side, ev[1 + slots + sl], 0))) return e;
+        hipLaunchKernelGGL(ring_fill_kernel, dim3(kRingPasses, kRows / kFillRows), dim3(kRows),
+                           (size_t)(a.G + 1 + kFillRows) * 4, side, a.counts, a.offsets, a.G, a.row_src, a.aq,
+                           p.aq_bytes, a.as, p.as_bytes, a.K, npass, (uint32_t*)a.ws, c * kRingPasses, slot,
+                           (uint32_t)slot_bytes);
+        if ((e = (int)hipGetLastError())) return e;
+        if ((e = (int)hipEventRecord(ev[1 + sl], side))) return e;
+        if ((e = (int)hipStreamWaitEvent(stream, ev[1 + sl], 0))) return e;
+        KParams q = p;
+        q.item_lo = c * kRingPasses * wtiles;
+        q.item_hi = (c + 1) * kRingPasses * wtiles;
+        q.ring_pass0 = c * kRingPasses;
+        q.aq = slot;
+        q.aq_bytes = (uint32_t)slot_bytes;
+        q.row_src = nullptr;
+        e = p.generic ? (fp4 ? launch_tiled<MFMA_FMT_FP4, kModeW1Gen>(q, a.R_max, stream, max_grid)
+                             : launch_tiled<MFMA_FMT_FP8, kModeW1Gen>(q, a.R_max, stream, max_grid))
+                      : (fp4 ? launch_tiled<MFMA_FMT_FP4, kModeW1>(q, a.R_max, stream, max_grid)
+                             : launch_tiled<MFMA_FMT_FP8, kModeW1>(q, a.R_max, stream, max_grid));
+        if (e) return e;
+        if ((e = (int)hipEventRecord(ev[1 + slots + sl], stream))) return e;
+    }
+    return 0;
 }
 
 int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream) {

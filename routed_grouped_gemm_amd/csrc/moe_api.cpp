@@ -6,6 +6,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 #define MOE_EXPORT extern "C" __attribute__((visibility("default")))
@@ -34,7 +36,9 @@ struct LayerLayout {
     size_t total;
 };
 
-LayerLayout layer_layout(int T, int E_tot, int k, int E_loc, int H, int I, int s) {
+constexpr int kRingSlots = 2;
+
+LayerLayout layer_layout(int T, int E_tot, int k, int E_loc, int H, int I, int s, uint32_t flags) {
     (void)E_tot;
     const size_t R = (size_t)T * k + (size_t)s * T;
     const int G = E_loc + s;
@@ -56,6 +60,8 @@ LayerLayout layer_layout(int T, int E_tot, int k, int E_loc, int H, int I, int s
     size_t gws1 = moe_grouped_workspace_size((int)R, G, 2 * I, H);
     size_t gws2 = moe_grouped_workspace_size((int)R, G, H, I);
     size_t pws = moe_permute_workspace_size(T, k, G);
+    // with the token ring, the ring's slots follow W1's scale tiles
+    if (flags & MOE_LAYER_TOKEN_RING) gws1 = align_up(gws1) + kRingSlots * moe_ring_slot_bytes(H);
     size_t scr = pws > gws1 ? pws : gws1;
     sz[11] = scr > gws2 ? scr : gws2;
     LayerLayout L;
@@ -66,6 +72,55 @@ LayerLayout layer_layout(int T, int E_tot, int k, int E_loc, int H, int I, int s
     }
     L.total = o;
     return L;
+}
+
+// The token ring's producer stream and its events, one set per device,
+// created on first use. The stream has the default priority; it is
+// restricted to kRingProducerCUs compute units (every 16th) where the
+// runtime can create such a stream, and unrestricted otherwise.
+constexpr int kRingProducerCUs = 16;
+struct RingResources {
+    hipStream_t side = nullptr;
+    hipEvent_t ev[1 + 2 * kRingSlots] = {};
+    bool cu_masked = false;
+};
+std::mutex g_ring_lock;
+RingResources g_ring[64];
+
+const RingResources* ring_resources() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> hold(g_ring_lock);
+    RingResources& r = g_ring[dev];
+    if (!r.side) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return nullptr;
+        const int words = (cus + 31) / 32;
+        uint32_t mask[64] = {};
+        const int stride = cus / kRingProducerCUs > 0 ? cus / kRingProducerCUs : 1;
+        for (int i = 0; i < kRingProducerCUs && i * stride < cus && words <= 64; ++i)
+            mask[(i * stride) / 32] |= 1u << ((i * stride) % 32);
+        hipStream_t s = nullptr;
+        if (words <= 64 && hipExtStreamCreateWithCUMask(&s, (uint32_t)words, mask) == hipSuccess && s) {
+            r.cu_masked = true;
+        } else {
+            (void)hipGetLastError();           // the failed creation's error must not reach later calls
+            s = nullptr;
+            if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess || !s) {
+                (void)hipGetLastError();
+                return nullptr;
+            }
+        }
+        for (auto& e : r.ev) {
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+                (void)hipGetLastError();
+                return nullptr;
+            }
+        }
+        r.side = s;
+    }
+    return &r;
 }
 
 }  // namespace
@@ -383,17 +438,15 @@ MOE_EXPORT int32_t moe_combine(const uint16_t* y, const int32_t* slot_row, const
 // ------------------------------------------------------------------ layer
 MOE_EXPORT size_t moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
                                            int32_t H, int32_t I, int32_t s, uint32_t flags) {
-    (void)flags;
     if (T < 0 || k < 1 || E_loc < 1 || H <= 0 || I <= 0 || (s != 0 && s != 1)) return 0;
-    return layer_layout(T, E_tot, k, E_loc, H, I, s).total;
+    return layer_layout(T, E_tot, k, E_loc, H, I, s, flags).total;
 }
 
 MOE_EXPORT int32_t moe_layer_workspace_offsets(int32_t T, int32_t E_tot, int32_t k, int32_t E_loc,
                                                int32_t H, int32_t I, int32_t s, uint32_t flags,
                                                size_t* offsets13) {
-    (void)flags;
     if (!offsets13) return 0;
-    LayerLayout L = layer_layout(T, E_tot, k, E_loc, H, I, s);
+    LayerLayout L = layer_layout(T, E_tot, k, E_loc, H, I, s, flags);
     memcpy(offsets13, L.off, sizeof(L.off));
     return kRegions;
 }
@@ -428,7 +481,7 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     if (!a->logits || !a->xq || !a->xs || !a->out) return MOE_ERR_NULL;
     const int R_max = T * k + s * T;
     if ((st = check_grouped_sizes(R_max, G, T, H, I, transpose))) return st;
-    const LayerLayout L = layer_layout(T, E_tot, k, E_loc, H, I, s);
+    const LayerLayout L = layer_layout(T, E_tot, k, E_loc, H, I, s, a->flags);
     if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
 
     char* base = (char*)ws;
@@ -476,6 +529,11 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
     const bool self_route = moe_w1_can_route(T, E_tot, k, E_loc, s, R_max, H, I, hint, a->flags);
     if (self_route) a1.route = &ra;
 
+    // the token ring (W1 on the LDS-tiled kernel only)
+    const bool ring = (a->flags & MOE_LAYER_TOKEN_RING) && !self_route && moe_grouped_uses_tiled(a1);
+    const RingResources* rr = nullptr;
+    if (ring && !(rr = ring_resources())) return MOE_ERR_HIP;
+
     int e;
     if (self_route) {
         // routing and grouping happen inside the W1 launch below
@@ -492,7 +550,13 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
                                scratch, stream);
         if (e) return MOE_ERR_HIP;
     }
-    if ((e = moe_launch_grouped_w1(a1, stream))) return MOE_ERR_HIP;
+    if (ring) {
+        // the scale tiles first, then the ring slots, in the scratch region
+        uint8_t* slots = (uint8_t*)scratch + align_up(moe_grouped_workspace_size(R_max, G, 2 * I, H));
+        e = moe_launch_tiled_w1_ring(a1, slots, moe_ring_slot_bytes(H), kRingSlots, stream, rr->side,
+                                     const_cast<hipEvent_t*>(rr->ev));
+        if (e) return MOE_ERR_HIP;
+    } else if ((e = moe_launch_grouped_w1(a1, stream))) return MOE_ERR_HIP;
     if ((e = moe_launch_grouped_w2(a2, stream))) return MOE_ERR_HIP;
     const bool wc = (a->flags & MOE_WEIGHT_AT_COMBINE) != 0;
     e = moe_launch_combine(y, slot_row, wc ? row_w : nullptr, T, k + s, H, a->out, stream);

@@ -80,6 +80,8 @@ int moe_launch_grouped_w1(const GemmArgs& a, hipStream_t stream);
 bool moe_w1_can_route(int T, int E_tot, int k, int E_loc, int s, int R_max, int H, int I,
                       int rows_hint, uint32_t flags);
 int moe_launch_grouped_w2(const GemmArgs& a, hipStream_t stream);
+// Whether the grouped GEMM launch takes the LDS-tiled kernel for these arguments.
+bool moe_grouped_uses_tiled(const GemmArgs& a);
 // LDS-tiled variants for groups with many rows (256 x 256 workgroup tiles)
 int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream);
 int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream);
@@ -88,6 +90,11 @@ int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream);
 // of 2 * a.N bytes, partials of the routing-weight gradient in a.dw_part),
 // then the sum of those partials into dw (when dw is non-null).
 int moe_launch_tiled_backward(const GemmArgs& a, float* dw, hipStream_t stream);
+// W1 on the LDS-tiled kernel fed through a token ring filled on `side`
+// (events ev: 1 + 2 * slots), and the bytes of one ring slot for K.
+int moe_launch_tiled_w1_ring(const GemmArgs& a, uint8_t* ring, size_t slot_bytes, int slots,
+                             hipStream_t stream, hipStream_t side, hipEvent_t* ev);
+size_t moe_ring_slot_bytes(int K);
 // Workspace of the tiled kernels: the activation scales rearranged per K-tile
 // and 256-row pass (see gemm_tiled.hip).
 size_t moe_tiled_scale_bytes(int R_max, int G, int K);
