@@ -72,13 +72,20 @@ extern "C" {
                                             instead of the OCP floor rule        */
 /* Kernel family of the grouped GEMMs (moe_grouped_w1 / moe_grouped_w2). By
  * default the library chooses from the expected rows per group, R_max / G:
- * below 96 the weight-streaming kernel (weights read once, K split across
- * waves), from 96 the LDS-tiled kernel (256 x 256 workgroup tiles). These
- * flags override the choice; setting both is MOE_ERR_UNSUPPORTED. The two
- * families sum the fp32 partial products in different orders, so their
- * results may differ in the last bits of the accumulation. */
+ * below 16 the weight-streaming kernel (weights read once, K split across
+ * waves); from 16 to 95 the pass-resident streaming kernel (a pass of 16 or
+ * 32 token rows staged in on-chip memory once, each weight unit streamed over
+ * the whole K by one wave), where its staging fits (K * 16 bytes of rows plus
+ * scales within the 160 KiB of a compute unit; 32-row passes with the
+ * transposed copy), else the K-split kernel; from 96 the LDS-tiled kernel
+ * (256 x 256 workgroup tiles). These flags override the choice (a forced
+ * pass-resident kernel whose staging does not fit runs the K-split kernel);
+ * setting more than one is MOE_ERR_UNSUPPORTED. The families sum the fp32
+ * partial products in different orders, so their results may differ in the
+ * last bits of the accumulation. */
 #define MOE_GEMM_STREAMED      (1u << 8)
 #define MOE_GEMM_TILED         (1u << 9)
+#define MOE_GEMM_PASS          (1u << 12)
 /* moe_layer: run the separate kernels (router, grouping, W1, W2, combine)
  * even where the single-launch decode path applies (see moe_layer). */
 #define MOE_LAYER_SEPARATE_KERNELS (1u << 10)
@@ -261,7 +268,7 @@ int32_t moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t T, int
  * w1 holds the routed groups [0, E_loc); w1_shared (NULL when G == E_loc)
  * holds group E_loc. hq [R_max, I], hs [R_max, I/32]; rows >= R untouched.
  * The launch configuration is chosen from R_max and G alone (expected rows
- * per group R_max / G, see MOE_GEMM_STREAMED / MOE_GEMM_TILED), so a caller
+ * per group R_max / G, see MOE_GEMM_STREAMED / MOE_GEMM_PASS / MOE_GEMM_TILED), so a caller
  * gets the best configuration by passing the tightest R_max it can
  * guarantee. R_max * I < 2^31; with the transposed copy I * ldT < 2^31.
  * ws: moe_grouped_workspace_size(...) bytes.
@@ -314,7 +321,7 @@ int32_t moe_grouped_w1_backward(const moe_weights* w2t, const moe_weights* w2t_s
  * y[r] = BF16_RNE(dec(hq[r]) . dec(W2_g)^T) for every row r of group g
  * (W2 produces BF16 fragments: GC-MoE page, "Approach"). hq [R_max, I],
  * hs [R_max, I/32], y bf16 [R_max, H]; rows >= R untouched. flags: only
- * MOE_GEMM_STREAMED / MOE_GEMM_TILED; the configuration is chosen as for
+ * MOE_GEMM_STREAMED / MOE_GEMM_PASS / MOE_GEMM_TILED; the configuration is chosen as for
  * moe_grouped_w1. R_max * I < 2^31.
  */
 int32_t moe_grouped_w2(const moe_weights* w2, const moe_weights* w2_shared,

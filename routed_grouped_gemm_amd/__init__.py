@@ -15,7 +15,8 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_ACT_GEGLU, MOE_ACT_SRELU, MOE_ACT_SWIGLU, MOE_FMT_MXFP4,  # noqa: F401
-                   MOE_FMT_MXFP8, MOE_GEMM_STREAMED, MOE_GEMM_TILED, MOE_LAYER_SEPARATE_KERNELS,
+                   MOE_FMT_MXFP8, MOE_GEMM_PASS, MOE_GEMM_STREAMED, MOE_GEMM_TILED,
+                   MOE_LAYER_SEPARATE_KERNELS,
                    MOE_LAYER_TOKEN_RING, MOE_ROUTE_RENORM,
                    MOE_SCALE_RULE_CEIL, MOE_W1_WRITE_TRANSPOSE, MOE_WEIGHT_AT_COMBINE,
                    moe_epilogue, moe_layer_args, moe_weights)

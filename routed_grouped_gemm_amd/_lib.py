@@ -15,6 +15,7 @@ MOE_W1_WRITE_TRANSPOSE = 1 << 2
 MOE_SCALE_RULE_CEIL = 1 << 3
 MOE_GEMM_STREAMED = 1 << 8
 MOE_GEMM_TILED = 1 << 9
+MOE_GEMM_PASS = 1 << 12
 MOE_LAYER_SEPARATE_KERNELS = 1 << 10
 MOE_LAYER_TOKEN_RING = 1 << 11
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20

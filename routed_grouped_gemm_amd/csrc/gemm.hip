@@ -328,6 +328,16 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
         return IS_W1 ? moe_launch_tiled_w1(a, stream) : moe_launch_tiled_w2(a, stream);
     }
     KParams p = make_params(a, IS_W1);
+    // groups of 16 or more rows: their weight units are read by several
+    // passes and every unit reads the pass's rows -> the pass-resident
+    // kernel with 32-row passes (measured on the full-expert shape, 16 rows
+    // per group expected: 16-row passes 349 us, 32-row 286 us, 64-row 311
+    // us per layer)
+    if (!a.route && !(a.flags & MOE_GEMM_STREAMED) && ((a.flags & MOE_GEMM_PASS) || avg >= 16)) {
+        int nt = avg >= 16 || p.transpose ? 2 : 1;   // 32-token blocks of the transposed copy: whole passes
+        if (nt == 2 && !p.transpose && !moe_pass_fits(a.K, a.G, 2, a.fmt)) nt = 1;
+        if (moe_pass_fits(a.K, a.G, nt, a.fmt)) return moe_launch_pass(a, IS_W1, nt, stream);
+    }
     int ntt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
     if (p.transpose && ntt < 2) ntt = 2;       // 32-token blocks must not straddle passes
     const int units = a.N / 64;

@@ -33,6 +33,7 @@ struct KParams {
     // >= 0 the token rows come from a ring slot (aq) holding the grouped rows
     // from the first row of pass ring_pass0 on, one after another
     int item_lo, item_hi, ring_pass0;
+    int pass_kc;                      // pass-resident kernel: K-tiles per staged chunk of token rows
     // W1 epilogue variant (act, beta, clamp limit, per-group bias [G][2I],
     // optional BF16 copy of the pre-activation [R_max, 2I]); generic = 0 is
     // SwiGLU with beta = 1 and none of the options

@@ -268,7 +268,8 @@ static int32_t check_grouped_sizes(int R_max, int G, int x_rows, int H, int I, b
 }
 
 static int32_t check_gemm_flags(uint32_t flags) {
-    if ((flags & MOE_GEMM_STREAMED) && (flags & MOE_GEMM_TILED)) return MOE_ERR_UNSUPPORTED;
+    const uint32_t fam = flags & (MOE_GEMM_STREAMED | MOE_GEMM_TILED | MOE_GEMM_PASS);
+    if (fam & (fam - 1)) return MOE_ERR_UNSUPPORTED;            // more than one family forced
     return MOE_OK;
 }
 
@@ -340,7 +341,7 @@ static int32_t prepare_w2(GemmArgs& a, const moe_weights* w2, const moe_weights*
     int32_t st = check_hi(H, I);
     if (st) return st;
     if ((st = check_gemm_flags(flags))) return st;
-    if (flags & ~(MOE_GEMM_STREAMED | MOE_GEMM_TILED)) return MOE_ERR_UNSUPPORTED;
+    if (flags & ~(MOE_GEMM_STREAMED | MOE_GEMM_TILED | MOE_GEMM_PASS)) return MOE_ERR_UNSUPPORTED;
     if ((st = check_grouped_sizes(R_max, G, 1, H, I, false))) return st;
     st = fill_gemm_args(a, w2, w2_shared, G, H, I, 0);
     if (st) return st;
@@ -508,7 +509,7 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
                     scratch_bytes);
     if (st) return st;
     st = prepare_w2(a2, a->w2, a->shared_w2, counts, offsets, hq, hs, R_max, H, I, G,
-                    a->flags & (MOE_GEMM_STREAMED | MOE_GEMM_TILED), y, scratch, scratch_bytes);
+                    a->flags & (MOE_GEMM_STREAMED | MOE_GEMM_TILED | MOE_GEMM_PASS), y, scratch, scratch_bytes);
     if (st) return st;
 
     // expected rows of a routed group under uniform routing; the shared group

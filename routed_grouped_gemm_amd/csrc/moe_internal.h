@@ -84,6 +84,10 @@ int moe_launch_grouped_w2(const GemmArgs& a, hipStream_t stream);
 bool moe_grouped_uses_tiled(const GemmArgs& a);
 // LDS-tiled variants for groups with many rows (256 x 256 workgroup tiles)
 int moe_launch_tiled_w1(const GemmArgs& a, hipStream_t stream);
+// the pass-resident streaming kernel (gemm_pass.hip): whether passes of NT
+// 16-row token tiles fit its staging for this K and G, and the launch
+bool moe_pass_fits(int K, int G, int NT, int fmt);
+int moe_launch_pass(const GemmArgs& a, bool w1, int NT, hipStream_t stream);
 int moe_launch_tiled_w2(const GemmArgs& a, hipStream_t stream);
 // The backward of the fused W1 epilogue on the LDS-tiled kernel: the W2^T
 // GEMM with the dActivation epilogue (outputs in a.hq/hs/hTq/hTs with rows

@@ -138,6 +138,9 @@ def test_grouped_w1_status_paths():
 
     both = _lib.MOE_GEMM_STREAMED | _lib.MOE_GEMM_TILED
     assert call(flags=both) == _lib.MOE_ERR_UNSUPPORTED
+    # any two of the three kernel families
+    assert call(flags=_lib.MOE_GEMM_PASS | _lib.MOE_GEMM_STREAMED) == _lib.MOE_ERR_UNSUPPORTED
+    assert call(flags=_lib.MOE_GEMM_PASS | _lib.MOE_GEMM_TILED) == _lib.MOE_ERR_UNSUPPORTED
     assert call(I=200) == _lib.MOE_ERR_SHAPE                                     # I % 128
     assert call(H=500) == _lib.MOE_ERR_SHAPE                                     # H % 256
     assert call(x_rows=0) == _lib.MOE_ERR_SHAPE
@@ -166,6 +169,7 @@ def test_grouped_w2_status_paths():
                                   ws_bytes, None)
 
     assert call(flags=_lib.MOE_GEMM_STREAMED | _lib.MOE_GEMM_TILED) == _lib.MOE_ERR_UNSUPPORTED
+    assert call(flags=_lib.MOE_GEMM_PASS | _lib.MOE_GEMM_TILED) == _lib.MOE_ERR_UNSUPPORTED
     assert call(flags=_lib.MOE_W1_WRITE_TRANSPOSE) == _lib.MOE_ERR_UNSUPPORTED   # no W1 flags here
     assert call(I=4224) == _lib.MOE_ERR_SHAPE                                    # I > 4096
     assert call(R_max=1 << 23) == _lib.MOE_ERR_SHAPE                             # R_max * I >= 2^31

@@ -60,7 +60,7 @@ VARIANTS = [
 ]
 
 
-@pytest.mark.parametrize("kernel", ["streamed", "tiled"])
+@pytest.mark.parametrize("kernel", ["streamed", "pass", "tiled"])
 @pytest.mark.parametrize("bias", [False, True])
 @pytest.mark.parametrize("name,var", VARIANTS, ids=[v[0] for v in VARIANTS])
 def test_w1_variant_parity(name, var, bias, kernel):
@@ -82,7 +82,7 @@ def test_w1_variant_parity(name, var, bias, kernel):
     pre = torch.zeros((R, 2 * I), dtype=torch.int16, device="cuda").view(torch.uint16)
     e = moe.Epilogue(act=var["act"], beta=var.get("beta", 1.0), limit=var.get("limit", 0.0),
                      bias=None if b is None else dev(b), save_pre=pre)
-    flags = moe.MOE_GEMM_TILED if kernel == "tiled" else moe.MOE_GEMM_STREAMED
+    flags = {"streamed": moe.MOE_GEMM_STREAMED, "pass": moe.MOE_GEMM_PASS, "tiled": moe.MOE_GEMM_TILED}[kernel]
     hq, hs, _, _ = moe.moe_grouped_w1(_packed(w1, fmt, True), dev(np.array(counts, np.int32)), dev(offsets),
                                       dev(row_w), dev(xq), dev(xs), I, flags, epi=e)
     # error bound of the fp32 sums, through bias, clamp and the activation

@@ -161,12 +161,18 @@ W1_CASES = [
     # scratch); ragged tails and an empty group, with the transposed copy
     ([5000, 257, 0, 3100, 2555, 1031], 512, 2048, "e4m3", (1 << 31) | moe.MOE_W1_WRITE_TRANSPOSE),
     ([4100, 6000, 1, 1955], 256, 2048, "e2m1", moe.MOE_SCALE_RULE_CEIL),
+    # a long K (64 K-tiles): the pass-resident kernel stages its token rows in
+    # K-chunks, double-buffered (32- and 64-row passes do not fit whole)
+    ([40, 0, 70, 5, 33], 8192, 256, "e2m1", 1 << 31),
+    ([23, 66, 130], 8192, 128, "e4m3", moe.MOE_W1_WRITE_TRANSPOSE),
 ]
 
-# The kernel family: the weight-streaming kernel (weights streamed once, K
-# split across waves) or the LDS-tiled kernel (256 x 256 workgroup tiles),
-# forced by a flag. Both must give the same answers.
-KERNELS = {"decode": moe.MOE_GEMM_STREAMED, "tiled": moe.MOE_GEMM_TILED}
+# The kernel family, forced by a flag: the weight-streaming kernel (weights
+# streamed once, K split across waves), the pass-resident streaming kernel
+# (a pass of token rows staged once, each weight unit over the whole K by one
+# wave; 32-row passes with the transposed copy) or the LDS-tiled kernel
+# (256 x 256 workgroup tiles). All must give the same answers.
+KERNELS = {"decode": moe.MOE_GEMM_STREAMED, "pass": moe.MOE_GEMM_PASS, "tiled": moe.MOE_GEMM_TILED}
 
 
 @pytest.mark.parametrize("kernel", list(KERNELS))
@@ -243,6 +249,8 @@ W2_CASES = [
     # items per workgroup of the LDS-tiled kernel, ragged tails
     ([5000, 257, 0, 3100, 2555, 1031], 4096, 256, "e4m3"),
     ([4100, 6000, 1, 1955], 4096, 384, "e2m1"),
+    # a long K (I = 4096, 32 K-tiles): K-chunked staging with 64-row passes
+    ([40, 90, 3, 0, 71], 512, 4096, "e2m1"),
 ]
 
 
