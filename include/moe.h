@@ -86,8 +86,8 @@ extern "C" {
 #define MOE_GEMM_STREAMED      (1u << 8)
 #define MOE_GEMM_TILED         (1u << 9)
 #define MOE_GEMM_PASS          (1u << 12)
-/* moe_layer: run the separate kernels (router, grouping, W1, W2, combine)
- * even where the single-launch decode path applies (see moe_layer). */
+/* moe_layer: run W2 and the combine as separate launches even where one
+ * launch does both (at most 16 tokens on few active groups, see moe_layer). */
 #define MOE_LAYER_SEPARATE_KERNELS (1u << 10)
 /* moe_layer, when W1 runs on the LDS-tiled kernel (many rows per group): the
  * token dispatch as a producer on a second stream. The GC-MoE page's role1
@@ -365,16 +365,19 @@ size_t  moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_
                                  int32_t H, int32_t I, int32_t s, uint32_t flags);
 
 /*
- * Run route -> permute -> W1 -> W2 -> combine on `stream`: 3 launches when
- * T <= 8 and groups average under 16 rows (every W1 workgroup routes and
- * groups the tokens itself), 4 when T <= 64 (router and grouping share one
- * workgroup), more otherwise. The grouped token rows are not materialised:
+ * Run route -> permute -> W1 -> W2 -> combine on `stream`. W1 routes and
+ * groups the tokens itself when T <= 8 and groups average under 16 rows
+ * (every W1 workgroup does it), router and grouping share one workgroup when
+ * T <= 64, and W2 and the combine are one launch when T <= 16 and at most
+ * 4 groups are expected to be active (each workgroup owns 32 output columns
+ * of every token: W2 for every active group, then the fp64 slot sum); so 2
+ * launches for a single decode token on a large expert set, up to 5
+ * otherwise. The grouped token rows are not materialised:
  * W1 reads them through row_src. Intermediates live in ws at offsets given
  * by moe_layer_workspace_offsets. Region [12] is the control block of a
  * single-launch decode path (every workgroup routes, W2 work on a group
  * waits for that group's W1 work, the last W2 item of a column block
- * combines it), which is built but switched off in this version: every call
- * takes the separate kernels (MOE_LAYER_SEPARATE_KERNELS changes nothing).
+ * combines it), which is built but switched off in this version.
  */
 int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -113,6 +113,12 @@ int moe_launch_fused_decode(const GemmArgs& a1, const GemmArgs& a2, uint32_t* ct
 
 int moe_launch_combine(const uint16_t* y, const int32_t* slot_row, const float* row_w, int T,
                        int ks, int H, uint16_t* out, hipStream_t stream);
+// W2 and the combine in one launch for at most 16 tokens and few active
+// groups (w2_combine.hip): whether it applies, and the launch (a: the W2
+// arguments; comb_w: the routing weights applied in the combine, or null)
+bool moe_w2_combine_ok(int T, int R_max, int G, int active_hint, uint32_t flags);
+int moe_launch_w2_combine(const GemmArgs& a, const int32_t* slot_row, const float* comb_w, int T, int ks,
+                          uint16_t* out, hipStream_t stream);
 int moe_launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 int moe_launch_quantize(const float* src, int rows, int K, int fmt, uint32_t flags,
                         uint8_t* q, uint8_t* s, hipStream_t stream);

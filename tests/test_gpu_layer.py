@@ -61,6 +61,15 @@ SMALL = [
     ("self-route-shared-wc", dict(T=5, H=1024, I=512, E=32, k=4, e0=8, n_local=12, shared=True),
      moe.MOE_WEIGHT_AT_COMBINE),
     ("self-route-one-token", dict(T=1, E=64, k=8, e0=16, n_local=24), 0),
+    # at most 16 tokens on at most 4 expected active groups (the one-token
+    # case above, single-expert, every-expert): W2 and the combine run as
+    # one launch; 16 tokens over 2 local experts and the shared one fill
+    # whole 16-row tiles in it; the same cases with the separate W2 and
+    # combine launches forced
+    ("w2-combine-full-tiles", dict(T=16, E=2, k=2, n_local=2, shared=True), moe.MOE_WEIGHT_AT_COMBINE),
+    ("w2-combine-full-tiles-separate", dict(T=16, E=2, k=2, n_local=2, shared=True),
+     moe.MOE_WEIGHT_AT_COMBINE | moe.MOE_LAYER_SEPARATE_KERNELS),
+    ("self-route-one-token-separate", dict(T=1, E=64, k=8, e0=16, n_local=24), moe.MOE_LAYER_SEPARATE_KERNELS),
     # degenerate routing: one expert (every weight exactly 1), and k = E
     # (every token picks every expert)
     ("single-expert", dict(T=7, E=1, k=1, n_local=1), 0),
