@@ -208,7 +208,7 @@ MOE_DEV float rows4_sum(float v) {
 // E4M3 codes, into the wave's LDS staging as [feature][token] bytes (tw) and
 // [block][feature] scale bytes (tsw, written by the lanes with r = 0).
 MOE_DEV void transpose_stage(const float (&h)[2][2][4], int jp, uint8_t* tw, uint8_t* tsw, int lane,
-                             bool ceil_rule) {
+                             bool ceil_rule, int stride = kTStride) {
     const int q = lane >> 4, r = lane & 15;
     #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -230,7 +230,7 @@ MOE_DEV void transpose_stage(const float (&h)[2][2][4], int jp, uint8_t* tw, uin
             const uint32_t pk = e4m3x4(sc[jj][0], sc[jj][1], sc[jj][2], sc[jj][3]);
             const uint32_t tr = quad_byte_transpose(pk, lane);
             const int fl = 16 * a + 4 * q + (lane & 3);
-            *(uint32_t*)(tw + fl * kTStride + 16 * (2 * jp + jj) + 4 * ((lane >> 2) & 3)) = tr;
+            *(uint32_t*)(tw + fl * stride + 16 * (2 * jp + jj) + 4 * ((lane >> 2) & 3)) = tr;
         }
     }
 }
@@ -256,6 +256,23 @@ MOE_DEV void transpose_flush(const uint8_t* tw, const uint8_t* tsw, uint8_t* dq,
     for (int b = 0; b < 4; ++b)
         __builtin_amdgcn_raw_buffer_store_b8(tsw[b * 32 + (lane & 31)], rhTs,
                                              (lane < 32 && tok0 + 32 * b < nrows) ? so + b : kInvalid, 0, 0);
+}
+
+// One staged 32-token block (32 features x 32 tokens at row stride
+// kT32Stride, from transpose_stage with jp = 0) -> rows [fbase, fbase + 32)
+// of the transposed copy at columns [col, col + 32), two 16-byte stores per
+// feature row, and its scale bytes at column block col / 32.
+constexpr int kT32Stride = 48;
+MOE_DEV void transpose_flush32(const uint8_t* tw, const uint8_t* tsw, uint8_t* dq, uint8_t* ds, int rows,
+                               int ldT, int fbase, int col, int lane) {
+    const rsrc_t rhT = make_rsrc(dq, (uint32_t)((size_t)rows * ldT));
+    const rsrc_t rhTs = make_rsrc(ds, (uint32_t)((size_t)rows * (ldT / 32)));
+    const int fl = lane >> 1, h = lane & 1;
+    const i32x4 d = *(const i32x4*)(tw + fl * kT32Stride + 16 * h);
+    __builtin_amdgcn_raw_buffer_store_b128(d, rhT, (uint32_t)((fbase + fl) * ldT + col + 16 * h), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8(tsw[lane & 31], rhTs,
+                                         lane < 32 ? (uint32_t)((fbase + lane) * (ldT / 32) + (col >> 5)) : kInvalid,
+                                         0, 0);
 }
 
 // Kernel modes: the epilogue that follows the shared K-loop.
@@ -510,99 +527,145 @@ void tiled_gemm_kernel(KParams p) {
                 const rsrc_t rw_w = make_rsrc(p.row_w + cur.rbase, p.use_w ? (uint32_t)(cur.nrows * 4) : 0u);
                 const rsrc_t rdw = make_rsrc(p.dw_part + (size_t)cur.rbase * units,
                                              p.dw_part ? (uint32_t)(cur.nrows * units * 4) : 0u);
-                float wrow[kBT];
-                #pragma unroll
-                for (int j = 0; j < kBT; ++j)
-                    wrow[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                        rw_w, (uint32_t)((tok0 + 16 * j + r) * 4), 0, 0));
-                #pragma unroll
-                for (int j = 0; j < kBT; ++j) wrow[j] = p.use_w ? wrow[j] : 1.0f;
                 const float lim = p.limit;
-                // dg (half 0) or du (half 1) of weight tiles t0, t0 + 1 for token
-                // tile j: x[tt][v]; returns those 8 features' part of dw
-                auto dact = [&](int j, int t0, int half, float (&x)[2][4]) __attribute__((always_inline)) -> float {
+                // The epilogue walks the token tiles in runtime loops (compiled
+                // once, not unrolled per tile, chunk and activation): the
+                // token tile in hand is always acc[0] (acc[0..1] for a pair),
+                // and the accumulators rotate by one tile per step, so every
+                // index stays a compile-time one. A token tile's
+                // pre-activations (gate and up of the unit's 64 features) and
+                // routing weight are requested one step ahead.
+                // weight tiles [T0, T0 + NTL): BF16 gate / up of features
+                // 64 uu + 16 t + 4 q + [0, 4), and the token's routing weight
+                struct PreAll { u32x2 g[kAT], u[kAT]; float w; };
+                struct PrePair { u32x2 g[2], u[2]; float w; };
+                auto load_pre = [&](int j, int T0, auto& P) {
+                    constexpr int NTL = sizeof(P.g) / sizeof(P.g[0]);
                     const int tok = tok0 + 16 * j + r;
+                    #pragma unroll
+                    for (int i = 0; i < NTL; ++i) {
+                        const uint32_t po = (uint32_t)((tok * L + 64 * uu + 16 * (T0 + i) + 4 * q) * 2);
+                        P.g[i] = __builtin_amdgcn_raw_buffer_load_b64(rpre, po, 0, 0);
+                        P.u[i] = __builtin_amdgcn_raw_buffer_load_b64(rpre, po + (uint32_t)(2 * I), 0, 0);
+                    }
+                    const float wl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw_w, (uint32_t)(tok * 4), 0, 0));
+                    P.w = p.use_w ? wl : 1.0f;
+                };
+                // dg (xg) and du (xu) of one weight tile (entry i of P) for one
+                // token tile's dh; returns the tile's part of the
+                // routing-weight gradient, dh * act(g) * u over its 4 features
+                auto dact_tile = [&](const f32x4& dh, const auto& P, int i, float (&xg)[4], float (&xu)[4]) -> float {
+                    const float gv[4] = {bf16_to_f32(P.g[i].x & 0xFFFFu), bf16_to_f32(P.g[i].x >> 16),
+                                         bf16_to_f32(P.g[i].y & 0xFFFFu), bf16_to_f32(P.g[i].y >> 16)};
+                    const float uv[4] = {bf16_to_f32(P.u[i].x & 0xFFFFu), bf16_to_f32(P.u[i].x >> 16),
+                                         bf16_to_f32(P.u[i].y & 0xFFFFu), bf16_to_f32(P.u[i].y >> 16)};
                     float dwp = 0.f;
                     #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const uint32_t po = (uint32_t)((tok * L + 64 * uu + 16 * (t0 + tt) + 4 * q) * 2);
-                        const u32x2 pg = __builtin_amdgcn_raw_buffer_load_b64(rpre, po, 0, 0);
-                        const u32x2 pu = __builtin_amdgcn_raw_buffer_load_b64(rpre, po + (uint32_t)(2 * I), 0, 0);
-                        const float gv[4] = {bf16_to_f32(pg.x & 0xFFFFu), bf16_to_f32(pg.x >> 16),
-                                             bf16_to_f32(pg.y & 0xFFFFu), bf16_to_f32(pg.y >> 16)};
-                        const float uv[4] = {bf16_to_f32(pu.x & 0xFFFFu), bf16_to_f32(pu.x >> 16),
-                                             bf16_to_f32(pu.y & 0xFFFFu), bf16_to_f32(pu.y >> 16)};
-                        #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            float g = gv[v], u = uv[v], mg = 1.f, mu = 1.f;
-                            if (lim > 0.f) {
-                                mg = fabsf(g) <= lim ? 1.f : 0.f;
-                                mu = fabsf(u) <= lim ? 1.f : 0.f;
-                                g = fminf(fmaxf(g, -lim), lim);
-                                u = fminf(fmaxf(u, -lim), lim);
-                            }
-                            float a, da;
-                            act_and_grad(g, p.act, p.beta, a, da);
-                            const float dh = acc[j][t0 + tt][v];
-                            x[tt][v] = half == 0 ? dh * wrow[j] * u * da * mg : dh * wrow[j] * a * mu;
-                            dwp += dh * a * u;
+                    for (int v = 0; v < 4; ++v) {
+                        float g = gv[v], u = uv[v], mg = 1.f, mu = 1.f;
+                        if (lim > 0.f) {
+                            mg = fabsf(g) <= lim ? 1.f : 0.f;
+                            mu = fabsf(u) <= lim ? 1.f : 0.f;
+                            g = fminf(fmaxf(g, -lim), lim);
+                            u = fminf(fmaxf(u, -lim), lim);
                         }
+                        float a, da;
+                        act_and_grad(g, p.act, p.beta, a, da);
+                        xg[v] = dh[v] * P.w * u * da * mg;
+                        xu[v] = dh[v] * P.w * a * mu;
+                        dwp += dh[v] * a * u;
                     }
                     return dwp;
                 };
-                static_for<kBT>([&](auto jc) {
-                    constexpr int j = decltype(jc)::value;
-                    const int tok = tok0 + 16 * j + r;
-                    float dwp = 0.f;
+                auto rotate = [&](int by) {             // acc[i] <- acc[i + by], cyclically
+                    f32x4 keep[2][kAT];
                     #pragma unroll
-                    for (int half = 0; half < 2; ++half)
+                    for (int i = 0; i < 2; ++i)
                         #pragma unroll
-                        for (int b = 0; b < 2; ++b) {
-                            float x[2][4];
-                            const float part = dact(j, 2 * b, half, x);
-                            if (half == 0) dwp += part;
-                            float amf = 0.f;
+                        for (int t = 0; t < kAT; ++t) keep[i][t] = acc[i][t];
+                    #pragma unroll
+                    for (int i = 0; i < kBT - 2; ++i)
+                        #pragma unroll
+                        for (int t = 0; t < kAT; ++t) acc[i][t] = by == 1 ? acc[i + 1][t] : acc[i + 2][t];
+                    #pragma unroll
+                    for (int t = 0; t < kAT; ++t) {
+                        acc[kBT - 2][t] = by == 1 ? acc[kBT - 1][t] : keep[0][t];
+                        acc[kBT - 1][t] = by == 1 ? keep[0][t] : keep[1][t];
+                    }
+                };
+                // Token tiles in pairs (one 32-token block): dg and du of both
+                // tiles computed once, then their E4M3 rows with scales
+                // (32-feature blocks: tiles 2b, 2b + 1), the dw part, and with
+                // the transposed copy the block's four 32-feature chunks (dg
+                // or du of tiles 2b, 2b + 1), staged in the wave's LDS area
+                // and flushed as 32-byte row pieces.
+                uint8_t* tw4 = scratch + w * (4 * (32 * kT32Stride + 32));
+                const int col0 = p.transpose ? p.offsets32[cur.g] + cur.pass * kRows + tok0 : 0;
+                #pragma nounroll
+                for (int jp = 0; jp < kBT / 2; ++jp) {
+                    PreAll P[2];
+                    load_pre(2 * jp, 0, P[0]);
+                    load_pre(2 * jp + 1, 0, P[1]);
+                    float x[2][2][kAT][4];              // [token tile of the pair][dg, du][weight tile][v]
+                    #pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int tok = tok0 + 16 * (2 * jp + jj) + r;
+                        float dwp = 0.f;
+                        #pragma unroll
+                        for (int t = 0; t < kAT; ++t) dwp += dact_tile(acc[jj][t], P[jj], t, x[jj][0][t], x[jj][1][t]);
+                        #pragma unroll
+                        for (int half = 0; half < 2; ++half)
                             #pragma unroll
-                            for (int tt = 0; tt < 2; ++tt)
+                            for (int b = 0; b < 2; ++b) {
+                                float amf = 0.f;
                                 #pragma unroll
-                                for (int v = 0; v < 4; ++v) amf = fmaxf(amf, fabsf(x[tt][v]));
-                            const uint32_t am = rows4_umax(__float_as_uint(amf));
-                            const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
-                            const float inv = inv_scale(code);
+                                for (int tt = 0; tt < 2; ++tt)
+                                    #pragma unroll
+                                    for (int v = 0; v < 4; ++v) amf = fmaxf(amf, fabsf(x[jj][half][2 * b + tt][v]));
+                                const uint32_t am = rows4_umax(__float_as_uint(amf));
+                                const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
+                                const float inv = inv_scale(code);
+                                #pragma unroll
+                                for (int tt = 0; tt < 2; ++tt) {
+                                    const float* xv = x[jj][half][2 * b + tt];
+                                    __builtin_amdgcn_raw_buffer_store_b32(
+                                        e4m3x4(xv[0] * inv, xv[1] * inv, xv[2] * inv, xv[3] * inv), rdq,
+                                        (uint32_t)(tok * L + half * I + 64 * uu + 16 * (2 * b + tt) + 4 * q), 0, 0);
+                                }
+                                __builtin_amdgcn_raw_buffer_store_b8(
+                                    (unsigned char)code, rds,
+                                    q == 0 ? (uint32_t)(tok * (L / 32) + half * (I / 32) + 2 * uu + b) : kInvalid, 0, 0);
+                            }
+                        // the routing weight's gradient: this unit's 64 features of the token
+                        const float dws = rows4_sum(dwp);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dws), rdw,
+                                                              q == 0 ? (uint32_t)((tok * units + uu) * 4) : kInvalid, 0, 0);
+                    }
+                    // a block that starts past the item's rows belongs to the
+                    // next group's columns: not written
+                    if (p.transpose && tok0 + 32 * jp < cur.nrows) {
+                        #pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int half = c >> 1, b = c & 1;
+                            float h2[2][2][4];
                             #pragma unroll
-                            for (int tt = 0; tt < 2; ++tt)
-                                __builtin_amdgcn_raw_buffer_store_b32(
-                                    e4m3x4(x[tt][0] * inv, x[tt][1] * inv, x[tt][2] * inv, x[tt][3] * inv), rdq,
-                                    (uint32_t)(tok * L + half * I + 64 * uu + 16 * (2 * b + tt) + 4 * q), 0, 0);
-                            __builtin_amdgcn_raw_buffer_store_b8(
-                                (unsigned char)code, rds,
-                                q == 0 ? (uint32_t)(tok * (L / 32) + half * (I / 32) + 2 * uu + b) : kInvalid, 0, 0);
+                            for (int jj = 0; jj < 2; ++jj)
+                                #pragma unroll
+                                for (int tt = 0; tt < 2; ++tt)
+                                    #pragma unroll
+                                    for (int v = 0; v < 4; ++v) h2[jj][tt][v] = x[jj][half][2 * b + tt][v];
+                            uint8_t* twc = tw4 + c * (32 * kT32Stride + 32);
+                            transpose_stage(h2, 0, twc, twc + 32 * kT32Stride, lane, p.ceil_rule, kT32Stride);
                         }
-                    // the routing weight's gradient: this unit's 64 features of the token
-                    const float dws = rows4_sum(dwp);
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dws), rdw,
-                                                          q == 0 ? (uint32_t)((tok * units + uu) * 4) : kInvalid, 0, 0);
-                    // one token tile at a time: its loads are not hoisted above the
-                    // previous tile's work (that would hold all 8 tiles' inputs at once)
-                    __builtin_amdgcn_sched_barrier(0);
-                });
-                if (p.transpose) {
-                    // four 32-feature chunks (dg or du, tiles 2b and 2b + 1),
-                    // each staged and flushed like the forward's transposed copy
-                    const int col0 = p.offsets32[cur.g] + cur.pass * kRows + tok0;
-                    static_for<4>([&](auto cc) {
-                        constexpr int c = decltype(cc)::value, half = c >> 1, b = c & 1;
-                        static_for<kBT / 2>([&](auto jpc) {
-                            constexpr int jp = decltype(jpc)::value;
-                            float x2[2][2][4];
-                            (void)dact(2 * jp, 2 * b, half, x2[0]);
-                            (void)dact(2 * jp + 1, 2 * b, half, x2[1]);
-                            transpose_stage(x2, jp, tw, tsw, lane, p.ceil_rule);
-                            __builtin_amdgcn_sched_barrier(0);
-                        });
-                        transpose_flush(tw, tsw, p.hTq, p.hTs, L, p.ldT, half * I + 64 * uu + 32 * b, col0, tok0,
-                                        cur.nrows, lane);
-                    });
+                        #pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int half = c >> 1, b = c & 1;
+                            const uint8_t* twc = tw4 + c * (32 * kT32Stride + 32);
+                            transpose_flush32(twc, twc + 32 * kT32Stride, p.hTq, p.hTs, L, p.ldT,
+                                              half * I + 64 * uu + 32 * b, col0 + 32 * jp, lane);
+                        }
+                    }
+                    rotate(2);
                 }
             }
             __syncthreads();                 // scratch free before the next prefetch lands in it

@@ -168,7 +168,9 @@ MOE_DEV void act_and_grad(float z, int act, float beta, float& a, float& da) {
         a = r * r;
         da = 2.0f * r;
     } else {
-        const float s = 1.0f / (1.0f + __expf(-beta * z));
+        // the sigmoid with the hardware reciprocal (1 ulp) instead of a full
+        // division; exp overflowing to inf gives s = 0, as the division does
+        const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-beta * z));
         a = z * s;
         da = s + beta * z * s * (1.0f - s);
     }
