@@ -111,12 +111,12 @@ void grouped_gemm_kernel(KParams p) {
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int pg = item / (units * IPU), ui = item - pg * units * IPU;
         const int u = ui / IPU, t0 = (ui - u * IPU) * TPI;     // unit, its first tile of this item
-        int glo = 0, ghi = G;                           // largest g with pass_off[g] <= pg
-        while (ghi - glo > 1) {
-            const int mid = (glo + ghi) >> 1;
-            if (pass_off[mid] <= pg) glo = mid; else ghi = mid;
-        }
-        const int g = glo, pass = pg - pass_off[g];
+        // the largest g with pass_off[g] <= pg: the count of such g, less
+        // one (pass_off is non-decreasing), one ballot per 64 groups
+        int ng = 0;
+        for (int g0 = 0; g0 < G; g0 += 64)
+            ng += __popcll(__ballot(g0 + lane < G && pass_off[g0 + lane] <= pg));
+        const int g = ng - 1, pass = pg - pass_off[g];
         const int n_g = cnt_tab[g];
         const int sel = g < p.E_loc ? 0 : 1;
         const int gi = g < p.E_loc ? g : 0;

@@ -67,12 +67,7 @@ MOE_DEV void pass_prefix(const int32_t* __restrict__ counts, int G, int rpp, int
     const int lo = min(G, lane * per), hi = min(G, lo + per);
     int s = 0;
     for (int i = lo; i < hi; ++i) s += (counts[i] + rpp - 1) / rpp;
-    int inc = s;
-    #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int a = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += a;
-    }
+    const int inc = wave_incl_scan(s);
     int run = inc - s;
     for (int i = lo; i < hi; ++i) {
         pass_off[i] = run;

@@ -257,6 +257,30 @@ MOE_DEV uint32_t rows4_umax(uint32_t v) {
     return max(b[0], b[1]);
 }
 
+// Unsigned max over the 64 lanes of the wave, returned as a scalar: the
+// integer max takes the DPP operand directly (no canonicalising step).
+MOE_DEV uint32_t wave_umax(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_XOR1, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_XOR2, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_HALF_MIRROR, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, MOE_DPP_MIRROR, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, MOE_DPP_BCAST15, 0xA, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, MOE_DPP_BCAST31, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (lanes without a source add 0), no LDS round trips.
+MOE_DEV int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);     // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);     // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);     // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);     // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, MOE_DPP_BCAST15, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, MOE_DPP_BCAST31, 0xC, 0xF, false);
+    return v;
+}
+
 MOE_DEV float row16_sum(float v) {
     v += MOE_DPP(v, MOE_DPP_XOR1, 0xF);
     v += MOE_DPP(v, MOE_DPP_XOR2, 0xF);
@@ -275,6 +299,17 @@ MOE_DEV float row16_sum(float v) {
 // max) in fp32. On return, lane j < k of the group holds the token's j-th
 // selection in (sel_e, sel_w). E <= LPT*VPL, k <= LPT.
 // ---------------------------------------------------------------------------
+// Order-preserving unsigned key of a finite fp32 value: a larger value has a
+// larger key, -0 and +0 share the key of +0, and every key is above 0.
+MOE_DEV uint32_t f32_order_key(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    u = u == 0x80000000u ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+MOE_DEV float order_key_f32(uint32_t k) {
+    return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 template <int LPT>
 MOE_DEV float group_max(float v) { return LPT == 64 ? wave_max(v) : row16_max(v); }
 template <int LPT>
@@ -294,38 +329,42 @@ MOE_DEV void route_values(const float (&v)[VPL], int E, int k, bool renorm, int 
     for (int i = 0; i < VPL; ++i) ls += (base + i < E) ? __expf(v[i] - m) : 0.f;
     const float inv = 1.0f / group_sum<LPT>(ls);
 
-    // Candidate values with taken / out-of-range entries at -inf (logits are
-    // finite, so -inf means "nothing left").
-    float c[VPL];
+    // Candidates as order-preserving unsigned keys of the fp32 logits (-0
+    // folded onto +0, since the two compare equal); 0 marks a taken or
+    // out-of-range entry (logits are finite, so every real key is above it).
+    uint32_t c[VPL];
     #pragma unroll
-    for (int i = 0; i < VPL; ++i) c[i] = (base + i < E) ? v[i] : -INFINITY;
+    for (int i = 0; i < VPL; ++i) c[i] = (base + i < E) ? f32_order_key(v[i]) : 0u;
     const int gshift = LPT == 64 ? 0 : (lane & 48);
-    float wsum = 0.f, my_w = 0.f;
+    uint32_t my_key = 0;
     int my_e = -1;
     for (int j = 0; j < k; ++j) {
-        // lane-local best, branch-free; a strict compare in ascending order
-        // keeps the lower index on ties
-        float bv = c[0];
-        int bi = 0;
+        // the lane's best key, then the group's
+        uint32_t bk = c[0];
         #pragma unroll
-        for (int i = 1; i < VPL; ++i) {
-            const bool better = c[i] > bv;
-            bv = better ? c[i] : bv;
-            bi = better ? i : bi;
-        }
-        const float mx = group_max<LPT>(bv);
-        const uint64_t hit = __ballot(bv == mx && bv != -INFINITY);
+        for (int i = 1; i < VPL; ++i) bk = max(bk, c[i]);
+        const uint32_t mk = LPT == 64 ? wave_umax(bk) : row16_umax(bk);
+        // the lowest lane holding it has the lowest expert id (ties go to
+        // the lower id), and within the lane its first slot
+        const uint64_t hit = __ballot(bk == mk && mk != 0u);
         const uint64_t ghit = LPT == 64 ? hit : ((hit >> gshift) & 0xFFFFull);
         const int win = gshift + (ghit ? __ffsll((unsigned long long)ghit) - 1 : 0);
-        const int e = LPT == 64 ? __builtin_amdgcn_readlane(base + bi, win)
-                                : __shfl(base + bi, win, 64);
+        int fi = VPL - 1;
+        #pragma unroll
+        for (int i = VPL - 2; i >= 0; --i) fi = c[i] == mk ? i : fi;
+        const int e = LPT == 64 ? __builtin_amdgcn_readlane(base + fi, win)
+                                : __shfl(base + fi, win, 64);
         const bool pop = ghit && lane == win;
         #pragma unroll
-        for (int i = 0; i < VPL; ++i) c[i] = (pop && i == bi) ? -INFINITY : c[i];
-        const float w = __expf(mx - m) * inv;
-        wsum += w;
-        if (li == j) { my_e = e; my_w = w; }
+        for (int i = 0; i < VPL; ++i) c[i] = (pop && i == fi) ? 0u : c[i];
+        if (li == j) { my_e = e; my_key = mk; }
     }
+    // weights of the selections, once (the same fp32 expressions as a
+    // per-round computation; the renormalising sum in selection order)
+    const float my_w = li < k ? __expf(order_key_f32(my_key) - m) * inv : 0.f;
+    float wsum = 0.f;
+    if (renorm)
+        for (int j = 0; j < k; ++j) wsum += __shfl(my_w, gshift + j, 64);
     if (li < k) {
         sel_e = my_e;
         sel_w = renorm ? my_w / wsum : my_w;

@@ -29,12 +29,7 @@ MOE_DEV void write_offsets(int* lds_counts, int G, int32_t* counts, int32_t* off
             s += c;
             s32 += (c + 31) & ~31;
         }
-        int inc = s, inc32 = s32;                  // inclusive scan over lanes
-        #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int a = __shfl_up(inc, d, 64), b = __shfl_up(inc32, d, 64);
-            if (lane >= d) { inc += a; inc32 += b; }
-        }
+        const int inc = wave_incl_scan(s), inc32 = wave_incl_scan(s32);   // inclusive scans over lanes
         int run = inc - s, run32 = inc32 - s32;
         for (int i = lo; i < hi; ++i) {
             const int c = lds_counts[i];
@@ -172,12 +167,7 @@ MOE_DEV void permute_in_wave(IdxF idx_of, WF w_of, int T, int k, int e0, int E_l
     }
     // offsets32: exclusive scan over the groups of the 32-rounded counts
     const int c32 = (cnt + 31) & ~31;
-    int inc = c32;
-    #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += y;
-    }
+    const int inc = wave_incl_scan(c32);
     if (q < G) {
         counts[q] = cnt;
         offsets[q] = off;

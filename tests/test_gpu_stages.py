@@ -64,6 +64,9 @@ def test_route_parity(name, T, flags):
     if c.T > 4:
         lg[1, :] = np.float32(0.5)                       # all tied
         lg[2, 5:9] = lg[2, 5:9].max() + 1                # ties at the top
+        lg[3, :] = -1.0                                  # -0 and +0 tie: the lower id first
+        lg[3, 10:20:2] = -0.0
+        lg[3, 11:21:2] = 0.0
     idx_ref, w_ref = omoe.route(lg, c.k, renorm=bool(flags & moe.MOE_ROUTE_RENORM))
     idx, w = moe.moe_route(dev(lg), c.k, flags)
     np.testing.assert_array_equal(host(idx), idx_ref)
