@@ -216,18 +216,21 @@ void grouped_gemm_kernel(KParams p) {
                 }
             }
             __syncthreads();
-            // row-wise MX-E4M3 quantisation: 32 threads per token (one 32-block)
+            // row-wise MX-E4M3 quantisation: 32 threads per token (one 32-block;
+            // the amax over the half wave with DPP and a row swap, the bytes
+            // of a quad gathered with quad broadcasts)
             for (int t0 = 0; t0 < rows_per_pass; t0 += NT / 32) {
                 const int tok = t0 + (tid >> 5), f = tid & 31;
                 const bool valid = tok < nrows;
                 const float h = valid ? hbuf[tok * 33 + f] : 0.f;
-                float amax = fabsf(h);
-                #pragma unroll
-                for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-                const uint32_t code = e4m3_scale_code(amax, p.ceil_rule);
+                uint32_t ab = row16_umax(__float_as_uint(fabsf(h)));
+                const auto sw = __builtin_amdgcn_permlane16_swap(ab, ab, false, false);
+                ab = max(sw[0], sw[1]);
+                const uint32_t code = e4m3_scale_code(__uint_as_float(ab), p.ceil_rule);
                 const uint32_t qb = f32_to_e4m3(h * inv_scale(code));
-                const uint32_t b1 = __shfl_down(qb, 1, 64), b2 = __shfl_down(qb, 2, 64),
-                               b3 = __shfl_down(qb, 3, 64);
+                const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)qb, 0x55, 0xF, 0xF, true);
+                const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)qb, 0xAA, 0xF, 0xF, true);
+                const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)qb, 0xFF, 0xF, 0xF, true);
                 if (valid) {
                     const size_t r = (size_t)(rbase + tok);
                     if ((f & 3) == 0)
