@@ -374,15 +374,16 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     // stream through non-temporally
     const bool reread = ntt > 1 || avg >= rpp;
     const bool fp4 = a.fmt == MOE_FMT_MXFP4;
-    // W2 streaming its weights once, with fewer items than one round of
-    // workgroups takes even at half a unit each: items of half a unit, each
-    // done in about half the time (one token: W2 7.3 -> 6.4 us). With more
-    // items, halves only thin out the weight bytes in flight per CU: at 20
-    // to 30 active experts, where the last round of whole units is partly
-    // idle, they were measured no faster (T = 32) or slower (T = 128).
+    // W2 streaming its weights once, with at most two rounds of workgroups
+    // of whole units: items of half a unit, each done in about half the
+    // time, so that the last round leaves less of the chip idle (one token:
+    // W2 7.3 -> 6.4 us; eight tokens on the decode share, about 840 units:
+    // layer 45.1 -> 43.8 us). With more items, halves only thin out the
+    // weight bytes in flight per CU: at 20 to 30 active experts they were
+    // measured no faster (T = 32) or slower (T = 128).
     if constexpr (!IS_W1) if (ntt == 1 && !reread) {
         const long slots = (long)device_cu_count() * (16 / kw);
-        if (2 * items <= slots)
+        if (items <= 2 * slots)
             return fp4 ? launch_kw<MFMA_FMT_FP4, IS_W1, 1, kNonTemporal, 0, 2>(p, kw, max_items, stream)
                        : launch_kw<MFMA_FMT_FP8, IS_W1, 1, kNonTemporal, 0, 2>(p, kw, max_items, stream);
     }
