@@ -299,12 +299,14 @@ int launch(const KParams& p, long max_items, hipStream_t stream) {
 }
 
 // 16 K-split waves only with one token tile: 1024-thread workgroups get 128
-// VGPRs, too few for more
+// VGPRs, too few for more; 2 only with one token tile as well
 template <int WFMT, bool IS_W1, int NTT, int CP, int RT = 0, int TPI = 4>
 int launch_kw(const KParams& p, int kw, long max_items, hipStream_t stream) {
     if constexpr (NTT == 1 && TPI == 4)
         if (kw >= 16) return launch<WFMT, IS_W1, NTT, 16, CP, RT>(p, max_items, stream);
     if (kw >= 8) return launch<WFMT, IS_W1, NTT, 8, CP, RT, TPI>(p, max_items, stream);
+    if constexpr (NTT == 1)
+        if (kw <= 2) return launch<WFMT, IS_W1, NTT, 2, CP, RT, TPI>(p, max_items, stream);
     return launch<WFMT, IS_W1, NTT, 4, CP, RT, TPI>(p, max_items, stream);
 }
 
@@ -349,25 +351,29 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     const long max_items = (long)units * ((long)a.R_max / rpp + a.G);
     // K-split waves per workgroup. W2 (the shorter K = I, where wider splits
     // cost more in the reduction than they gain): enough waves for two per
-    // SIMD, but never 16 (slower even with a single token). W1 with one
-    // token tile: 16 waves per CU whatever the split, so a round of items
-    // covers cus * 16 / kw of them, each in about 1/kw of the time of a
-    // one-wave item; the split with the fewest kw-weighted rounds leaves the
-    // least of the last, partly idle round (ties: fewer waves).
+    // SIMD, but never 16 (slower even with a single token); with one token
+    // tile and at least 1024 items, 2 (eight small workgroups per CU, so one
+    // item's start and end overlap seven others: T = 32 95.5 -> 94.2 us on
+    // the decode share, same-box A/B). W1 with one token tile: 16 waves per
+    // CU whatever the split, so a round of items covers cus * 16 / kw of
+    // them, each in about 1/kw of the time of a one-wave item; the split with
+    // the fewest kw-weighted rounds leaves the least of the last, partly idle
+    // round (ties: fewer waves; at T = 128 every split ties and 2 is taken:
+    // W1 launch rate 5.48 -> 5.57 TB/s).
     const long active = a.active_hint > 0 ? a.active_hint
                         : std::min<long>(a.G, std::max<long>(1, a.R_max / std::max(avg, 1)));
     const long items = active * units * std::max(1, (avg + rpp - 1) / rpp);
-    int kw = items * 4 >= 2048 ? 4 : (items * 8 >= 2048 || !IS_W1 ? 8 : 16);
+    int kw = !IS_W1 && ntt == 1 && items * 2 >= 2048 ? 2 : (items * 4 >= 2048 ? 4 : (items * 8 >= 2048 || !IS_W1 ? 8 : 16));
     if (IS_W1 && ntt == 1) {
         const long cus = device_cu_count();
         double best = 1e30;
-        for (int c : {4, 8, 16}) {
+        for (int c : {2, 4, 8, 16}) {
             const long slots = cus * (16 / c);
             const double t = (double)((items + slots - 1) / slots) / c;
             if (t < best - 1e-9) { best = t; kw = c; }
         }
     }
-    kw = std::min(kw, std::max(4, p.kt));       // no more waves than K-tiles
+    kw = std::min(kw, std::max(ntt == 1 ? 2 : 4, p.kt));     // no more waves than K-tiles
     if (ntt > 1) kw = std::min(kw, 8);          // 1024-thread workgroups get 128 VGPRs: too few
     // weights stay in L2 (cached loads) when a typical group needs more than
     // one pass, so that its other passes re-read them there; otherwise they
@@ -378,8 +384,9 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     // of whole units: items of half a unit, each done in about half the
     // time, so that the last round leaves less of the chip idle (one token:
     // W2 7.3 -> 6.4 us; eight tokens on the decode share, about 840 units:
-    // layer 45.1 -> 43.8 us). With more items, halves only thin out the
-    // weight bytes in flight per CU: at 20 to 30 active experts they were
+    // layer 45.1 -> 43.8 us). With two-wave workgroups (2048 slots) that
+    // covers up to 4096 items, T = 32 and 128 of the decode share included.
+    // With four-wave workgroups and 20 to 30 active experts, halves had been
     // measured no faster (T = 32) or slower (T = 128).
     if constexpr (!IS_W1) if (ntt == 1 && !reread) {
         const long slots = (long)device_cu_count() * (16 / kw);

@@ -168,6 +168,9 @@ W1_CASES = [
     # K-chunks, double-buffered (32- and 64-row passes do not fit whole)
     ([40, 0, 70, 5, 33], 8192, 256, "e2m1", 1 << 31),
     ([23, 66, 130], 8192, 128, "e4m3", moe.MOE_W1_WRITE_TRANSPOSE),
+    # 32 active groups x 64 units (I = 2048): 2048 work items, where every
+    # K split ties and the decode kernel takes two waves per workgroup
+    ([(7 * g) % 16 + 1 for g in range(32)], 1024, 2048, "e2m1", 1 << 31),
 ]
 
 # The kernel family, forced by a flag: the weight-streaming kernel (weights
@@ -246,8 +249,12 @@ W2_CASES = [
     ([200], 768, 384, "e2m1"),
     ([0, 1, 255, 256, 257, 600, 33], 512, 256, "e4m3"),
     ([300, 17, 513], 1024, 512, "e2m1"),
-    # enough items (9 groups x 64 units) that the decode kernel keeps whole units
+    # 9 groups x 64 units: four waves per workgroup, half units
     ([5, 1, 0, 20, 3, 7, 2, 16, 40], 4096, 256, "e4m3"),
+    # 32 groups x 32 units: two waves per workgroup, half units
+    ([(5 * g) % 9 + 1 for g in range(32)], 2048, 1024, "e2m1"),
+    # 80 groups x 64 units: two waves per workgroup, whole units
+    ([(3 * g) % 7 + 1 for g in range(80)], 4096, 256, "e4m3"),
     # 16 weight tiles (H = 4096) x about 50 row passes: three or four work
     # items per workgroup of the LDS-tiled kernel, ragged tails
     ([5000, 257, 0, 3100, 2555, 1031], 4096, 256, "e4m3"),
