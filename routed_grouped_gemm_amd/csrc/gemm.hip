@@ -358,8 +358,8 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     // CU whatever the split, so a round of items covers cus * 16 / kw of
     // them, each in about 1/kw of the time of a one-wave item; the split with
     // the fewest kw-weighted rounds leaves the least of the last, partly idle
-    // round (ties: fewer waves; at T = 128 every split ties and 2 is taken:
-    // W1 launch rate 5.48 -> 5.57 TB/s).
+    // round (ties: fewer waves), but from four items per CU on two waves
+    // (T = 32 and 128: W1 launch rate 5.48 -> 5.63 TB/s).
     const long active = a.active_hint > 0 ? a.active_hint
                         : std::min<long>(a.G, std::max<long>(1, a.R_max / std::max(avg, 1)));
     const long items = active * units * std::max(1, (avg + rpp - 1) / rpp);
@@ -372,6 +372,9 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
             const double t = (double)((items + slots - 1) / slots) / c;
             if (t < best - 1e-9) { best = t; kw = c; }
         }
+        // from four items per CU on, two-wave workgroups, whatever the
+        // rounds say (T = 32 of the decode share: 94.6 -> 93.9 us)
+        if (items >= 4 * cus) kw = 2;
     }
     kw = std::min(kw, std::max(ntt == 1 ? 2 : 4, p.kt));     // no more waves than K-tiles
     if (ntt > 1) kw = std::min(kw, 8);          // 1024-thread workgroups get 128 VGPRs: too few
