@@ -383,17 +383,19 @@ int launch_grouped(const GemmArgs& a, hipStream_t stream) {
     // stream through non-temporally
     const bool reread = ntt > 1 || avg >= rpp;
     const bool fp4 = a.fmt == MOE_FMT_MXFP4;
-    // W2 streaming its weights once, with at most two rounds of workgroups
-    // of whole units: items of half a unit, each done in about half the
-    // time, so that the last round leaves less of the chip idle (one token:
-    // W2 7.3 -> 6.4 us; eight tokens on the decode share, about 840 units:
-    // layer 45.1 -> 43.8 us). With two-wave workgroups (2048 slots) that
-    // covers up to 4096 items, T = 32 and 128 of the decode share included.
-    // With four-wave workgroups and 20 to 30 active experts, halves had been
-    // measured no faster (T = 32) or slower (T = 128).
+    // W2 streaming its weights once: items of half a unit, each done in
+    // about half the time, when whole units would not fill one round of
+    // workgroups or when the halves' rounds take less time than the whole
+    // units' rounds, so that the last round leaves less of the chip idle.
+    // Measured on the decode share (same-box A/B): one token, W2 7.3 -> 6.4
+    // us; eight tokens (about 840 units), layer 45.1 -> 43.8 us; T = 32
+    // (2285 units on two-wave workgroups, 2048 slots: 1.5 rounds of halves
+    // against 2 of whole units) halves faster; T = 128 (3528 units, 2 rounds
+    // either way) whole units 1.0 us faster.
     if constexpr (!IS_W1) if (ntt == 1 && !reread) {
         const long slots = (long)device_cu_count() * (16 / kw);
-        if (items <= 2 * slots)
+        const long r_whole = (items + slots - 1) / slots, r_half = (2 * items + slots - 1) / slots;
+        if (items <= slots || r_half < 2 * r_whole)
             return fp4 ? launch_kw<MFMA_FMT_FP4, IS_W1, 1, kNonTemporal, 0, 2>(p, kw, max_items, stream)
                        : launch_kw<MFMA_FMT_FP8, IS_W1, 1, kNonTemporal, 0, 2>(p, kw, max_items, stream);
     }
