@@ -366,7 +366,7 @@ size_t  moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_
 
 /*
  * Run route -> permute -> W1 -> W2 -> combine on `stream`. W1 routes and
- * groups the tokens itself when T <= 8 and groups average under 16 rows
+ * groups the tokens itself when T <= 16 and groups average under 16 rows
  * (every W1 workgroup does it), router and grouping share one workgroup when
  * T <= 64, and W2 and the combine are one launch when T <= 16 and at most
  * 4 groups are expected to be active (each workgroup owns 32 output columns

@@ -313,7 +313,9 @@ int launch_kw(const KParams& p, int kw, long max_items, hipStream_t stream) {
 constexpr int kTiledMinRows = 96;   // expected rows per group from which the tiled kernel runs
 // tokens a W1 launch routes itself, at most: every workgroup routes all of
 // them, so the saving of a launch turns into a loss from about 32 tokens on
-constexpr int kRouteMaxT = 8;
+// (measured on the decode share: 12 tokens 58.3 -> 56.5 us, 16 tokens
+// unchanged; 16 tokens of the 8-expert case 16.3 -> 15.5 us)
+constexpr int kRouteMaxT = 16;
 
 // expected rows per group, as the launch sees them
 inline int expected_rows(int rows_hint, int R_max, int G) { return rows_hint > 0 ? rows_hint : R_max / G; }
@@ -433,7 +435,7 @@ bool moe_grouped_uses_tiled(const GemmArgs& a) {
 
 // The conditions under which launch_grouped<true> takes the one-token-tile,
 // non-temporal path, plus the limits of the in-workgroup routing (at most
-// 256 experts, k <= 16, T <= 8 tokens, at most 513 groups).
+// 256 experts, k <= 16, T <= 16 tokens, at most 513 groups).
 bool moe_w1_can_route(int T, int E_tot, int k, int E_loc, int s, int R_max, int H, int I,
                       int rows_hint, uint32_t flags) {
     (void)H; (void)I;
