@@ -269,7 +269,10 @@ MOE_DEV void transpose_flush32(const uint8_t* tw, const uint8_t* tsw, uint8_t* d
     const rsrc_t rhTs = make_rsrc(ds, (uint32_t)((size_t)rows * (ldT / 32)));
     const int fl = lane >> 1, h = lane & 1;
     const i32x4 d = *(const i32x4*)(tw + fl * kT32Stride + 16 * h);
-    __builtin_amdgcn_raw_buffer_store_b128(d, rhT, (uint32_t)((fbase + fl) * ldT + col + 16 * h), 0, 0);
+    // non-temporal: these 32-byte pieces of 32 rows are not kept in L2
+    // (backward 1319-1352 -> 1263-1292 us; the same hint on the row-major
+    // stores of either epilogue was slower)
+    __builtin_amdgcn_raw_buffer_store_b128(d, rhT, (uint32_t)((fbase + fl) * ldT + col + 16 * h), 0, 2);
     __builtin_amdgcn_raw_buffer_store_b8(tsw[lane & 31], rhTs,
                                          lane < 32 ? (uint32_t)((fbase + lane) * (ldT / 32) + (col >> 5)) : kInvalid,
                                          0, 0);
