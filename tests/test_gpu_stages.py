@@ -259,6 +259,9 @@ W2_CASES = [
     # items per workgroup of the LDS-tiled kernel, ragged tails
     ([5000, 257, 0, 3100, 2555, 1031], 4096, 256, "e4m3"),
     ([4100, 6000, 1, 1955], 4096, 384, "e2m1"),
+    # one K-tile (I = 128) and several items per workgroup: no weight tiles
+    # requested ahead, every step an item's last
+    ([5000, 257, 0, 3100, 2555, 1031], 4096, 128, "e2m1"),
     # a long K (I = 4096, 32 K-tiles): K-chunked staging with 64-row passes
     ([40, 90, 3, 0, 71], 512, 4096, "e2m1"),
 ]
