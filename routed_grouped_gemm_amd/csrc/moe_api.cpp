@@ -559,9 +559,9 @@ MOE_EXPORT int32_t moe_layer(const moe_layer_args* a, void* ws, size_t ws_bytes,
         if (e) return MOE_ERR_HIP;
     } else if ((e = moe_launch_grouped_w1(a1, stream))) return MOE_ERR_HIP;
     const bool wc = (a->flags & MOE_WEIGHT_AT_COMBINE) != 0;
-    // at most 16 tokens on at most 4 active groups: W2 and the combine in
-    // one launch (column ownership)
-    if (moe_w2_combine_ok(T, R_max, G, active, a->flags))
+    // at most 16 tokens on few active groups: W2 and the combine in one
+    // launch (column ownership)
+    if (moe_w2_combine_ok(T, R_max, G, H, I, active, a->flags))
         return hip_status(moe_launch_w2_combine(a2, slot_row, wc ? row_w : nullptr, T, k + s, a->out, stream));
     if ((e = moe_launch_grouped_w2(a2, stream))) return MOE_ERR_HIP;
     e = moe_launch_combine(y, slot_row, wc ? row_w : nullptr, T, k + s, H, a->out, stream);

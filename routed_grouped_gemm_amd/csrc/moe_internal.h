@@ -116,7 +116,7 @@ int moe_launch_combine(const uint16_t* y, const int32_t* slot_row, const float* 
 // W2 and the combine in one launch for at most 16 tokens and few active
 // groups (w2_combine.hip): whether it applies, and the launch (a: the W2
 // arguments; comb_w: the routing weights applied in the combine, or null)
-bool moe_w2_combine_ok(int T, int R_max, int G, int active_hint, uint32_t flags);
+bool moe_w2_combine_ok(int T, int R_max, int G, int H, int I, int active_hint, uint32_t flags);
 int moe_launch_w2_combine(const GemmArgs& a, const int32_t* slot_row, const float* comb_w, int T, int ks,
                           uint16_t* out, hipStream_t stream);
 int moe_launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -151,15 +151,19 @@ void w2_combine_kernel(KParams p, const int32_t* __restrict__ slot_row, const fl
 }  // namespace
 
 // Whether moe_layer's W2 and combine run as one launch: at most 16 tokens
-// (so at most 16 rows per group), at most 4 active groups expected, the
-// grouped rows staged within the LDS, and no kernel family or separate
-// launches forced. Each workgroup streams its 32 columns of every active
+// (so at most 16 rows per group), the grouped rows staged within the LDS,
+// no kernel family or separate launches forced, and either at most 4 active
+// groups expected or at most 8 whose W2 weights are small (active * H * I at
+// most 2^24 elements). Each workgroup streams its 32 columns of every active
 // group's weights plus all their h rows, on H / 32 workgroups, so the cost
-// grows with the active groups: on the decode share (H = 7168) one token
-// (0.8 active experts) took 3-5 us against 10.3 us for W2 and the combine,
-// eight tokens (7.5 active) 21-28 us against 18.9 us.
-bool moe_w2_combine_ok(int T, int R_max, int G, int active_hint, uint32_t flags) {
-    if (T < 1 || T > 16 || R_max > 1024 || G > 4096 || active_hint > 4) return false;
+// grows with the active groups' weights: on the decode share (H = 7168,
+// I = 2048) one token (0.8 active experts) took 3-5 us against 10.3 us for
+// W2 and the combine, eight tokens (7.5 active) 2.8 us more per layer; the
+// 16-token, 8-expert case (H = 512, I = 256, all 8 active) 14.3 against
+// 15.4 us per layer (same-box A/B).
+bool moe_w2_combine_ok(int T, int R_max, int G, int H, int I, int active_hint, uint32_t flags) {
+    if (T < 1 || T > 16 || R_max > 1024 || G > 4096) return false;
+    if (active_hint > 8 || (active_hint > 4 && (int64_t)active_hint * H * I > ((int64_t)1 << 24))) return false;
     return !(flags & (MOE_LAYER_SEPARATE_KERNELS | MOE_GEMM_STREAMED | MOE_GEMM_TILED | MOE_GEMM_PASS));
 }
 
