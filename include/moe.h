@@ -369,8 +369,9 @@ size_t  moe_layer_workspace_size(int32_t T, int32_t E_tot, int32_t k, int32_t E_
  * groups the tokens itself when T <= 16 and groups average under 16 rows
  * (every W1 workgroup does it), router and grouping share one workgroup when
  * T <= 64, and W2 and the combine are one launch when T <= 16 and at most
- * 4 groups are expected to be active (each workgroup owns 32 output columns
- * of every token: W2 for every active group, then the fp64 slot sum); so 2
+ * 4 groups are expected to be active, or at most 8 whose W2 weights total at
+ * most 2^24 elements (each workgroup owns 32 output columns of every token:
+ * W2 for every active group, then the fp64 slot sum); so 2
  * launches for a single decode token on a large expert set, up to 5
  * otherwise. The grouped token rows are not materialised:
  * W1 reads them through row_src. Intermediates live in ws at offsets given
