@@ -245,12 +245,27 @@ def measured_traffic():
         return None
 
 
-def other_workloads(torch, moe, synth, device, names, reps=4):
+def pct(xs, q):
+    """The q-quantile of the sorted list xs (nearest rank)."""
+    return xs[min(len(xs) - 1, max(0, round(q * (len(xs) - 1))))]
+
+
+def spread(each):
+    """min / median / max and p10 / median / p90 of per-replay latencies (us)."""
+    each = sorted(each)
+    return {"latency_us_min_median_max": [round(each[0], 2), round(pct(each, 0.5), 2), round(each[-1], 2)],
+            "latency_us_p10_median_p90": [round(pct(each, 0.1), 2), round(pct(each, 0.5), 2),
+                                          round(pct(each, 0.9), 2)]}
+
+
+def other_workloads(torch, moe, synth, device, names, reps=10):
     """Layer latency of the other workloads (one GPU, graph replay, HIP events
     on the replay stream): the tiny case, the full-expert case, the 16K-token
     prefill case (MXFP8 weights, transposed copy of h) and the decode share
     at T = 32 with a shared expert. Each call alternates between two routing
     draws and two weight copies, so weights stream from HBM as in a model.
+    `reps` back-to-back replays, each between its own pair of events: the
+    mean over all of them, and the spread of the per-replay means.
     Algorithmic bytes and FLOPs as for the decode bench; roofline: HBM for
     the bandwidth-bound shapes, dense FP8 MFMA for prefill."""
     out = {}
@@ -294,13 +309,14 @@ def other_workloads(torch, moe, synth, device, names, reps=4):
         g.replay()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
             g.replay()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (4 * reps)
+        us = ev[0].elapsed_time(ev[reps]) * 1e3 / (4 * reps)
+        each = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / 4 for i in range(reps)]
         fp4 = c.w_fmt == "e2m1"
         bw = 0.5 if fp4 else 1.0
         nbytes, flops = 0.0, 0.0
@@ -315,8 +331,8 @@ def other_workloads(torch, moe, synth, device, names, reps=4):
         frac = tflops / MFMA_FP8_PEAK_TFLOPS if bound == "mfma" else tbps * 1e3 / HBM_PEAK_GBS
         out[name] = {"T": c.T, "H": c.H, "I": c.I, "E": c.E, "k": c.k, "local": c.n_local,
                      "shared": bool(c.shared), "weights": "MXFP4" if fp4 else "MXFP8",
-                     "latency_us": round(us, 2), "TBps": round(tbps, 3), "TFLOPs": round(tflops, 1),
-                     "bound": bound, "roofline_frac": round(frac, 4),
+                     "latency_us": round(us, 2), **spread(each), "TBps": round(tbps, 3),
+                     "TFLOPs": round(tflops, 1), "bound": bound, "roofline_frac": round(frac, 4),
                      "active_groups": [a for a, _ in stats], "rows": [R for _, R in stats]}
         log(f"{name}: {out[name]}")
         del dw, copies, w1, w2, ws, hT, res, g
@@ -324,14 +340,15 @@ def other_workloads(torch, moe, synth, device, names, reps=4):
     return out
 
 
-def backward_workload(torch, moe, synth, device, reps=4):
+def backward_workload(torch, moe, synth, device, reps=8):
     """The backward of the fused W1 epilogue at the 16K-token prefill shape:
     the forward layer runs once with the BF16 pre-activation saved, then the
     backward (dh = dy . W2^T on MFMA, the SwiGLU derivative with the routing
     weight, MX-E4M3 rows and 32-row transposed blocks of [dg | du], dw) on
     that grouping, with W2^T quantised along H and prepacked, and dy a seeded
-    N(0, 1) gradient quantised to MXFP8. Timed with HIP events around `reps`
-    back-to-back calls after one untimed call; FLOPs 2 R H I."""
+    N(0, 1) gradient quantised to MXFP8. Timed with HIP events between
+    `reps` back-to-back calls after one untimed call (the mean, and the
+    spread of the single calls); FLOPs 2 R H I."""
     import numpy as np
     c = synth.config("prefill")
     fmt = moe.MOE_FMT_MXFP8
@@ -360,16 +377,19 @@ def backward_workload(torch, moe, synth, device, reps=4):
     call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    keep = [call() for _ in range(reps)]
-    e1.record(stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    keep = []
+    for i in range(reps):
+        keep.append(call())
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     del keep
-    us = e0.elapsed_time(e1) * 1e3 / reps
+    us = ev[0].elapsed_time(ev[reps]) * 1e3 / reps
+    each = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]
     flops = 2.0 * R * c.H * c.I
     res = {"T": c.T, "H": c.H, "I": c.I, "E": c.E, "k": c.k, "rows": R, "weights": "MXFP8 (W2 transposed)",
-           "latency_us": round(us, 2), "TFLOPs": round(flops / us / 1e6, 1), "bound": "mfma",
+           "latency_us": round(us, 2), **spread(each), "TFLOPs": round(flops / us / 1e6, 1), "bound": "mfma",
            "roofline_frac": round(flops / us / 1e6 / MFMA_FP8_PEAK_TFLOPS, 4),
            "work": "dh = dy . W2^T, SwiGLU derivative, MX-E4M3 rows + 32-row transposed blocks, dw"}
     log(f"prefill_backward: {res}")
@@ -519,9 +539,6 @@ def main():
         each = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 / N_VARIANTS for i in range(reps))
         return us, each
 
-    def pct(xs, q):
-        return xs[min(len(xs) - 1, max(0, round(q * (len(xs) - 1))))]
-
     per_t = {}
     for T in DECODE_T:
         # 20 replays: min / p10 / median / p90 / max of the per-replay means
@@ -530,11 +547,7 @@ def main():
         # warm cache, labelled as such: every call on the same weight copy, so
         # the weights of the smaller T stay in the 256 MB MALL between calls
         wus, _ = graph_latency(T, copies[:1], 4)
-        per_t[str(T)] = {"latency_us": round(us, 2), "TBps": round(b / us / 1e6, 3),
-                         "latency_us_min_median_max": [round(each[0], 2), round(pct(each, 0.5), 2),
-                                                       round(each[-1], 2)],
-                         "latency_us_p10_median_p90": [round(pct(each, 0.1), 2), round(pct(each, 0.5), 2),
-                                                       round(pct(each, 0.9), 2)],
+        per_t[str(T)] = {"latency_us": round(us, 2), "TBps": round(b / us / 1e6, 3), **spread(each),
                          "warm_cache_latency_us": round(wus, 2),
                          "active_experts": round(sum(active[T, v] for v in range(N_VARIANTS)) / N_VARIANTS, 2)}
 
