@@ -488,6 +488,26 @@ def main():
     warm_graph = capture(0, args.warmup) if args.warmup > 0 else None
     timed_graph = capture(args.warmup, args.steps)
     torch.cuda.synchronize()
+    # The measured HBM read rate: the library's plain streaming read of 2 GiB
+    # (one pass per launch), 20 launches between HIP events. It runs here,
+    # after the host-side graph captures (during which the GPU idles) and
+    # right before the warm-up steps, so that the timed steps start on a GPU
+    # that has been busy for several milliseconds (with 5 warm-up steps the
+    # step rate was still rising over the first 20-60 steps otherwise).
+    stream = torch.cuda.current_stream()
+    nb = 1 << 31
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(moe.MOE_HBM_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        moe.moe_hbm_read_probe(buf, sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(20):
+        moe.moe_hbm_read_probe(buf, sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    read_tbps = nb * 20 / (a.elapsed_time(b) * 1e-3) / 1e12
+    del buf, sink
     if warm_graph is not None:
         warm_graph.replay()
     torch.cuda.synchronize()
@@ -603,21 +623,6 @@ def main():
                 "avg_launch_us": round(w1_ms * 1e3 / nlaunch, 2), "launches": nlaunch,
                 "bytes_per_launch": round(w1_b / nlaunch)}
 
-    # the measured HBM read rate: the library's plain streaming read of 2 GiB
-    # (one pass per launch), 20 launches between HIP events on their stream
-    nb = 1 << 31
-    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    sink = torch.empty(moe.MOE_HBM_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
-    for _ in range(3):
-        moe.moe_hbm_read_probe(buf, sink)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(20):
-        moe.moe_hbm_read_probe(buf, sink)
-    b.record(stream)
-    torch.cuda.synchronize()
-    read_tbps = nb * 20 / (a.elapsed_time(b) * 1e-3) / 1e12
-    del buf, sink
     hbm_read = {"kernel": "hbm_read_kernel: one streaming read of 2 GiB per launch",
                 "TBps": round(read_tbps, 3), "frac_of_peak": round(read_tbps * 1e3 / HBM_PEAK_GBS, 4),
                 "value_over_measured": round(value / read_tbps, 4),
