@@ -289,9 +289,29 @@ MOE_DEV float row16_sum(float v) {
     return v;
 }
 
+// Reductions over a half wave (lanes 32h .. 32h+31); every lane of the half
+// receives the result. The float forms take the other row through a lane
+// exchange (both lanes of a pair add the same two values, and fp32 addition
+// is commutative, so both get the same bits); the integer max, used in every
+// selection round, through a row swap.
+MOE_DEV float row32_max(float v) {
+    v = row16_max(v);
+    return fmaxf(v, __shfl_xor(v, 16, 64));
+}
+MOE_DEV float row32_sum(float v) {
+    v = row16_sum(v);
+    return v + __shfl_xor(v, 16, 64);
+}
+MOE_DEV uint32_t row32_umax(uint32_t v) {
+    v = row16_umax(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return max(a[0], a[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Top-k softmax routing with LPT lanes per token (LPT = 64: one token per
-// wave; LPT = 16: one token per DPP row, four tokens per wave). Lane i of a
+// wave; 32: two tokens per wave; 16: one token per DPP row, four tokens per
+// wave). Lane i of a
 // token's lane group holds experts [i*VPL, i*VPL + VPL), so among lanes whose
 // best remaining logit equals the group maximum, the lowest lane holds the
 // lowest expert id: ties resolve to the lower id. Selection compares fp32
@@ -311,9 +331,11 @@ MOE_DEV float order_key_f32(uint32_t k) {
 }
 
 template <int LPT>
-MOE_DEV float group_max(float v) { return LPT == 64 ? wave_max(v) : row16_max(v); }
+MOE_DEV float group_max(float v) { return LPT == 64 ? wave_max(v) : (LPT == 32 ? row32_max(v) : row16_max(v)); }
 template <int LPT>
-MOE_DEV float group_sum(float v) { return LPT == 64 ? wave_sum(v) : row16_sum(v); }
+MOE_DEV float group_sum(float v) { return LPT == 64 ? wave_sum(v) : (LPT == 32 ? row32_sum(v) : row16_sum(v)); }
+template <int LPT>
+MOE_DEV uint32_t group_umax(uint32_t v) { return LPT == 64 ? wave_umax(v) : (LPT == 32 ? row32_umax(v) : row16_umax(v)); }
 
 template <int LPT, int VPL>
 MOE_DEV void route_values(const float (&v)[VPL], int E, int k, bool renorm, int lane,
@@ -335,7 +357,7 @@ MOE_DEV void route_values(const float (&v)[VPL], int E, int k, bool renorm, int 
     uint32_t c[VPL];
     #pragma unroll
     for (int i = 0; i < VPL; ++i) c[i] = (base + i < E) ? f32_order_key(v[i]) : 0u;
-    const int gshift = LPT == 64 ? 0 : (lane & 48);
+    const int gshift = lane & (64 - LPT);           // the group's first lane
     uint32_t my_key = 0;
     int my_e = -1;
     for (int j = 0; j < k; ++j) {
@@ -343,11 +365,11 @@ MOE_DEV void route_values(const float (&v)[VPL], int E, int k, bool renorm, int 
         uint32_t bk = c[0];
         #pragma unroll
         for (int i = 1; i < VPL; ++i) bk = max(bk, c[i]);
-        const uint32_t mk = LPT == 64 ? wave_umax(bk) : row16_umax(bk);
+        const uint32_t mk = group_umax<LPT>(bk);
         // the lowest lane holding it has the lowest expert id (ties go to
         // the lower id), and within the lane its first slot
         const uint64_t hit = __ballot(bk == mk && mk != 0u);
-        const uint64_t ghit = LPT == 64 ? hit : ((hit >> gshift) & 0xFFFFull);
+        const uint64_t ghit = LPT == 64 ? hit : ((hit >> gshift) & ((1ull << LPT) - 1));
         const int win = gshift + (ghit ? __ffsll((unsigned long long)ghit) - 1 : 0);
         int fi = VPL - 1;
         #pragma unroll

@@ -1,4 +1,5 @@
-// S1: top-k softmax router. One wave64 per token.
+// S1: top-k softmax router: 32 lanes per token (two tokens per wave) up to
+// 256 experts and top-16, a whole wave per token beyond.
 //
 // Selection compares the fp32 logits (ties to the lower expert id), so the
 // chosen experts do not depend on how exp() is evaluated; the weights are the
@@ -45,19 +46,19 @@ int moe_launch_route(const float* logits, int T, int E, int k, uint32_t flags,
     if (T == 0) return 0;
     const int renorm = (flags & MOE_ROUTE_RENORM) ? 1 : 0;
     const dim3 block(64 * kWavesPerBlock);
-    if (E <= 256 && k <= 16) {                       // four tokens per wave
-        const dim3 grid((T + 4 * kWavesPerBlock - 1) / (4 * kWavesPerBlock));
-        const int vpl = (E + 15) / 16;
-#define MOE_ROUTE16_CASE(N)                                                                     \
+    if (E <= 256 && k <= 16) {                       // two tokens per wave, 32 lanes each
+        const dim3 grid((T + 2 * kWavesPerBlock - 1) / (2 * kWavesPerBlock));
+        const int vpl = (E + 31) / 32;
+#define MOE_ROUTE32_CASE(N)                                                                     \
         if (vpl <= N) {                                                                         \
-            hipLaunchKernelGGL((route_kernel<16, N>), grid, block, 0, stream, logits, T, E, k,  \
+            hipLaunchKernelGGL((route_kernel<32, N>), grid, block, 0, stream, logits, T, E, k,  \
                                renorm, topk_idx, topk_w);                                       \
             return (int)hipGetLastError();                                                      \
         }
-        MOE_ROUTE16_CASE(4)
-        MOE_ROUTE16_CASE(8)
-        MOE_ROUTE16_CASE(16)
-#undef MOE_ROUTE16_CASE
+        MOE_ROUTE32_CASE(2)
+        MOE_ROUTE32_CASE(4)
+        MOE_ROUTE32_CASE(8)
+#undef MOE_ROUTE32_CASE
     }
     const dim3 grid((T + kWavesPerBlock - 1) / kWavesPerBlock);
     const int vpl = (E + 63) / 64;
