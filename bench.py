@@ -24,7 +24,7 @@ the kernel sources differ from those the counters were taken with);
 "hbm_read_measured" is the HBM read rate of a plain streaming read (the
 library's read probe over 2 GiB), with the step value and the W1 rate as
 fractions of it; "cpu_baseline" times the CPU oracle on
-a bounded sample (the T=8 call of one routing draw). "other_workloads"
+a bounded sample (the step's calls at T = 1, 8 and 32 of one routing draw). "other_workloads"
 gives the layer latency, TB/s, TFLOP/s and roofline fraction of the tiny,
 full-expert, 16K-token prefill and shared-expert workloads (graph replay),
 each with the oracle timed on a token sample of the same workload
@@ -71,9 +71,12 @@ def w1_bytes(R: int, H: int, I: int, active: int, fp4: bool) -> int:
     return active * wb + R * (H + H // 32) + 4 * R + R * (I + I // 32)
 
 
-def cpu_baseline(c8, moe_bytes_fn):
-    """Time the oracle on one T=8 call (routing draw 0); weights of the experts
-    that call touches are quantised by the oracle beforehand (untimed)."""
+def cpu_baseline(cfgs, moe_bytes_fn, Ts=(1, 8, 32)):
+    """Time the oracle on the step's layer calls at T in Ts (routing draw 0),
+    three of the step's four calls (T = 128 alone takes longer than the
+    three together); the weights of the experts those calls touch are
+    quantised by the oracle beforehand (untimed). Returns the calls' bytes
+    over their summed wall time."""
     import numpy as np
     from oracle import moe as omoe, mx
     import synth
@@ -82,22 +85,30 @@ def cpu_baseline(c8, moe_bytes_fn):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    lg = synth.logits(c8, 0)
-    xq, xs = mx.quantize_mx(synth.x(c8, 0), mx.FMT_E4M3)
-    idx, _ = omoe.route(lg, c8.k)
-    active = sorted({int(e) - c8.e0 for e in idx.ravel() if 0 <= int(e) - c8.e0 < c8.n_local})
-    w1q, w1s, w2q, w2s = [None] * c8.n_local, [None] * c8.n_local, [None] * c8.n_local, [None] * c8.n_local
-    for g in active:
-        w1q[g], w1s[g] = mx.quantize_mx(synth.w1(c8, g), c8.w_fmt)
-        w2q[g], w2s[g] = mx.quantize_mx(synth.w2(c8, g), c8.w_fmt)
-    t0 = time.perf_counter()
-    omoe.moe_layer(lg, xq, xs, c8.k, w1q, w1s, w2q, w2s, c8.w_fmt, c8.I, e0=c8.e0, n_local=c8.n_local)
-    dt = time.perf_counter() - t0
-    nbytes = moe_bytes_fn(c8.T, len(active))
-    return {"value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one layer call at T=8 (routing draw 0, {len(active)} active experts), "
-                      f"{dt:.2f} s wall on the host CPU, fp64 NumPy",
-            "host": host_description()}, dt
+    c0 = cfgs[Ts[0]]
+    w1q, w1s, w2q, w2s = [None] * c0.n_local, [None] * c0.n_local, [None] * c0.n_local, [None] * c0.n_local
+    total_dt, total_bytes, parts = 0.0, 0.0, []
+    for T in Ts:
+        c = cfgs[T]
+        lg = synth.logits(c, 0)
+        xq, xs = mx.quantize_mx(synth.x(c, 0), mx.FMT_E4M3)
+        idx, _ = omoe.route(lg, c.k)
+        active = sorted({int(e) - c.e0 for e in idx.ravel() if 0 <= int(e) - c.e0 < c.n_local})
+        for g in active:
+            if w1q[g] is None:
+                w1q[g], w1s[g] = mx.quantize_mx(synth.w1(c, g), c.w_fmt)
+                w2q[g], w2s[g] = mx.quantize_mx(synth.w2(c, g), c.w_fmt)
+        t0 = time.perf_counter()
+        omoe.moe_layer(lg, xq, xs, c.k, w1q, w1s, w2q, w2s, c.w_fmt, c.I, e0=c.e0, n_local=c.n_local)
+        dt = time.perf_counter() - t0
+        total_dt += dt
+        total_bytes += moe_bytes_fn(T, len(active))
+        parts.append(f"T={T} ({len(active)} active experts) {dt:.2f} s")
+    return {"value": total_bytes / total_dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "sample": "the step's layer calls at T = " + ", ".join(str(T) for T in Ts)
+                      + " (routing draw 0): " + "; ".join(parts)
+                      + f"; {total_dt:.1f} s wall on the host CPU, fp64 NumPy",
+            "host": host_description()}, total_dt
 
 
 def host_description():
@@ -637,7 +648,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu, _ = cpu_baseline(cfg[8], lambda T, act: layer_bytes(T, c.E, c.H, c.I, act, fp4))
+        cpu, _ = cpu_baseline(cfg, lambda T, act: layer_bytes(T, c.E, c.H, c.I, act, fp4))
         if others is not None:
             import numpy  # noqa: F401  (loads BLAS so its thread count is visible)
             threads = oracle_threads()
