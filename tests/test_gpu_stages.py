@@ -73,6 +73,26 @@ def test_route_parity(name, T, flags):
     np.testing.assert_allclose(host(w), w_ref, rtol=1e-5, atol=0)
 
 
+@pytest.mark.parametrize("T,E,k", [(37, 100, 16), (70, 33, 3), (5, 256, 16)])
+def test_route_parity_lane_edges(T, E, k):
+    """Expert counts that leave the last lanes of a token's lane group partly
+    or wholly past E, and top-16 (as many selections as half a lane group);
+    ties as in test_route_parity."""
+    banner(f"route lane edges T={T} E={E} k={k}")
+    rng = np.random.default_rng(T * 1000 + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[1, :] = np.float32(0.25)                          # all tied
+    lg[2, E // 2:E // 2 + 4] = lg[2].max() + 1           # ties at the top
+    lg[3, :] = -1.0                                      # -0 and +0 tie: the lower id first
+    lg[3, 1:E:3] = -0.0
+    lg[3, 2:E:3] = 0.0
+    for flags in (0, moe.MOE_ROUTE_RENORM):
+        idx_ref, w_ref = omoe.route(lg, k, renorm=bool(flags & moe.MOE_ROUTE_RENORM))
+        idx, w = moe.moe_route(dev(lg), k, flags)
+        np.testing.assert_array_equal(host(idx), idx_ref)
+        np.testing.assert_allclose(host(w), w_ref, rtol=1e-5, atol=0)
+
+
 # ------------------------------------------------------------------- permute
 PERMUTE_CASES = [
     # T, E, k, e0, n_local, shared, H
