@@ -275,6 +275,9 @@ W2_CASES = [
     ([(5 * g) % 9 + 1 for g in range(32)], 2048, 1024, "e2m1"),
     # 80 groups x 64 units: two waves per workgroup, whole units
     ([(3 * g) % 7 + 1 for g in range(80)], 4096, 256, "e4m3"),
+    # 40 groups x 56 units: 2240 units on two-wave workgroups, half units
+    # (2.2 rounds of halves against 2 of whole units)
+    ([(3 * g) % 7 + 1 for g in range(40)], 3584, 512, "e2m1"),
     # 16 weight tiles (H = 4096) x about 50 row passes: three or four work
     # items per workgroup of the LDS-tiled kernel, ragged tails
     ([5000, 257, 0, 3100, 2555, 1031], 4096, 256, "e4m3"),
