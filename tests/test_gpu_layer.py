@@ -296,6 +296,38 @@ def _check_group(c, g, w, ws, perm, x32, xq_d, xs_d, hT):
     assert_layer_close(bf16_bits(ws.view("y"))[lo:hi], y_ref, f"group {g} y")
 
 
+@pytest.mark.parametrize("T", [16, 32, 48])
+def test_layer_routing_ties(T):
+    """Routing and grouping with tied logits on the routers that give each
+    token 16 lanes: W1's own routing at T = 16 of the decode share (4-wave
+    items, so a wave routes several tokens) and the one-workgroup router and
+    grouping at T = 32 and 48; every selection, weight, count, offset and
+    row bit-exact against the oracle (weights to 1e-5)."""
+    from synth import device
+    c = synth.config("decode", T)
+    banner(f"layer routing ties T={T} E={c.E} k={c.k} local={c.n_local}")
+    dw = _device_weights(c)
+    _, xq_d, xs_d = device.build_inputs(c)
+    lg = synth.logits(c).copy()
+    lg[1, :] = np.float32(0.5)                           # all tied
+    lg[2, 40:48] = lg[2].max() + 1                       # ties at the top
+    lg[3, :] = -1.0                                      # -0 and +0 tie: the lower id first
+    lg[3, 10:40:2] = -0.0
+    lg[3, 11:41:2] = 0.0
+    lg[5, 0:32] = lg[5].max() + 2                        # a tie across every local expert
+    ws = moe.LayerWorkspace(c.T, c.E, c.k, c.n_local, c.H, c.I, c.shared, 0)
+    moe.moe_layer(dev(lg), xq_d, xs_d, dw.w1, dw.w2, c.k, c.e0, c.n_local, dw.shared, 0, ws=ws)
+    idx_ref, w_ref = omoe.route(lg, c.k)
+    np.testing.assert_array_equal(host(ws.view("topk_idx")), idx_ref)
+    np.testing.assert_allclose(host(ws.view("topk_w")), w_ref, rtol=1e-5, atol=0)
+    perm = omoe.permute(idx_ref, w_ref, c.e0, c.n_local, c.shared)
+    R = int(perm.offsets[-1])
+    np.testing.assert_array_equal(host(ws.view("counts")), perm.counts)
+    np.testing.assert_array_equal(host(ws.view("offsets")), perm.offsets)
+    np.testing.assert_array_equal(host(ws.view("slot_row")), perm.slot_row)
+    np.testing.assert_array_equal(host(ws.view("row_src"))[:R], perm.row_src)
+
+
 FULL = [("decode", 1), ("decode", 8), ("decode", 32), ("decode", 128), ("shared", None),
         ("full", None), ("prefill", None)]
 
