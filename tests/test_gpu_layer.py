@@ -296,13 +296,14 @@ def _check_group(c, g, w, ws, perm, x32, xq_d, xs_d, hT):
     assert_layer_close(bf16_bits(ws.view("y"))[lo:hi], y_ref, f"group {g} y")
 
 
-@pytest.mark.parametrize("T", [16, 32, 48])
+@pytest.mark.parametrize("T", [8, 16, 32, 48])
 def test_layer_routing_ties(T):
-    """Routing and grouping with tied logits on the routers that give each
-    token 16 lanes: W1's own routing at T = 16 of the decode share (4-wave
-    items, so a wave routes several tokens) and the one-workgroup router and
-    grouping at T = 32 and 48; every selection, weight, count, offset and
-    row bit-exact against the oracle (weights to 1e-5)."""
+    """Routing and grouping with tied logits on the routers inside the
+    layer: W1's own routing at T = 8 of the decode share (8-wave items, a
+    whole wave per token) and at T = 16 (4-wave items, 16 lanes per token),
+    and the one-workgroup router and grouping (16 lanes per token) at T = 32
+    and 48; every selection, weight, count, offset and row bit-exact against
+    the oracle (weights to 1e-5)."""
     from synth import device
     c = synth.config("decode", T)
     banner(f"layer routing ties T={T} E={c.E} k={c.k} local={c.n_local}")
