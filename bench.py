@@ -428,7 +428,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU's share of the expert-parallel layer on one MI355X; "
-              "runs on more than one GPU are not part of this build (use --gpus 1).", file=sys.stderr)
+              "it has no multi-GPU mode (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
