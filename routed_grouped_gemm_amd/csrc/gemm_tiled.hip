@@ -49,6 +49,7 @@
 // workgroups that run together on one XCD (blockIdx % 8) take consecutive
 // items and share operands in that XCD's L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "gemm_common.h"
 
@@ -341,179 +342,194 @@ void tiled_gemm_kernel(KParams p) {
 
     f32x4 acc[kBT][kAT];
     // one K-tile of the item: step s of the workgroup's sequence
-    auto kstep = [&](int kt, int s) {
+    // (full: false for a wave with no rows in the item, which only stages
+    // its share of the operands and keeps the barriers)
+    auto kstep = [&](int kt, int s, auto full) {
         // prefetch step s + 1 into the other stage (zeros past the last step)
         {
             const bool same = kt + 1 < nkt;
             stage_all<WFMT>(p, rx, rxs, same ? cur : nxt, same ? kt + 1 : 0, s + 1 < total,
                             ring + ((s + 1) & 1) * S::Bytes, w, lane);
         }
-        const uint8_t* st = ring + (s & 1) * S::Bytes;
-        // this wave's 4 weight tiles stay in registers for the K-tile; its
-        // 8 token tiles stream from LDS, each against all 4, the next token
-        // tile's reads in flight while the current one is multiplied
-        const int ash = 8 * (kt & 3);
-        i32x8 A[kAT];
-        int sa[kAT];
-        #pragma unroll
-        for (int t = 0; t < kAT; ++t) {
-            const int T = wi * kAT + t;
-            const uint8_t* ap = st + S::A + T * 64 * S::kBPL + lane * 16;
-            const i32x4 alo = *(const i32x4*)ap;
-            const i32x4 ahi = WFMT == MFMA_FMT_FP8 ? *(const i32x4*)(ap + 1024) : i32x4{0, 0, 0, 0};
-            A[t] = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
-            sa[t] = ((const int*)(st + S::AS))[T * 64 + lane];
-        }
-        auto load_b = [&](int j, i32x8& B, int& bs) {
-            const i32x4 blo = *(const i32x4*)(st + boff_lo[j]);
-            const i32x4 bhi = *(const i32x4*)(st + boff_hi[j]);
-            B = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
-            bs = ((const int*)(st + S::BS))[ti * 128 + 16 * j + r];
-        };
-        i32x8 Bb[2];
-        int bsb[2];
-        load_b(0, Bb[0], bsb[0]);
-        #pragma unroll
-        for (int t = 0; t < kAT; ++t) sa[t] >>= ash;
-        #pragma unroll
-        for (int j = 0; j < kBT; ++j) {
-            if (j + 1 < kBT) load_b(j + 1, Bb[(j + 1) & 1], bsb[(j + 1) & 1]);
-            const int bs = bsb[j & 1] >> (8 * q);
+        if constexpr (decltype(full)::value) {
+            const uint8_t* st = ring + (s & 1) * S::Bytes;
+            // this wave's 4 weight tiles stay in registers for the K-tile; its
+            // 8 token tiles stream from LDS, each against all 4, the next token
+            // tile's reads in flight while the current one is multiplied
+            const int ash = 8 * (kt & 3);
+            i32x8 A[kAT];
+            int sa[kAT];
             #pragma unroll
-            for (int t = 0; t < kAT; ++t)
-                acc[j][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, 0, 0>(A[t], Bb[j & 1], acc[j][t], sa[t], bs);
-        }
-        // issue order: the weight tiles, their scales and the first two token
-        // tiles; then per token tile its 4 MFMAs followed by the reads of the
-        // token tile after next (the scheduler would otherwise reuse one
-        // register buffer for every token tile and wait for each read)
-        constexpr int kAR = WFMT == MFMA_FMT_FP8 ? 3 : 2;      // LDS reads per weight tile
-        __builtin_amdgcn_sched_group_barrier(0x100, kAR * kAT + 6, 0);
-        #pragma unroll
-        for (int j = 0; j < kBT; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, kAT, 0);
-            if (j + 2 < kBT) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            for (int t = 0; t < kAT; ++t) {
+                const int T = wi * kAT + t;
+                const uint8_t* ap = st + S::A + T * 64 * S::kBPL + lane * 16;
+                const i32x4 alo = *(const i32x4*)ap;
+                const i32x4 ahi = WFMT == MFMA_FMT_FP8 ? *(const i32x4*)(ap + 1024) : i32x4{0, 0, 0, 0};
+                A[t] = __builtin_shufflevector(alo, ahi, 0, 1, 2, 3, 4, 5, 6, 7);
+                sa[t] = ((const int*)(st + S::AS))[T * 64 + lane];
+            }
+            auto load_b = [&](int j, i32x8& B, int& bs) {
+                const i32x4 blo = *(const i32x4*)(st + boff_lo[j]);
+                const i32x4 bhi = *(const i32x4*)(st + boff_hi[j]);
+                B = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+                bs = ((const int*)(st + S::BS))[ti * 128 + 16 * j + r];
+            };
+            i32x8 Bb[2];
+            int bsb[2];
+            load_b(0, Bb[0], bsb[0]);
+            #pragma unroll
+            for (int t = 0; t < kAT; ++t) sa[t] >>= ash;
+            #pragma unroll
+            for (int j = 0; j < kBT; ++j) {
+                if (j + 1 < kBT) load_b(j + 1, Bb[(j + 1) & 1], bsb[(j + 1) & 1]);
+                const int bs = bsb[j & 1] >> (8 * q);
+                #pragma unroll
+                for (int t = 0; t < kAT; ++t)
+                    acc[j][t] = mfma16x16x128<WFMT, MFMA_FMT_FP8, 0, 0>(A[t], Bb[j & 1], acc[j][t], sa[t], bs);
+            }
+            // issue order: the weight tiles, their scales and the first two token
+            // tiles; then per token tile its 4 MFMAs followed by the reads of the
+            // token tile after next (the scheduler would otherwise reuse one
+            // register buffer for every token tile and wait for each read)
+            constexpr int kAR = WFMT == MFMA_FMT_FP8 ? 3 : 2;      // LDS reads per weight tile
+            __builtin_amdgcn_sched_group_barrier(0x100, kAR * kAT + 6, 0);
+            #pragma unroll
+            for (int j = 0; j < kBT; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, kAT, 0);
+                if (j + 2 < kBT) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0);       // the next step's operands have landed
         __syncthreads();
     };
     for (int it = 0; it < n_my; ++it) {
         int s = it * nkt;
-        #pragma unroll
-        for (int j = 0; j < kBT; ++j)
+        // the waves of the second token half of a half pass (at most 128
+        // rows) have no rows: they skip the MFMAs, LDS reads and epilogue,
+        // and the other wave of their SIMD runs alone (forward modes)
+        const bool idle = (MODE == kModeW1 || MODE == kModeW2) &&
+                          ti * (kBT * 16) >= __builtin_amdgcn_readfirstlane(cur.nrows);
+        if (idle) {
+            for (int kt = 0; kt < nkt; ++kt, ++s) kstep(kt, s, std::false_type{});
+        } else {
             #pragma unroll
-            for (int t = 0; t < kAT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kt = 0; kt < nkt; ++kt, ++s) kstep(kt, s);
+            for (int j = 0; j < kBT; ++j)
+                #pragma unroll
+                for (int t = 0; t < kAT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < nkt; ++kt, ++s) kstep(kt, s, std::true_type{});
+        }
 
         // ---------------------------------------------------- epilogue
         const int tok0 = ti * (kBT * 16);
         const int uu = cur.wt * kUnits + wi;                    // this wave's unit
         if constexpr (IS_W1) {
-            // the stage just consumed serves as scratch; the next step's
-            // prefetch lands in it only after the barrier below
-            uint8_t* scratch = ring + ((s - 1) & 1) * S::Bytes;
-            uint8_t* tw = scratch + w * kTWave;
-            uint8_t* tsw = scratch + kWaves * kTWave + w * 128;
-            const int I = p.N / 2;
-            // the item's rows of h, its scales and its routing weights
-            const rsrc_t rhq = make_rsrc(p.hq + (size_t)cur.rbase * I, (uint32_t)(cur.nrows * I));
-            const rsrc_t rhs = make_rsrc(p.hs + (size_t)cur.rbase * (I / 32), (uint32_t)(cur.nrows * (I / 32)));
-            const rsrc_t rw_w = make_rsrc(p.row_w + cur.rbase, p.use_w ? (uint32_t)(cur.nrows * 4) : 0u);
-            // the routing weights of this lane's 8 token rows, all requested
-            // before the first is used (one memory latency per item, not 8);
-            // rows past the item read 0 and have zero sums anyway
-            // (without weights the resource is empty: the loads return 0 and
-            // are replaced by 1 without a branch)
-            float wrow[kBT];
-            #pragma unroll
-            for (int j = 0; j < kBT; ++j)
-                wrow[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    rw_w, (uint32_t)((tok0 + 16 * j + r) * 4), 0, 0));
-            #pragma unroll
-            for (int j = 0; j < kBT; ++j) wrow[j] = p.use_w ? wrow[j] : 1.0f;
-            // generic variant: this lane's 8 gate and 8 up biases (features
-            // 32 uu + 16 a + 4 q + v), zero without a bias; the BF16
-            // pre-activation copy goes to rows of 2I
-            float bg[2][4] = {}, bu[2][4] = {};
-            const bool spre = MODE == kModeW1Gen && p.save_pre;
-            const rsrc_t rpre = make_rsrc(spre ? p.save_pre + (size_t)cur.rbase * 2 * I : (uint16_t*)p.hq,
-                                          spre ? (uint32_t)(cur.nrows * 2 * I * 2) : 0u);
-            if constexpr (MODE == kModeW1Gen) {
-                const rsrc_t rb = make_rsrc(p.bias + (size_t)cur.g * 2 * I, p.bias ? (uint32_t)(2 * I * 4) : 0u);
+            if (!idle) {
+                // the stage just consumed serves as scratch; the next step's
+                // prefetch lands in it only after the barrier below
+                uint8_t* scratch = ring + ((s - 1) & 1) * S::Bytes;
+                uint8_t* tw = scratch + w * kTWave;
+                uint8_t* tsw = scratch + kWaves * kTWave + w * 128;
+                const int I = p.N / 2;
+                // the item's rows of h, its scales and its routing weights
+                const rsrc_t rhq = make_rsrc(p.hq + (size_t)cur.rbase * I, (uint32_t)(cur.nrows * I));
+                const rsrc_t rhs = make_rsrc(p.hs + (size_t)cur.rbase * (I / 32), (uint32_t)(cur.nrows * (I / 32)));
+                const rsrc_t rw_w = make_rsrc(p.row_w + cur.rbase, p.use_w ? (uint32_t)(cur.nrows * 4) : 0u);
+                // the routing weights of this lane's 8 token rows, all requested
+                // before the first is used (one memory latency per item, not 8);
+                // rows past the item read 0 and have zero sums anyway
+                // (without weights the resource is empty: the loads return 0 and
+                // are replaced by 1 without a branch)
+                float wrow[kBT];
                 #pragma unroll
-                for (int a = 0; a < 2; ++a)
-                    #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const uint32_t f = (uint32_t)(32 * uu + 16 * a + 4 * q + v);
-                        bg[a][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * f, 0, 0));
-                        bu[a][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (f + I), 0, 0));
-                    }
-            }
-            #pragma unroll
-            for (int jp = 0; jp < kBT / 2; ++jp) {
-                float h[2][2][4];                               // [j in pair][gate tile][v]
+                for (int j = 0; j < kBT; ++j)
+                    wrow[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rw_w, (uint32_t)((tok0 + 16 * j + r) * 4), 0, 0));
                 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int j = 2 * jp + jj;
-                    const int tok = tok0 + 16 * j + r;
-                    // rows past the item have zero token rows, so zero sums and h = 0
-                    const float wgt = wrow[j];
-                    float amf = 0.f;
-                    #pragma unroll
-                    for (int a = 0; a < 2; ++a) {
-                        if constexpr (MODE == kModeW1Gen) {
-                            float gz[4], uz[4];
-                            #pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                gz[v] = acc[j][a][v] + bg[a][v];
-                                uz[v] = acc[j][a + 2][v] + bu[a][v];
-                            }
-                            // pre-activation rows (dropped past the item's rows)
-                            u32x2 pg, pu;
-                            pg.x = bf16x2(gz[0], gz[1]); pg.y = bf16x2(gz[2], gz[3]);
-                            pu.x = bf16x2(uz[0], uz[1]); pu.y = bf16x2(uz[2], uz[3]);
-                            const uint32_t po = (uint32_t)((tok * 2 * I + 32 * uu + 16 * a + 4 * q) * 2);
-                            __builtin_amdgcn_raw_buffer_store_b64(pg, rpre, po, 0, 0);
-                            __builtin_amdgcn_raw_buffer_store_b64(pu, rpre, po + (uint32_t)(2 * I), 0, 0);
-                            #pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                float g = gz[v], u = uz[v];
-                                if (p.limit > 0.f) {
-                                    g = fminf(fmaxf(g, -p.limit), p.limit);
-                                    u = fminf(fmaxf(u, -p.limit), p.limit);
-                                }
-                                const float hv = act_value(g, p.act, p.beta) * u * wgt;
-                                h[jj][a][v] = hv;
-                                amf = fmaxf(amf, fabsf(hv));
-                            }
-                        } else {
-                            #pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const float hv = silu_fast(acc[j][a][v]) * acc[j][a + 2][v] * wgt;
-                                h[jj][a][v] = hv;
-                                amf = fmaxf(amf, fabsf(hv));
-                            }
-                        }
-                    }
-                    // the unit's 32 features of this token: 4 lanes (q) x 8 values
-                    const uint32_t am = rows4_umax(__float_as_uint(amf));
-                    const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
-                    const float inv = inv_scale(code);
-                    // rows past the item fall outside the resources' range: dropped
+                for (int j = 0; j < kBT; ++j) wrow[j] = p.use_w ? wrow[j] : 1.0f;
+                // generic variant: this lane's 8 gate and 8 up biases (features
+                // 32 uu + 16 a + 4 q + v), zero without a bias; the BF16
+                // pre-activation copy goes to rows of 2I
+                float bg[2][4] = {}, bu[2][4] = {};
+                const bool spre = MODE == kModeW1Gen && p.save_pre;
+                const rsrc_t rpre = make_rsrc(spre ? p.save_pre + (size_t)cur.rbase * 2 * I : (uint16_t*)p.hq,
+                                              spre ? (uint32_t)(cur.nrows * 2 * I * 2) : 0u);
+                if constexpr (MODE == kModeW1Gen) {
+                    const rsrc_t rb = make_rsrc(p.bias + (size_t)cur.g * 2 * I, p.bias ? (uint32_t)(2 * I * 4) : 0u);
                     #pragma unroll
                     for (int a = 0; a < 2; ++a)
-                        __builtin_amdgcn_raw_buffer_store_b32(
-                            e4m3x4(h[jj][a][0] * inv, h[jj][a][1] * inv, h[jj][a][2] * inv, h[jj][a][3] * inv),
-                            rhq, (uint32_t)(tok * I + 32 * uu + 16 * a + 4 * q), 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, rhs,
-                                                         q == 0 ? (uint32_t)(tok * (I / 32) + uu) : kInvalid, 0, 0);
+                        #pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const uint32_t f = (uint32_t)(32 * uu + 16 * a + 4 * q + v);
+                            bg[a][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * f, 0, 0));
+                            bu[a][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, 4 * (f + I), 0, 0));
+                        }
                 }
-                // 32-token block jp of this wave, staged in LDS for the transposed copy
-                if (p.transpose) transpose_stage(h, jp, tw, tsw, lane, p.ceil_rule);
+                #pragma unroll
+                for (int jp = 0; jp < kBT / 2; ++jp) {
+                    float h[2][2][4];                               // [j in pair][gate tile][v]
+                    #pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int j = 2 * jp + jj;
+                        const int tok = tok0 + 16 * j + r;
+                        // rows past the item have zero token rows, so zero sums and h = 0
+                        const float wgt = wrow[j];
+                        float amf = 0.f;
+                        #pragma unroll
+                        for (int a = 0; a < 2; ++a) {
+                            if constexpr (MODE == kModeW1Gen) {
+                                float gz[4], uz[4];
+                                #pragma unroll
+                                for (int v = 0; v < 4; ++v) {
+                                    gz[v] = acc[j][a][v] + bg[a][v];
+                                    uz[v] = acc[j][a + 2][v] + bu[a][v];
+                                }
+                                // pre-activation rows (dropped past the item's rows)
+                                u32x2 pg, pu;
+                                pg.x = bf16x2(gz[0], gz[1]); pg.y = bf16x2(gz[2], gz[3]);
+                                pu.x = bf16x2(uz[0], uz[1]); pu.y = bf16x2(uz[2], uz[3]);
+                                const uint32_t po = (uint32_t)((tok * 2 * I + 32 * uu + 16 * a + 4 * q) * 2);
+                                __builtin_amdgcn_raw_buffer_store_b64(pg, rpre, po, 0, 0);
+                                __builtin_amdgcn_raw_buffer_store_b64(pu, rpre, po + (uint32_t)(2 * I), 0, 0);
+                                #pragma unroll
+                                for (int v = 0; v < 4; ++v) {
+                                    float g = gz[v], u = uz[v];
+                                    if (p.limit > 0.f) {
+                                        g = fminf(fmaxf(g, -p.limit), p.limit);
+                                        u = fminf(fmaxf(u, -p.limit), p.limit);
+                                    }
+                                    const float hv = act_value(g, p.act, p.beta) * u * wgt;
+                                    h[jj][a][v] = hv;
+                                    amf = fmaxf(amf, fabsf(hv));
+                                }
+                            } else {
+                                #pragma unroll
+                                for (int v = 0; v < 4; ++v) {
+                                    const float hv = silu_fast(acc[j][a][v]) * acc[j][a + 2][v] * wgt;
+                                    h[jj][a][v] = hv;
+                                    amf = fmaxf(amf, fabsf(hv));
+                                }
+                            }
+                        }
+                        // the unit's 32 features of this token: 4 lanes (q) x 8 values
+                        const uint32_t am = rows4_umax(__float_as_uint(amf));
+                        const uint32_t code = e4m3_scale_code(__uint_as_float(am), p.ceil_rule);
+                        const float inv = inv_scale(code);
+                        // rows past the item fall outside the resources' range: dropped
+                        #pragma unroll
+                        for (int a = 0; a < 2; ++a)
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                e4m3x4(h[jj][a][0] * inv, h[jj][a][1] * inv, h[jj][a][2] * inv, h[jj][a][3] * inv),
+                                rhq, (uint32_t)(tok * I + 32 * uu + 16 * a + 4 * q), 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, rhs,
+                                                             q == 0 ? (uint32_t)(tok * (I / 32) + uu) : kInvalid, 0, 0);
+                    }
+                    // 32-token block jp of this wave, staged in LDS for the transposed copy
+                    if (p.transpose) transpose_stage(h, jp, tw, tsw, lane, p.ceil_rule);
+                }
+                if (p.transpose)
+                    transpose_flush(tw, tsw, p.hTq, p.hTs, I, p.ldT, 32 * uu,
+                                    p.offsets32[cur.g] + cur.pass * kRows + tok0, tok0, cur.nrows, lane);
             }
-            if (p.transpose)
-                transpose_flush(tw, tsw, p.hTq, p.hTs, I, p.ldT, 32 * uu,
-                                p.offsets32[cur.g] + cur.pass * kRows + tok0, tok0, cur.nrows, lane);
             __syncthreads();                 // scratch free before the next prefetch lands in it
         } else if constexpr (MODE == kModeBwd) {
             // dActivation epilogue. acc holds dh for this wave's 64 features
@@ -677,28 +693,30 @@ void tiled_gemm_kernel(KParams p) {
             // instruction writes whole 128-byte lines (8 rows x 64 features),
             // streamed out non-temporally: the burst of stores at the end of
             // an item then drains sooner, before the next K-tile's wait
-            const int H = p.N;
-            uint8_t* ys = ring + ((s - 1) & 1) * S::Bytes + w * (32 * kYStride);
-            #pragma unroll
-            for (int c = 0; c < kBT / 2; ++c) {
+            if (!idle) {
+                const int H = p.N;
+                uint8_t* ys = ring + ((s - 1) & 1) * S::Bytes + w * (32 * kYStride);
                 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int j = 2 * c + jj;
+                for (int c = 0; c < kBT / 2; ++c) {
                     #pragma unroll
-                    for (int t = 0; t < kAT; ++t) {
-                        uint2 o;
-                        o.x = bf16x2(acc[j][t][0], acc[j][t][1]);
-                        o.y = bf16x2(acc[j][t][2], acc[j][t][3]);
-                        *(uint2*)(ys + (16 * jj + r) * kYStride + (16 * t + 4 * q) * 2) = o;
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int j = 2 * c + jj;
+                        #pragma unroll
+                        for (int t = 0; t < kAT; ++t) {
+                            uint2 o;
+                            o.x = bf16x2(acc[j][t][0], acc[j][t][1]);
+                            o.y = bf16x2(acc[j][t][2], acc[j][t][3]);
+                            *(uint2*)(ys + (16 * jj + r) * kYStride + (16 * t + 4 * q) * 2) = o;
+                        }
                     }
-                }
-                #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 8 * i + (lane >> 3), k16 = lane & 7;
-                    const i32x4 d = *(const i32x4*)(ys + row * kYStride + 16 * k16);
-                    const int tok = tok0 + 32 * c + row;
-                    if (tok < cur.nrows)
-                        __builtin_nontemporal_store(d, (i32x4*)(p.y + (size_t)(cur.rbase + tok) * H + 64 * uu + 8 * k16));
+                    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 8 * i + (lane >> 3), k16 = lane & 7;
+                        const i32x4 d = *(const i32x4*)(ys + row * kYStride + 16 * k16);
+                        const int tok = tok0 + 32 * c + row;
+                        if (tok < cur.nrows)
+                            __builtin_nontemporal_store(d, (i32x4*)(p.y + (size_t)(cur.rbase + tok) * H + 64 * uu + 8 * k16));
+                    }
                 }
             }
             __syncthreads();                 // scratch free before the next prefetch lands in it

@@ -178,6 +178,9 @@ W1_CASES = [
     ([0, 1, 255, 256, 257, 600, 33], 512, 256, "e4m3", (1 << 31) | moe.MOE_W1_WRITE_TRANSPOSE),
     ([300, 17, 513], 1024, 512, "e2m1", 0),
     ([520, 0, 64], 512, 384, "e4m3", moe.MOE_SCALE_RULE_CEIL | moe.MOE_W1_WRITE_TRANSPOSE),
+    # last passes of exactly 128 and of 129 rows (in a pass of at most 128
+    # rows the LDS-tiled kernel's second token half skips its work)
+    ([128, 384, 0, 129, 640, 1], 512, 256, "e4m3", moe.MOE_W1_WRITE_TRANSPOSE),
     # 16 weight tiles (I = 2048) x about 50 row passes: about 800 work items,
     # so each workgroup of the LDS-tiled kernel's persistent grid walks three
     # or four of them (the cross-item prefetch, the stage reused as epilogue
@@ -269,6 +272,7 @@ W2_CASES = [
     ([200], 768, 384, "e2m1"),
     ([0, 1, 255, 256, 257, 600, 33], 512, 256, "e4m3"),
     ([300, 17, 513], 1024, 512, "e2m1"),
+    ([128, 384, 0, 129, 640, 1], 1024, 256, "e4m3"),
     # 9 groups x 64 units: four waves per workgroup, half units
     ([5, 1, 0, 20, 3, 7, 2, 16, 40], 4096, 256, "e4m3"),
     # 32 groups x 32 units: two waves per workgroup, half units
