@@ -84,6 +84,9 @@ struct Stage {
     static constexpr int AS = BS + kRows * 4;
     static constexpr int Bytes = AS + 16 * 64 * 4;
 };
+// the W1 epilogue's scratch (per wave: transposed staging, its scales, a
+// 2 KiB fp32 tile) fits in one stage
+static_assert(kWaves * (kTWave + 128 + 2048) <= Stage<MFMA_FMT_FP4>::Bytes, "W1 epilogue scratch");
 
 MOE_DEV int bswz(int row) { return (row >> 1) & 7; }
 
@@ -233,6 +236,47 @@ MOE_DEV void transpose_stage(const float (&h)[2][2][4], int jp, uint8_t* tw, uin
             const int fl = 16 * a + 4 * q + (lane & 3);
             *(uint32_t*)(tw + fl * stride + 16 * (2 * jp + jj) + 4 * ((lane >> 2) & 3)) = tr;
         }
+    }
+}
+
+// Transposed copy, staging of one 32-token block jp of a wave through an
+// fp32 tile in LDS, one 16-feature half a at a time: the lanes write their
+// values (token 16 jj + r, features 16 a + 4 q + [0, 4)) as [token][feature]
+// rows, then lane l reads feature l % 16 of tokens 8 (l / 16) + [0, 8), takes
+// their amax locally and over the four lanes of its feature, and writes its
+// 8 E4M3 codes as one 8-byte piece of the feature's row of tw, and lanes
+// 0-15 the E8M0 byte to tsw. Same values and order of operations per code
+// as the register-only staging above, with one scale computation per lane
+// and half instead of eight.
+// xs (2 KiB, 16 B aligned): row t at 64-byte half (t & 1) ^ ((t >> 3) & 1)
+// of line t / 2, its 16-byte chunks XOR-swizzled by (t >> 1) & 3: the
+// writes of 8 consecutive lanes and the reads of 32 hit distinct banks.
+MOE_DEV int xs_word(int t, int f) {
+    return (t >> 1) * 32 + (((t & 1) ^ ((t >> 3) & 1)) << 4) + ((((f >> 2) ^ (t >> 1)) & 3) << 2) + (f & 3);
+}
+MOE_DEV void transpose_stage_f32(const float (&h)[2][2][4], int jp, float* xs, uint8_t* tw, uint8_t* tsw,
+                                 int lane, bool ceil_rule) {
+    const int q = lane >> 4, r = lane & 15;
+    const int f = lane & 15, tg = lane >> 4;
+    #pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        #pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+            *(f32x4*)(xs + xs_word(16 * jj + r, 4 * q)) =
+                f32x4{h[jj][a][0], h[jj][a][1], h[jj][a][2], h[jj][a][3]};
+        float v[8];
+        #pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = xs[xs_word(8 * tg + i, f)];
+        float amf = 0.f;
+        #pragma unroll
+        for (int i = 0; i < 8; ++i) amf = fmaxf(amf, fabsf(v[i]));
+        const uint32_t code = e4m3_scale_code(__uint_as_float(rows4_umax(__float_as_uint(amf))), ceil_rule);
+        const float inv = inv_scale(code);
+        u32x2 pk;
+        pk.x = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        pk.y = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        *(u32x2*)(tw + (16 * a + f) * kTStride + 32 * jp + 8 * tg) = pk;
+        if (tg == 0) tsw[jp * 32 + 16 * a + f] = (uint8_t)code;
     }
 }
 
@@ -429,6 +473,7 @@ void tiled_gemm_kernel(KParams p) {
                 uint8_t* scratch = ring + ((s - 1) & 1) * S::Bytes;
                 uint8_t* tw = scratch + w * kTWave;
                 uint8_t* tsw = scratch + kWaves * kTWave + w * 128;
+                float* xs = (float*)(scratch + kWaves * (kTWave + 128) + w * 2048);
                 const int I = p.N / 2;
                 // the item's rows of h, its scales and its routing weights
                 const rsrc_t rhq = make_rsrc(p.hq + (size_t)cur.rbase * I, (uint32_t)(cur.nrows * I));
@@ -524,7 +569,12 @@ void tiled_gemm_kernel(KParams p) {
                                                              q == 0 ? (uint32_t)(tok * (I / 32) + uu) : kInvalid, 0, 0);
                     }
                     // 32-token block jp of this wave, staged in LDS for the transposed copy
-                    if (p.transpose) transpose_stage(h, jp, tw, tsw, lane, p.ceil_rule);
+                    // (the generic variant keeps the register-only staging:
+                    // its bias and pre-activation leave no registers for this one)
+                    if (p.transpose) {
+                        if constexpr (MODE == kModeW1) transpose_stage_f32(h, jp, xs, tw, tsw, lane, p.ceil_rule);
+                        else transpose_stage(h, jp, tw, tsw, lane, p.ceil_rule);
+                    }
                 }
                 if (p.transpose)
                     transpose_flush(tw, tsw, p.hTq, p.hTs, I, p.ldT, 32 * uu,
