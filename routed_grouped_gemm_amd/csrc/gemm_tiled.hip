@@ -449,10 +449,11 @@ void tiled_gemm_kernel(KParams p) {
     for (int it = 0; it < n_my; ++it) {
         int s = it * nkt;
         // the waves of the second token half of a half pass (at most 128
-        // rows) have no rows: they skip the MFMAs, LDS reads and epilogue,
-        // and the other wave of their SIMD runs alone (forward modes)
-        const bool idle = (MODE == kModeW1 || MODE == kModeW2) &&
-                          ti * (kBT * 16) >= __builtin_amdgcn_readfirstlane(cur.nrows);
+        // rows) have no rows: they skip the MFMAs, LDS reads and epilogue
+        // (whose stores all stop at the item's rows), and the other wave of
+        // their SIMD runs alone (the forward modes; in the backward the
+        // second copy of the K-loop made its epilogue spill 70% more)
+        const bool idle = MODE != kModeBwd && ti * (kBT * 16) >= __builtin_amdgcn_readfirstlane(cur.nrows);
         if (idle) {
             for (int kt = 0; kt < nkt; ++kt, ++s) kstep(kt, s, std::false_type{});
         } else {
