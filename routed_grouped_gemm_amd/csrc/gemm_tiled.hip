@@ -36,12 +36,16 @@
 //  - Memory requests that an item waits for are issued together: the routing
 //    weights of the item's rows (W1 epilogue) and the source rows of the next
 //    item, one latency each per item.
+//  - In a pass of at most 128 rows (a group's last), the four waves of the
+//    empty token half only stage their share of the operands and keep the
+//    barriers; the other wave of each SIMD then runs alone.
 //  - Epilogues run on the accumulators. W1: gate and up of the same feature
 //    sit in the same lane (the prepacked units pair them), so
 //    h = SiLU(gate) * up * w is formed in place; the 32 features of a unit are
 //    one MX block along I (4 lanes x 8 values) and go out as one dword per
 //    lane; the transposed copy (32-token blocks along the group's rows) is
-//    transposed through LDS and leaves as 16-byte row stores. W2: BF16 rows.
+//    transposed through an fp32 tile in LDS, so that each lane scales 8
+//    tokens of one feature, and leaves as 16-byte row stores. W2: BF16 rows.
 //    Conversions use the hardware's round-to-nearest-even converters.
 //
 // Work items are (group, 256-row pass, 256-row weight tile), weight tile
